@@ -1,0 +1,232 @@
+"""Benchmark: backward TFLOPS on selected blocks for 64-token block-sparse attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4] [--no-cpu-baseline]
+
+One step runs the whole path once over one batch of synthetic input already resident in HBM:
+invert_indices (q2k -> k2q), the forward (o, lse), and the backward chain (preprocess, work order,
+main kernel, postprocess). Every stage is bracketed by HIP events on the stream it runs on.
+
+  value       = selected-block FLOPs of the backward / time of the backward chain, where
+                selected-block FLOPs = pairs * 5 GEMMs * 2*64*64*128 (the FastVideo commit
+                message's "TFLOPS on selected blocks", kernels-only window: preprocess -> order ->
+                main -> postprocess);
+  ms_per_step = mean time of a whole step (invert + forward + backward);
+  roofline    = the main backward kernel: its selected-block FLOPs / its mean launch duration,
+                against the MI355X dense bf16 MFMA peak (2.5 PFLOP/s);
+  cpu_baseline= the float64 CPU oracle's backward on a bounded sample of the same workload.
+
+The headline workload is B=1 H=8 S=32768 D=128, 25 % density (default); --workload 4 selects
+S=65536 at 12.5 % density. The line also carries the other headline workload's backward TFLOPS.
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "bwd TFLOPS on selected blocks, B=1 H=8 D=128 S=32k/65k; % bf16 MFMA peak"
+FLOP_PER_PAIR = 5 * 2 * 64 * 64 * 128
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+WORKLOAD_TEXT = {
+    3: "VSA 64-token block-sparse attention backward, B=1 H=8 S=32768 D=128 bf16, 25% density "
+       "(top-k 128 of 512 kv blocks per q block), all blocks full, o/lse from the GPU forward",
+    4: "VSA 64-token block-sparse attention backward, B=1 H=8 S=65536 D=128 bf16, 12.5% density "
+       "(top-k 128 of 1024 kv blocks per q block), all blocks full, device work order",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_workload(n, steps, warmup):
+    import torch
+
+    import block_sparse_attention_attn_amd as V
+    import workloads
+
+    dev = "cuda:0"
+    c = workloads.config(n)
+    pairs = c.pairs
+    q, k, v, do = (t.to(dev) for t in (c.q, c.k, c.v, c.do))
+    idx, num, vbs = c.q2k_idx.to(dev), c.q2k_num.to(dev), c.vbs.to(dev)
+    # buffers allocated once; every step rewrites them
+    o = torch.empty_like(q)
+    lse = torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=dev)
+    k2q_idx = torch.empty(c.B, c.H, c.nb, c.nb, dtype=torch.int32, device=dev)
+    k2q_num = torch.empty(c.B, c.H, c.nb, dtype=torch.int32, device=dev)
+    inv_ws = torch.empty(V.invert_workspace_bytes(c.B, c.H, c.nb, c.nb), dtype=torch.uint8,
+                         device=dev)
+    plan = V.BwdPlan(do, q, k, v, o, lse, k2q_idx, k2q_num, vbs)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        V.invert_indices(idx, num, c.nb, workspace=inv_ws, out=(k2q_idx, k2q_num))
+        if ev is not None:
+            ev[1].record()
+        V.forward(q, k, v, idx, num, vbs, out=(o, lse))
+        if ev is not None:
+            ev[2].record()
+        for i, s in enumerate((plan.PREPROCESS, plan.ORDER, plan.MAIN, plan.POSTPROCESS)):
+            plan.stage(s)
+            if ev is not None:
+                ev[3 + i].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    def span(e, a, b):
+        return [x[a].elapsed_time(x[b]) for x in e]
+
+    invert = span(evs, 0, 1)
+    fwd = span(evs, 1, 2)
+    bwd = span(evs, 2, 6)
+    pre, order, main, post = (span(evs, 2 + i, 3 + i) for i in range(4))
+    total = t_start.elapsed_time(t_end) / steps
+    res = dict(
+        workload=n, pairs=pairs, ms_per_step=total, wall_s=wall,
+        bwd_ms=statistics.mean(bwd), bwd_ms_median=statistics.median(bwd),
+        invert_ms=statistics.mean(invert), fwd_ms=statistics.mean(fwd),
+        pre_ms=statistics.mean(pre), order_ms=statistics.mean(order),
+        main_ms=statistics.mean(main), main_ms_median=statistics.median(main),
+        post_ms=statistics.mean(post))
+    res["bwd_tflops"] = pairs * FLOP_PER_PAIR / (res["bwd_ms"] * 1e-3) / 1e12
+    res["main_tflops"] = pairs * FLOP_PER_PAIR / (res["main_ms"] * 1e-3) / 1e12
+    res["fwd_tflops"] = pairs * 2 * 2 * 64 * 64 * 128 / (res["fwd_ms"] * 1e-3) / 1e12
+    del plan
+    torch.cuda.empty_cache()
+    return res, c
+
+
+def cpu_baseline(c, budget_s=15.0):
+    """The oracle's backward, q block by q block of head 0, until ~budget_s of CPU work."""
+    import numpy as np
+    from oracle import vsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    Q, K, V_, DO = (O.f64(t[0, 0]) for t in (c.q, c.k, c.v, c.do))
+    idx = c.q2k_idx[:1, :1]
+    num = c.q2k_num[:1, :1]
+    done_pairs = 0
+    blocks = 0
+    t0 = time.perf_counter()
+    while blocks < c.nb and (time.perf_counter() - t0 < budget_s or blocks < 4):
+        keys = O.kept_keys(idx, num, c.vbs, 0, 0, blocks)
+        rows = slice(blocks * 64, (blocks + 1) * 64)
+        O.qblock_backward(Q[rows], DO[rows], K[keys], V_[keys], c.sm_scale)
+        done_pairs += int(num[0, 0, blocks])
+        blocks += 1
+    dt = time.perf_counter() - t0
+    return dict(value=done_pairs * FLOP_PER_PAIR / dt / 1e12, unit="TFLOPS", cores=int(threads),
+                kind="oracle",
+                sample=f"float64 numpy oracle backward (recomputing each q block's softmax) over q "
+                       f"blocks 0..{blocks - 1} of head 0 of the same workload: {done_pairs} "
+                       f"selected pairs in {dt:.1f} s; BLAS threads {threads}, "
+                       f"os.cpu_count()={os.cpu_count()}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=(3, 4))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: the work shards over (batch, head) with no exchange", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    log(f"[bench] workload {args.workload}: steps={args.steps} warmup={args.warmup}")
+    res, case = run_workload(args.workload, args.steps, args.warmup)
+    log(f"[bench] {json.dumps(res)}")
+    secondary = None
+    if not args.no_secondary:
+        other = 4 if args.workload == 3 else 3
+        log(f"[bench] secondary workload {other}")
+        r2, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2))
+        log(f"[bench] {json.dumps(r2)}")
+        secondary = dict(workload=WORKLOAD_TEXT[other], bwd_tflops=round(r2["bwd_tflops"], 2),
+                         bwd_ms=round(r2["bwd_ms"], 4), main_ms=round(r2["main_ms"], 4),
+                         frac_of_peak=round(r2["bwd_tflops"] / PEAK_BF16_TFLOPS, 4))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(case)
+        log(f"[bench] cpu {json.dumps(cpu)}")
+
+    achieved = res["main_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(res["bwd_tflops"], 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload],
+            "global_batch": case.B,
+            "seq_len": case.S,
+            "heads": case.H,
+            "head_dim": 128,
+            "selected_pairs": res["pairs"],
+            "parallelism": "none (1 GPU)",
+        },
+        "frac_of_peak": round(res["bwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "breakdown_ms": {k: round(res[k], 4) for k in ("invert_ms", "fwd_ms", "pre_ms", "order_ms",
+                                                      "main_ms", "post_ms", "bwd_ms")},
+        "roofline": {
+            "kernel": "bwd_main_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "secondary": secondary,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,349 @@
+"""MI355X (gfx950) 64-token block-sparse attention, VSA style: forward, backward, k2q inversion.
+
+A thin ctypes binding over ``libvsa.so`` (the C ABI in ``include/vsa.h``). This layer only checks
+tensor metadata (device, dtype, shape, contiguity -- never tensor contents), allocates outputs and
+workspaces with PyTorch, and passes raw device pointers plus the current HIP stream. Every step of
+the computation runs in the library's HIP kernels; there is no CPU path. If the library is not
+built, every entry point raises.
+
+Semantics follow the FastVideo pages (sm_100a backward commit message; the backward Python
+module: ``is_supported``, ``block_sparse_attn_backward_sm100a_from_k2q`` and the q2k entry that
+inverts first; the forward module docstring for the lse "M form"):
+  * activations are bf16 ``[B, H, S, 128]`` contiguous (BHSD), ``S = 64 * num_kv_blocks``;
+  * ``lse = max(q k^T * sm_scale * log2 e) + log2(l)``, fp32 ``[B, H, S]``;
+  * ``sm_scale = 1 / sqrt(head_dim)``; dq and dk carry it, dv does not;
+  * kv blocks no q block selects get exact-zero dk/dv rows, as do kv rows at or past vbs;
+  * the gradient with respect to lse is not supported (the pages' backward ignores it).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "library_path", "is_built", "is_supported",
+    "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
+    "bwd_workspace_bytes", "bwd_workspace_layout", "invert_workspace_bytes", "BwdPlan",
+]
+
+BLOCK = 64
+HEAD_DIM = 128
+ORDER_MIN_KV_BLOCKS = 1024
+ORDER_MAX_KV_BLOCKS = 16384
+_LOG2E = 1.4426950408889634
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libvsa.so")
+_lib = None
+
+_p = ctypes.c_void_p
+
+
+class _FwdArgs(ctypes.Structure):
+    _fields_ = [("q", _p), ("k", _p), ("v", _p), ("q2k_idx", _p), ("q2k_num", _p), ("vbs", _p),
+                ("o", _p), ("lse", _p), ("batch", ctypes.c_int), ("heads", ctypes.c_int),
+                ("seqlen", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("num_kv_blocks", ctypes.c_int), ("q2k_stride", ctypes.c_int),
+                ("sm_scale", ctypes.c_float)]
+
+
+class _BwdArgs(ctypes.Structure):
+    _fields_ = [("q", _p), ("k", _p), ("v", _p), ("o", _p), ("dout", _p), ("lse", _p),
+                ("k2q_idx", _p), ("k2q_num", _p), ("vbs", _p), ("order", _p), ("dq", _p),
+                ("dk", _p), ("dv", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+                ("batch", ctypes.c_int), ("heads", ctypes.c_int), ("seqlen", ctypes.c_int),
+                ("head_dim", ctypes.c_int), ("num_kv_blocks", ctypes.c_int),
+                ("max_q_blocks", ctypes.c_int), ("sm_scale", ctypes.c_float)]
+
+
+# name -> (restype, argtypes); exactly the symbols include/vsa.h declares
+_SIGNATURES = {
+    "vsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "vsa_last_error": (ctypes.c_char_p, []),
+    "vsa_invert_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "vsa_invert_indices": (ctypes.c_int, [_p, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, _p, _p, _p,
+                                          ctypes.c_size_t, _p]),
+    "vsa_fwd_check": (ctypes.c_int, [ctypes.POINTER(_FwdArgs)]),
+    "vsa_fwd": (ctypes.c_int, [ctypes.POINTER(_FwdArgs), _p]),
+    "vsa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 3),
+    "vsa_bwd_workspace_layout": (None, [ctypes.c_int] * 3 + [ctypes.POINTER(ctypes.c_size_t)] * 3),
+    "vsa_bwd_check": (ctypes.c_int, [ctypes.POINTER(_BwdArgs)]),
+    "vsa_bwd": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), _p]),
+    "vsa_bwd_stage": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), ctypes.c_int, _p]),
+    "vsa_bwd_order": (ctypes.c_int, [_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     _p, _p]),
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def is_built() -> bool:
+    return os.path.exists(_LIB_PATH)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it is not built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m "
+                               "block_sparse_attention_attn_amd.build` (needs hipcc)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        msg = L.vsa_last_error().decode()
+        raise RuntimeError(f"{what}: {L.vsa_status_string(status).decode()}: {msg}")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need_gpu(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise RuntimeError(f"{name} must be a GPU tensor (this library has no CPU path)")
+
+
+def _act(t: torch.Tensor, name: str, shape) -> None:
+    _need_gpu(t, name)
+    if t.dtype != torch.bfloat16:
+        raise RuntimeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4 or tuple(t.shape) != tuple(shape):
+        raise RuntimeError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+
+
+def _idx(t: torch.Tensor, name: str) -> torch.Tensor:
+    """Metadata: an integer GPU tensor, converted to contiguous int32 (value-preserving)."""
+    _need_gpu(t, name)
+    if t.dtype not in (torch.int32, torch.int64):
+        raise RuntimeError(f"{name} must be int32 or int64, got {t.dtype}")
+    return t.to(torch.int32).contiguous()
+
+
+def is_supported(q: torch.Tensor, variable_block_sizes: torch.Tensor) -> bool:
+    """Static facts only (never tensor contents): built, GPU tensors, bf16, 4-D, head_dim 128,
+    contiguous, integer vbs, S == 64 * num_kv_blocks. Any block count >= 1 is allowed."""
+    if not is_built() or not q.is_cuda or not variable_block_sizes.is_cuda:
+        return False
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[-1] != HEAD_DIM:
+        return False
+    if not q.is_contiguous():
+        return False
+    if variable_block_sizes.dtype not in (torch.int32, torch.int64):
+        return False
+    nb = variable_block_sizes.numel()
+    return nb > 0 and q.shape[2] == BLOCK * nb
+
+
+def invert_workspace_bytes(batch: int, heads: int, nq: int, nkv: int) -> int:
+    return int(lib().vsa_invert_workspace_bytes(batch, heads, nq, nkv))
+
+
+def invert_indices(q2k_idx: torch.Tensor, q2k_num: torch.Tensor, num_kv_blocks: int,
+                   workspace: Optional[torch.Tensor] = None,
+                   out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """q2k ``[B, H, nq, topk]`` / ``[B, H, nq]`` -> k2q ``[B, H, nkv, nq]`` (ascending, 0-padded)
+    and ``[B, H, nkv]``, int32, bit-exact."""
+    idx = _idx(q2k_idx, "q2k_idx")
+    num = _idx(q2k_num, "q2k_num")
+    if idx.dim() != 4 or num.dim() != 3 or tuple(num.shape) != tuple(idx.shape[:3]):
+        raise RuntimeError(f"q2k_idx {tuple(idx.shape)} / q2k_num {tuple(num.shape)}: expected "
+                           "[B, H, nq, topk] and [B, H, nq]")
+    B, H, nq, topk = idx.shape
+    dev = idx.device
+    if out is None:
+        k2q_idx = torch.empty((B, H, num_kv_blocks, nq), dtype=torch.int32, device=dev)
+        k2q_num = torch.empty((B, H, num_kv_blocks), dtype=torch.int32, device=dev)
+    else:
+        k2q_idx, k2q_num = out
+    need = invert_workspace_bytes(B, H, nq, num_kv_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().vsa_invert_indices(idx.data_ptr(), num.data_ptr(), B, H, nq, topk, num_kv_blocks,
+                                  k2q_idx.data_ptr(), k2q_num.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "vsa_invert_indices")
+    return k2q_idx, k2q_num
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Tensor,
+            q2k_num: torch.Tensor, variable_block_sizes: torch.Tensor,
+            sm_scale: Optional[float] = None,
+            out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Block-sparse forward: returns ``(o bf16 [B,H,S,128], lse fp32 [B,H,S] M form)``."""
+    _need_gpu(q, "q")
+    if q.dim() != 4:
+        raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
+    B, H, S, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _act(t, n, (B, H, S, D))
+    idx = _idx(q2k_idx, "q2k_idx")
+    num = _idx(q2k_num, "q2k_num")
+    vbs = _idx(variable_block_sizes, "variable_block_sizes")
+    nb = vbs.numel()
+    if idx.dim() != 4:
+        idx = idx.view(B, H, -1, idx.shape[-1])
+    if num.dim() != 3:
+        num = num.view(B, H, -1)
+    if idx.shape[2] != nb or num.shape[2] != nb:
+        raise RuntimeError(f"q2k metadata must have num_kv_blocks = {nb} q blocks per (b, h)")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    a = _FwdArgs(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), num.data_ptr(),
+                 vbs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, S, D, nb, idx.shape[-1],
+                 float(sm_scale))
+    _check(lib().vsa_fwd(ctypes.byref(a), _stream(q.device)), "vsa_fwd")
+    return o, lse
+
+
+def bwd_workspace_bytes(batch: int, heads: int, seqlen: int) -> int:
+    return int(lib().vsa_bwd_workspace_bytes(batch, heads, seqlen))
+
+
+def bwd_workspace_layout(batch: int, heads: int, seqlen: int):
+    """Byte offsets (dq accumulator, Delta, order) inside the backward workspace."""
+    offs = [ctypes.c_size_t() for _ in range(3)]
+    lib().vsa_bwd_workspace_layout(batch, heads, seqlen, *[ctypes.byref(o) for o in offs])
+    return tuple(int(o.value) for o in offs)
+
+
+def bwd_order(k2q_num: torch.Tensor, bin_width: int = 8,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Length-binned work order ``[B*H*nb]`` int32 of item ids (b*H + h)*nb + kv."""
+    num = _idx(k2q_num, "k2q_num")
+    if num.dim() != 3:
+        raise RuntimeError("k2q_num must be [B, H, nb]")
+    B, H, nb = num.shape
+    order = out if out is not None else torch.empty(B * H * nb, dtype=torch.int32,
+                                                    device=num.device)
+    _check(lib().vsa_bwd_order(num.data_ptr(), B, H, nb, bin_width, order.data_ptr(),
+                               _stream(num.device)), "vsa_bwd_order")
+    return order
+
+
+class BwdPlan:
+    """A checked, ready-to-launch backward call over fixed tensors (argument marshalling only).
+
+    ``run()`` enqueues the whole backward (``vsa_bwd``); ``stage(i)`` enqueues one of its stages
+    (``vsa_bwd_stage``: PREPROCESS=0, ORDER=1, MAIN=2, POSTPROCESS=3), all on the current stream.
+    The plan keeps references to every tensor it points at.
+    """
+
+    PREPROCESS, ORDER, MAIN, POSTPROCESS = 0, 1, 2, 3
+
+    def __init__(self, grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
+                 sm_scale=None, order=None, workspace=None, out=None):
+        _need_gpu(q, "q")
+        if q.dim() != 4:
+            raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
+        B, H, S, D = q.shape
+        for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (grad_o, "grad_o")):
+            _act(t, n, (B, H, S, D))
+        _need_gpu(lse, "lse")
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * S:
+            raise RuntimeError(f"lse must be contiguous float32 holding [B, H, S] = {B * H * S} "
+                               f"values, got {lse.dtype} with {lse.numel()}")
+        idx = _idx(k2q_idx, "k2q_idx")
+        num = _idx(k2q_num, "k2q_num")
+        vbs = _idx(variable_block_sizes, "variable_block_sizes")
+        nb = vbs.numel()
+        if S != BLOCK * nb:
+            raise RuntimeError(f"seqlen {S} must equal num_kv_blocks ({nb}) * {BLOCK}")
+        if idx.dim() not in (2, 4) or idx.numel() != B * H * nb * idx.shape[-1]:
+            raise RuntimeError(f"k2q_idx has shape {tuple(idx.shape)}, expected "
+                               f"[{B},{H},{nb},max_q] or [{B * H * nb},max_q]")
+        if num.numel() != B * H * nb:
+            raise RuntimeError(f"k2q_num must hold {B * H * nb} counts, got {num.numel()}")
+        if order is not None:
+            order = _idx(order, "order")
+            if order.numel() != B * H * nb:
+                raise RuntimeError(f"order must hold {B * H * nb} item ids")
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        if workspace is None:
+            workspace = torch.empty(bwd_workspace_bytes(B, H, S), dtype=torch.uint8,
+                                    device=q.device)
+        self.dq, self.dk, self.dv = out
+        self.workspace = workspace
+        self.device = q.device
+        self._keep = (grad_o, q, k, v, o, lse, idx, num, vbs, order)
+        self.args = _BwdArgs(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             grad_o.data_ptr(), lse.data_ptr(), idx.data_ptr(), num.data_ptr(),
+                             vbs.data_ptr(), _ptr(order), self.dq.data_ptr(), self.dk.data_ptr(),
+                             self.dv.data_ptr(), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), B, H, S, D, nb,
+                             idx.shape[-1], float(sm_scale))
+        self._ref = ctypes.byref(self.args)
+        _check(lib().vsa_bwd_check(self._ref), "vsa_bwd")
+
+    def run(self):
+        _check(lib().vsa_bwd(self._ref, _stream(self.device)), "vsa_bwd")
+        return self.dq, self.dk, self.dv
+
+    def stage(self, i: int):
+        _check(lib().vsa_bwd_stage(self._ref, i, _stream(self.device)), "vsa_bwd_stage")
+
+    def delta(self) -> torch.Tensor:
+        """The workspace's Delta region as fp32 [B, H, S] (valid after PREPROCESS)."""
+        a = self.args
+        _, off, _ = bwd_workspace_layout(a.batch, a.heads, a.seqlen)
+        n = a.batch * a.heads * a.seqlen
+        return self.workspace[off:off + 4 * n].view(torch.float32).view(a.batch, a.heads, a.seqlen)
+
+
+def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      o: torch.Tensor, lse: torch.Tensor, k2q_idx: torch.Tensor,
+                      k2q_num: torch.Tensor, variable_block_sizes: torch.Tensor,
+                      sm_scale: Optional[float] = None, order: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Backward from k2q metadata (``[B, H, nb, max_q_blocks]`` or ``[B*H*nb, max_q_blocks]``
+    plus ``[B, H, nb]`` counts). Returns ``(dq, dk, dv)`` bf16."""
+    return BwdPlan(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
+                   sm_scale=sm_scale, order=order, workspace=workspace, out=out).run()
+
+
+def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
+             sm_scale: Optional[float] = None):
+    """Backward from the forward's q2k metadata: inverts to k2q on the GPU, then runs
+    :func:`backward_from_k2q`. Returns ``(dq, dk, dv)``."""
+    B, H = q.shape[0], q.shape[1]
+    idx = _idx(q2k_idx, "q2k_idx")
+    num = _idx(q2k_num, "q2k_num")
+    if idx.dim() != 4:
+        idx = idx.view(B, H, -1, idx.shape[-1])
+    if num.dim() != 3:
+        num = num.view(B, H, -1)
+    nb = variable_block_sizes.numel()
+    k2q_idx, k2q_num = invert_indices(idx, num, nb)
+    return backward_from_k2q(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
+                             sm_scale=sm_scale)

@@ -1,0 +1,155 @@
+// vsa_device.h -- device-side building blocks shared by the gfx950 kernels of the 64-token
+// block-sparse attention library: vector types, MFMA wrappers, the LDS tile swizzles, the
+// transposing LDS read and the global->LDS copy.
+//
+// Lane layouts (verified on gfx950 with an in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] B[16x32]
+//     A: lane l holds A[m = l%32][k = 8*(l/32) + j], j = 0..7 (8 bf16)
+//     B: lane l holds B[k = 8*(l/32) + j][n = l%32]
+//     D: lane l holds D[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32], i = 0..15 (16 fp32)
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] B[32x16]
+//     A: lane l holds A[m = l%16][k = 8*(l/16) + j]; B: B[k = 8*(l/16) + j][n = l%16]
+//     D: lane l holds D[m = 4*(l/16) + i][n = l%16], i = 0..3
+//   ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element j (j = 0..3) as
+//     element i%4 of the 8 bytes addressed by lane 4*j + i/4 of the group. So when lanes
+//     4r..4r+3 address the 16 contiguous bf16 of row r (r = 0..3), lane i gets column i of that
+//     4 x 16 block: a transposed read.
+//   global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l.
+//
+// The contraction index of an MFMA may be permuted freely as long as A and B use the same
+// permutation; the kernels use that to feed a D fragment straight back as an operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa {
+
+constexpr int BLOCK = 64;      // tokens per sparse block
+constexpr int HEAD_DIM = 128;  // head dimension
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+#define VSA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two transposed 8-byte LDS reads joined into one 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
+  union {
+    s16x4 h[2];
+    bf16x8 v;
+  } u;
+  u.h[0] = lo;
+  u.h[1] = hi;
+  return u.v;
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const VSA_LDS void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA_LDS s16x4*)p);
+}
+
+// Eight fp32 values to one bf16x8 operand, round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
+                                        float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (bf16)a0;
+  r[1] = (bf16)a1;
+  r[2] = (bf16)a2;
+  r[3] = (bf16)a3;
+  r[4] = (bf16)a4;
+  r[5] = (bf16)a5;
+  r[6] = (bf16)a6;
+  r[7] = (bf16)a7;
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// LDS tile formats
+// ---------------------------------------------------------------------------------------------
+// A [64 rows][128] bf16 tile (Q, dO, K, V) occupies 16 KiB = 64 rows x 16 chunks of 16 bytes.
+// Chunk cc of row r is stored at chunk slot r*16 + (cc ^ swz128(r)). swz128 permutes the low
+// four row bits (b3 b2 b1 b0) -> (b3 b1 b0 b2): a bijection on any 16 aligned rows, so 16 lanes
+// reading the same chunk of 16 consecutive rows hit 16 different bank groups; and for 4 aligned
+// rows it XORs the row's low two bits into chunk bits 1..2, so a transposed read of two adjacent
+// chunks of 4 aligned rows touches 8 different bank groups.
+__device__ __forceinline__ int swz128(int r) {
+  return (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1);
+}
+__device__ __forceinline__ int tile_byte(int r, int cc) {  // byte offset of chunk cc of row r
+  return (r * 16 + (cc ^ swz128(r))) * 16;
+}
+// Byte offset of element (r, c) (c = column 0..127, a multiple of 4 for 8-byte accesses).
+__device__ __forceinline__ int tile_elem_byte(int r, int c) {
+  return tile_byte(r, c >> 3) + (c & 7) * 2;
+}
+
+// A [64 rows][64] bf16 tile (dS^T) occupies 8 KiB = 64 rows x 8 chunks. Chunk cc of row r is at
+// slot r*8 + (cc ^ swz64(r)); swz64 maps row bits (b3 b2 b1) -> chunk bits (2 0 1). Rows of one
+// parity share bank halves (128-byte rows), so the permutation runs on r >> 1.
+__device__ __forceinline__ int swz64(int r) {
+  return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2);
+}
+__device__ __forceinline__ int ds_elem_byte(int r, int c) {
+  return (r * 8 + ((c >> 3) ^ swz64(r))) * 16 + (c & 7) * 2;
+}
+
+// Read-only metadata (index lists, counts, block sizes) through the constant address space, so
+// the compiler issues scalar loads: they count against lgkmcnt, not vmcnt, and a read of a list
+// entry never waits for the vector memory traffic (atomics, prefetches) in flight.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, size_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+// One global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes land at
+// LDS byte address lds_base + 16*l. Issued through inline assembly so the compiler does not track
+// it; callers wait with an explicit s_waitcnt vmcnt before a barrier that publishes the tile.
+// M0 is saved and restored around the DMA (the compiler does not allow it on a clobber list).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(base)
+      : "memory");
+}
+
+// Index of the calling wave inside its workgroup, as a value the compiler knows to be uniform.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ uint32_t lds_addr(const VSA_LDS void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Copy one [64][128] bf16 tile (row stride 128 elements) from global memory into the swizzled LDS
+// format. A wave moves 64 lanes x 16 bytes per DMA; NPARTS waves share the tile, wave `part`
+// issuing slices part, part + NPARTS, ... of the tile's 16 one-KiB slices.
+template <int NPARTS>
+__device__ __forceinline__ void tile_load_async(const bf16* __restrict__ g, VSA_LDS char* lds,
+                                                int lane, int part) {
+#pragma unroll
+  for (int i = 0; i < 16 / NPARTS; ++i) {
+    const int u = part + i * NPARTS;
+    const int slot = u * 64 + lane;  // chunk slot this lane fills
+    const int r = slot >> 4;
+    const int cc = (slot & 15) ^ swz128(r);
+    dma16(g + r * HEAD_DIM + cc * 8, lds_addr(lds + u * 1024));
+  }
+}
+
+}  // namespace vsa

@@ -1,0 +1,78 @@
+// vsa_kernels.h -- internal launch interface between the C-ABI entry points (vsa_api.hip) and the
+// gfx950 kernels. Not part of the public ABI. All pointers are device pointers; every launcher
+// enqueues on `stream` and returns without synchronizing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "vsa_device.h"
+
+namespace vsa {
+
+// ---- invert_indices: q2k -> k2q, sorted ascending, bit-exact ----
+void launch_invert(const int32_t* q2k_idx, const int32_t* q2k_num, int BH, int nq, int topk,
+                   int nkv, int32_t* k2q_idx, int32_t* k2q_num, uint32_t* bitmap,
+                   hipStream_t stream);
+size_t invert_bitmap_bytes(int BH, int nq, int nkv);
+
+// ---- forward: o (bf16) and lse (fp32, base-2 M form) ----
+struct FwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const int32_t* q2k_idx;  // [BH, nq, q2k_stride]
+  const int32_t* q2k_num;  // [BH, nq]
+  const int32_t* vbs;      // [nkv]
+  bf16* o;
+  float* lse;
+  int BH, S, nb, q2k_stride;
+  float scale_log2;
+};
+void launch_fwd(const FwdParams& p, hipStream_t stream);
+
+// ---- backward preprocess: Delta, dQ accumulator zeroing, zero dK/dV rows of empty kv blocks ----
+struct BwdPreParams {
+  const bf16* o;
+  const bf16* dout;
+  const int32_t* k2q_num;  // [BH, nb]
+  float* delta;            // [BH, S]
+  float* dqaccum;          // [BH, S, 128]
+  bf16* dk;
+  bf16* dv;
+  int BH, S, nb;
+};
+void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream);
+
+// ---- backward work order: per (b, h) a length-binned permutation of its kv items ----
+constexpr int ORDER_MIN_KV_BLOCKS = 1024;  // below: identity order
+constexpr int ORDER_MAX_KV_BLOCKS = 16384; // LDS holds one 32-bit key per kv block
+void launch_bwd_order(const int32_t* k2q_num, int BH, int nb, int bin_width, int32_t* order,
+                      hipStream_t stream);
+
+// ---- backward main kernel ----
+struct BwdMainParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* dout;
+  const float* lse;
+  const float* delta;
+  const int32_t* k2q_idx;
+  const int32_t* k2q_num;
+  const int32_t* vbs;
+  const int32_t* order;  // nullptr: identity
+  float* dqaccum;
+  bf16* dk;
+  bf16* dv;
+  int S, nb, max_q_blocks, total_items, items_per_xcd;
+  float scale_log2, sm_scale;
+};
+void launch_bwd_main(const BwdMainParams& p, hipStream_t stream);
+
+// ---- backward postprocess: dq = bf16(sm_scale * dqaccum) ----
+void launch_bwd_post(const float* dqaccum, bf16* dq, size_t n_elems, float sm_scale,
+                     hipStream_t stream);
+
+}  // namespace vsa

@@ -1,0 +1,138 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports every entry point
+the public header declares, sizes workspaces as documented, and rejects bad arguments with the
+right status before anything is launched (validation never touches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_attn_amd as V
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+VSA_OK, VSA_EINVAL, VSA_EUNSUPPORTED, VSA_ELAUNCH = 0, 1, 2, 3
+
+pytestmark = pytest.mark.skipif(not V.is_built(), reason="libvsa.so not built (run build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert "vsa_bwd" in names and "vsa_invert_indices" in names and "vsa_fwd" in names
+    handle = ctypes.CDLL(V.library_path())
+    for n in names:
+        assert hasattr(handle, n), f"libvsa.so does not export {n}"
+    # and the binding declares exactly those
+    assert sorted(V._SIGNATURES) == names
+
+
+def test_status_strings():
+    L = V.lib()
+    for st, word in ((0, b"OK"), (1, b"EINVAL"), (2, b"EUNSUPPORTED"), (3, b"ELAUNCH")):
+        assert word in L.vsa_status_string(st)
+    assert b"unknown" in L.vsa_status_string(42)
+
+
+def test_workspace_sizes_and_layout():
+    B, H, S = 1, 8, 32768
+    dq_off, delta_off, order_off = V.bwd_workspace_layout(B, H, S)
+    assert dq_off == 0
+    assert delta_off == B * H * S * 128 * 4
+    assert order_off == delta_off + B * H * S * 4
+    assert V.bwd_workspace_bytes(B, H, S) == order_off + B * H * (S // 64) * 4
+    # 256-byte alignment of every region with an odd size
+    d, de, o = V.bwd_workspace_layout(1, 1, 64)
+    assert de % 256 == 0 and o % 256 == 0
+    assert V.bwd_workspace_bytes(0, 1, 64) == 0
+    assert V.invert_workspace_bytes(2, 3, 100, 50) == ((2 * 3 * 50 * 4 * 4 + 255) // 256) * 256
+    assert V.invert_workspace_bytes(1, 1, 0, 1) == 0
+
+
+def _bwd_args(**over):
+    fake = 0x10000  # never dereferenced: validation fails or we do not launch
+    a = dict(q=fake, k=fake, v=fake, o=fake, dout=fake, lse=fake, k2q_idx=fake, k2q_num=fake,
+             vbs=fake, order=None, dq=fake, dk=fake, dv=fake, workspace=fake,
+             workspace_bytes=V.bwd_workspace_bytes(1, 2, 256), batch=1, heads=2, seqlen=256,
+             head_dim=128, num_kv_blocks=4, max_q_blocks=4, sm_scale=0.088)
+    a.update(over)
+    return V._BwdArgs(**a)
+
+
+def _check(args):
+    return V.lib().vsa_bwd_check(ctypes.byref(args))
+
+
+def test_bwd_check_accepts_a_valid_call():
+    assert _check(_bwd_args()) == VSA_OK
+    assert _check(_bwd_args(num_kv_blocks=3, seqlen=192, workspace_bytes=V.bwd_workspace_bytes(1, 2, 192))) == VSA_OK  # odd nb ok
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=64), VSA_EUNSUPPORTED),
+    (dict(seqlen=250), VSA_EINVAL),
+    (dict(num_kv_blocks=0, seqlen=0), VSA_EINVAL),
+    (dict(batch=0), VSA_EINVAL),
+    (dict(heads=-1), VSA_EINVAL),
+    (dict(max_q_blocks=0), VSA_EINVAL),
+    (dict(sm_scale=float("nan")), VSA_EINVAL),
+    (dict(sm_scale=float("inf")), VSA_EINVAL),
+    (dict(q=None), VSA_EINVAL),
+    (dict(lse=None), VSA_EINVAL),
+    (dict(k2q_idx=None), VSA_EINVAL),
+    (dict(vbs=None), VSA_EINVAL),
+    (dict(dv=None), VSA_EINVAL),
+    (dict(workspace=None), VSA_EINVAL),
+    (dict(workspace_bytes=1024), VSA_EINVAL),
+])
+def test_bwd_check_rejects(over, status):
+    assert _check(_bwd_args(**over)) == status
+    assert V.lib().vsa_last_error() != b""
+
+
+def test_bwd_and_stage_fail_before_launch_on_bad_args():
+    L = V.lib()
+    a = _bwd_args(head_dim=96)
+    assert L.vsa_bwd(ctypes.byref(a), None) == VSA_EUNSUPPORTED
+    assert L.vsa_bwd_stage(ctypes.byref(a), 2, None) == VSA_EUNSUPPORTED
+    assert L.vsa_bwd_stage(ctypes.byref(_bwd_args()), 7, None) == VSA_EINVAL
+
+
+def test_fwd_check():
+    fake = 0x10000
+    base = dict(q=fake, k=fake, v=fake, q2k_idx=fake, q2k_num=fake, vbs=fake, o=fake, lse=fake,
+                batch=1, heads=1, seqlen=256, head_dim=128, num_kv_blocks=4, q2k_stride=2,
+                sm_scale=0.088)
+    L = V.lib()
+    assert L.vsa_fwd_check(ctypes.byref(V._FwdArgs(**base))) == VSA_OK
+    for over, st in ((dict(head_dim=256), VSA_EUNSUPPORTED), (dict(q2k_stride=0), VSA_EINVAL),
+                     (dict(o=None), VSA_EINVAL), (dict(seqlen=255), VSA_EINVAL)):
+        assert L.vsa_fwd_check(ctypes.byref(V._FwdArgs(**{**base, **over}))) == st
+        assert L.vsa_fwd(ctypes.byref(V._FwdArgs(**{**base, **over})), None) == st
+
+
+def test_invert_and_order_validation():
+    L = V.lib()
+    fake = 0x10000
+    assert L.vsa_invert_indices(fake, fake, 1, 1, 0, 2, 4, fake, fake, fake, 1 << 20, None) == VSA_EINVAL
+    assert L.vsa_invert_indices(None, fake, 1, 1, 4, 2, 4, fake, fake, fake, 1 << 20, None) == VSA_EINVAL
+    assert L.vsa_invert_indices(fake, fake, 1, 1, 4, 2, 4, fake, fake, fake, 0, None) == VSA_EINVAL
+    assert L.vsa_bwd_order(fake, 1, 1, 20000, 8, fake, None) == VSA_EUNSUPPORTED
+    assert L.vsa_bwd_order(fake, 1, 1, 1024, 0, fake, None) == VSA_EINVAL
+    assert L.vsa_bwd_order(None, 1, 1, 1024, 8, fake, None) == VSA_EINVAL
+
+
+def test_python_layer_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
+    vbs = torch.full((1,), 64, dtype=torch.int32)
+    assert not V.is_supported(q, vbs)
+    with pytest.raises(RuntimeError, match="GPU"):
+        V.forward(q, q, q, torch.zeros(1, 1, 1, 1, dtype=torch.int32),
+                  torch.ones(1, 1, 1, dtype=torch.int32), vbs)

@@ -1,0 +1,349 @@
+"""GPU parity tests: the HIP path through the C ABI against the float64 CPU oracle.
+
+Gates (per tensor):
+  * index metadata (k2q lists and counts, work order): bit-exact;
+  * gradients and o: max|gpu - ref| / max|ref| <= 1e-2, and mean|gpu - ref| <= 1e-3 * mean|ref|
+    beyond the irreducible rounding of the bf16 outputs, i.e.
+    mean|gpu - ref| <= 1e-3 * mean|ref| + mean|bf16(ref) - ref|  (ref = unrounded oracle);
+    the absolute mean of the FastVideo test page (mean|diff| <= 1e-3) is reported too;
+  * lse: max|gpu - ref| <= 1e-4 (absolute, base-2 units);
+  * exact zeros where the method defines them (unselected kv blocks, padded kv rows, empty q rows).
+Small workloads are compared in full; the 32k and 65k-token workloads on sampled blocks, each
+computed by the oracle one block at a time, plus invariants that hold at any size.
+"""
+import itertools
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_attn_amd as V
+import workloads
+from oracle import vsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+REL_MAX_TOL = 1e-2
+MEAN_REL_TOL = 1e-3
+LSE_ABS_TOL = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert V.is_built(), "libvsa.so must be built before the GPU tests"
+    V.lib()
+
+
+def to_dev(c):
+    return {n: getattr(c, n).to(DEV) for n in ("q", "k", "v", "do", "q2k_idx", "q2k_num", "vbs")}
+
+
+def nan_like(t):
+    out = torch.empty_like(t)
+    if out.dtype.is_floating_point:
+        out.fill_(float("nan"))
+    else:
+        out.fill_(-7)
+    return out
+
+
+def check_close(name, got, ref, report=None):
+    """got: GPU tensor (any float dtype); ref: float64 numpy array of the same shape."""
+    g = got.detach().to("cpu", torch.float64).numpy()
+    assert g.shape == ref.shape, f"{name}: shape {g.shape} vs {ref.shape}"
+    assert np.isfinite(g).all(), f"{name}: non-finite values"
+    diff = np.abs(g - ref)
+    max_ref = max(np.abs(ref).max(), 1e-30)
+    mean_ref = np.abs(ref).mean()
+    rel_max = diff.max() / max_ref
+    mean_abs = diff.mean()
+    rounding = np.abs(O.bf16_rne(ref) - ref).mean()
+    line = dict(tensor=name, rel_max=float(rel_max), mean_abs=float(mean_abs),
+                mean_ref=float(mean_ref), mean_rel=float(mean_abs / max(mean_ref, 1e-30)),
+                mean_rel_vs_bf16_ref=float(np.abs(g - O.bf16_rne(ref)).mean() / max(mean_ref, 1e-30)),
+                page_abs_mean_ok=bool(mean_abs <= 1e-3))
+    say("  " + json.dumps(line))
+    if report is not None:
+        report.append(line)
+    assert rel_max <= REL_MAX_TOL, f"{name}: max|diff|/max|ref| = {rel_max:.3e}"
+    assert mean_abs <= MEAN_REL_TOL * mean_ref + rounding, (
+        f"{name}: mean|diff| = {mean_abs:.3e} > 1e-3*mean|ref| ({mean_ref:.3e}) + bf16 rounding "
+        f"{rounding:.3e}")
+
+
+# -----------------------------------------------------------------------------------------------
+# invert_indices (bit-exact)
+# -----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_invert_bit_exact(n):
+    c = workloads.config(n)
+    say(f"[invert] config {n}")
+    d = to_dev(c)
+    out = (nan_like(torch.empty(c.B, c.H, c.nb, c.nb, dtype=torch.int32, device=DEV)),
+           nan_like(torch.empty(c.B, c.H, c.nb, dtype=torch.int32, device=DEV)))
+    k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb, out=out)
+    torch.cuda.synchronize()
+    ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
+    assert np.array_equal(k2q_num.cpu().numpy(), rnum)
+    assert np.array_equal(k2q_idx.cpu().numpy(), ridx)
+
+
+def test_invert_duplicates_counts_and_rectangular():
+    """Duplicate kv ids count once; counts below the row width; nq != nkv."""
+    g = torch.Generator().manual_seed(9)
+    B, H, nq, nkv, K = 2, 3, 40, 70, 9
+    idx = torch.randint(0, nkv, (B, H, nq, K), generator=g, dtype=torch.int32)
+    idx[..., 1] = idx[..., 0]  # duplicates
+    num = torch.randint(0, K + 1, (B, H, nq), generator=g, dtype=torch.int32)
+    say("[invert] duplicates / rectangular")
+    k2q_idx, k2q_num = V.invert_indices(idx.to(DEV), num.to(DEV), nkv)
+    torch.cuda.synchronize()
+    ridx, rnum = O.invert_indices(idx, num, nkv)
+    assert np.array_equal(k2q_num.cpu().numpy(), rnum)
+    assert np.array_equal(k2q_idx.cpu().numpy(), ridx)
+
+
+# -----------------------------------------------------------------------------------------------
+# work order (bit-exact)
+# -----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,nb,bw", [(1, 8, 1024, 8), (2, 3, 3000, 12), (1, 2, 16384, 8),
+                                       (1, 1, 5, 8)])
+def test_order_bit_exact(B, H, nb, bw):
+    g = torch.Generator().manual_seed(nb)
+    num = torch.randint(0, 300, (B, H, nb), generator=g, dtype=torch.int32)
+    say(f"[order] B={B} H={H} nb={nb} bin={bw}")
+    got = V.bwd_order(num.to(DEV), bw)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.work_order(num, bw))
+
+
+# -----------------------------------------------------------------------------------------------
+# forward
+# -----------------------------------------------------------------------------------------------
+
+def _fwd_compare(c, d, o, lse, qblocks=None):
+    ro, rl = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale, qblocks=qblocks)
+    if qblocks is None:
+        check_close("o", o, ro)
+        got_l = lse.cpu().double().numpy()
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(got_l), fin)
+        assert np.all(got_l[~fin] == rl[~fin])
+        assert np.abs(got_l[fin] - rl[fin]).max() <= LSE_ABS_TOL
+    else:
+        for b, h, qb in qblocks:
+            rows = slice(qb * 64, (qb + 1) * 64)
+            check_close(f"o[{b},{h},{qb}]", o[b, h, rows], ro[b, h, rows])
+            assert np.abs(lse[b, h, rows].cpu().double().numpy() - rl[b, h, rows]).max() <= LSE_ABS_TOL
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_forward_parity(n):
+    c = workloads.config(n)
+    d = to_dev(c)
+    say(f"[forward] config {n}")
+    o = nan_like(d["q"])
+    lse = nan_like(torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=DEV))
+    V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"], out=(o, lse))
+    torch.cuda.synchronize()
+    _fwd_compare(c, d, o, lse)
+
+
+# -----------------------------------------------------------------------------------------------
+# backward on small workloads, o and lse from the oracle (as the FastVideo test does)
+# -----------------------------------------------------------------------------------------------
+
+def _bwd_small(c, label):
+    d = to_dev(c)
+    ro, rl = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    o = torch.from_numpy(O.bf16_rne(ro)).to(torch.bfloat16).to(DEV)
+    lse = torch.from_numpy(rl).to(torch.float32).to(DEV)
+    ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
+    k2q_idx = torch.from_numpy(ridx).to(DEV)
+    k2q_num = torch.from_numpy(rnum).to(DEV)
+    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S),), 0xFF, dtype=torch.uint8, device=DEV)
+    out = (nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"]))
+    say(f"[backward] {label}")
+    plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                     workspace=ws, out=out)
+    dq, dk, dv = plan.run()
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert got.dtype == torch.bfloat16
+        check_close(name, got, ref)
+    # Delta from the preprocess, on the bf16 o it was given
+    rdelta = O.delta(o.cpu(), c.do)
+    gd = plan.delta().cpu().double().numpy()
+    assert np.abs(gd - rdelta).max() <= 1e-5 * max(1.0, np.abs(rdelta).max())
+    return dq, dk, dv, rdq, rdk, rdv
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_backward_parity(n):
+    c = workloads.config(n)
+    dq, dk, dv, *_ = _bwd_small(c, f"config {n}")
+    if n == 2:
+        dk, dv = dk.float().cpu(), dv.float().cpu()
+        for kb in (4, 11):  # selected by no q block
+            assert torch.all(dk[:, :, kb * 64:(kb + 1) * 64] == 0)
+            assert torch.all(dv[:, :, kb * 64:(kb + 1) * 64] == 0)
+        for kb, nvalid in ((7, 50), (15, 37)):  # padded kv rows
+            assert torch.all(dk[:, :, kb * 64 + nvalid:(kb + 1) * 64] == 0)
+            assert torch.all(dv[:, :, kb * 64 + nvalid:(kb + 1) * 64] == 0)
+
+
+EDGE_CASES = {
+    # name: (B, H, nb, topk, vbs, kv_pool, empty_q_blocks)
+    "odd_blocks_ragged": (2, 3, 5, 3, [64, 17, 64, 40, 1], None, ()),
+    "dense_all_selected": (1, 2, 8, 8, None, None, ()),
+    "single_block": (1, 1, 1, 1, [29], None, ()),
+    "zero_valid_block": (1, 2, 6, 3, [64, 0, 64, 64, 33, 64], None, ()),
+    "empty_q_blocks": (2, 2, 6, 2, [64, 64, 50, 64, 64, 64], None, ((0, 1, 2), (1, 0, 5))),
+    "topk_7_ragged_tail": (1, 2, 8, 7, [64, 64, 64, 64, 64, 64, 64, 23], None, ()),
+    "pool_excludes_three": (1, 2, 12, 4, None, [0, 1, 2, 4, 5, 7, 8, 10, 11], ()),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE_CASES))
+def test_backward_edge_cases(name):
+    B, H, nb, topk, vbs, pool, empty = EDGE_CASES[name]
+    c = workloads.make_case(B, H, nb, topk, seed=17, vbs=vbs, kv_pool=pool, name=name)
+    for b, h, qb in empty:
+        c.q2k_num[b, h, qb] = 0
+    # forward first: also the GPU forward's o/lse on these shapes
+    d = to_dev(c)
+    say(f"[forward] edge case {name}")
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    torch.cuda.synchronize()
+    _fwd_compare(c, d, o, lse)
+    dq, dk, dv, rdq, rdk, rdv = _bwd_small(c, f"edge case {name}")
+    # exact zeros wherever the oracle is exactly zero (unselected, padded, empty rows)
+    for got, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
+        zero = ref == 0
+        assert np.all(got.float().cpu().numpy()[zero] == 0)
+
+
+def test_backward_user_order_gives_identical_dk_dv():
+    """Any work order: the same dk/dv bits (fixed per-item summation order); dq within fp32
+    summation noise."""
+    c = workloads.config(2)
+    d = to_dev(c)
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
+    say("[backward] identity vs reversed order")
+    a = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"])
+    rev = torch.arange(c.B * c.H * c.nb - 1, -1, -1, dtype=torch.int32, device=DEV)
+    b = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                            order=rev)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    rel = (a[0].float() - b[0].float()).abs().max() / a[0].float().abs().max()
+    assert rel <= 2e-2
+
+
+def test_nondefault_stream():
+    c = workloads.config(1)
+    d = to_dev(c)
+    s = torch.cuda.Stream()
+    say("[stream] side stream")
+    with torch.cuda.stream(s):
+        o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+        dq, dk, dv = V.backward(d["do"], d["q"], d["k"], d["v"], o, lse, d["q2k_idx"],
+                                d["q2k_num"], d["vbs"])
+    s.synchronize()
+    rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    check_close("dq", dq, rdq)
+    check_close("dk", dk, rdk)
+    check_close("dv", dv, rdv)
+
+
+# -----------------------------------------------------------------------------------------------
+# full-size workloads: sampled blocks + invariants
+# -----------------------------------------------------------------------------------------------
+
+def _end_to_end(c):
+    """GPU forward -> GPU invert -> GPU backward, outputs and workspace NaN-prefilled."""
+    d = to_dev(c)
+    o = nan_like(d["q"])
+    lse = nan_like(torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=DEV))
+    V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"], out=(o, lse))
+    k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
+    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S),), 0xFF, dtype=torch.uint8, device=DEV)
+    out = (nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"]))
+    plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                     workspace=ws, out=out)
+    dq, dk, dv = plan.run()
+    torch.cuda.synchronize()
+    return d, o, lse, k2q_num, plan, (dq, dk, dv)
+
+
+def _sampled_checks(c, o, lse, grads, qblocks, kvblocks):
+    dq, dk, dv = grads
+    _fwd_compare(c, None, o, lse, qblocks=qblocks)
+    sdq, sdkv = O.backward_sampled(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale,
+                                   qblocks=qblocks, kvblocks=kvblocks)
+    for (b, h, qb), ref in sdq.items():
+        check_close(f"dq[{b},{h},{qb}]", dq[b, h, qb * 64:(qb + 1) * 64], ref)
+    for (b, h, kb), (rk, rv) in sdkv.items():
+        check_close(f"dk[{b},{h},{kb}]", dk[b, h, kb * 64:(kb + 1) * 64], rk)
+        check_close(f"dv[{b},{h},{kb}]", dv[b, h, kb * 64:(kb + 1) * 64], rv)
+
+
+def _invariants(c, grads):
+    """dS rows sum to zero: per head sum_j dk_j = 0 and sum_j dv_j = sum_i dO_i (every q row here
+    has keys). Checked column-wise against the column's absolute mass."""
+    dq, dk, dv = grads
+    for g in grads:
+        assert torch.isfinite(g.float()).all()
+    dk64 = dk.double()
+    colsum = dk64.sum(dim=2).abs()
+    mass = dk64.abs().sum(dim=2)
+    assert (colsum <= 2e-3 * mass + 1e-6).all(), float((colsum / mass).max())
+    dvs = dv.double().sum(dim=2)
+    dos = c.do.to(DEV).double().sum(dim=2)
+    mass = dv.double().abs().sum(dim=2)
+    assert ((dvs - dos).abs() <= 2e-3 * mass + 1e-6).all()
+
+
+def test_config3_32k_end_to_end_sampled():
+    c = workloads.config(3)
+    say("[end-to-end] config 3 (B=1 H=8 S=32768, 25%)")
+    d, o, lse, k2q_num, plan, grads = _end_to_end(c)
+    _invariants(c, grads)
+    _sampled_checks(c, o, lse, grads, qblocks=[(0, 0, 0), (0, 3, 200), (0, 7, 511)],
+                    kvblocks=[(0, 0, 1), (0, 5, 300), (0, 7, 511)])
+
+
+def test_config4_65k_order_stability_sampled():
+    c = workloads.config(4)
+    say("[end-to-end] config 4 (B=1 H=8 S=65536, 12.5%, device work order)")
+    d, o, lse, k2q_num, plan, grads = _end_to_end(c)
+    # the library computed the length-binned order into the workspace; it matches the oracle's
+    _, _, order_off = V.bwd_workspace_layout(c.B, c.H, c.S)
+    n = c.B * c.H * c.nb
+    got_order = plan.workspace[order_off:order_off + 4 * n].view(torch.int32).cpu().numpy()
+    assert np.array_equal(got_order, O.work_order(k2q_num.cpu(), 8))
+    _invariants(c, grads)
+    # run-to-run: dk, dv bitwise; dq within summation-order noise
+    grads = tuple(t.clone() for t in grads)
+    again = plan.run()
+    torch.cuda.synchronize()
+    dq, dk, dv = grads
+    assert torch.equal(dk, again[1]) and torch.equal(dv, again[2])
+    diff = (dq.float() - again[0].float()).abs()
+    rel = float(diff.max() / dq.float().abs().max())
+    say(f"  run-to-run dq rel_max={rel:.3e} mean={float(diff.mean()):.3e}")
+    assert rel <= 2e-2 and float(diff.mean()) <= 1e-4
+    _sampled_checks(c, o, lse, grads, qblocks=[(0, 1, 7), (0, 6, 1023)],
+                    kvblocks=[(0, 2, 0), (0, 7, 777)])
