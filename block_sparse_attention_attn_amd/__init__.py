@@ -27,7 +27,7 @@ import torch
 __all__ = [
     "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
-    "bwd_workspace_bytes", "bwd_workspace_layout", "invert_workspace_bytes", "BwdPlan",
+    "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
 ]
 
 BLOCK = 64
@@ -53,11 +53,16 @@ class _FwdArgs(ctypes.Structure):
 
 class _BwdArgs(ctypes.Structure):
     _fields_ = [("q", _p), ("k", _p), ("v", _p), ("o", _p), ("dout", _p), ("lse", _p),
-                ("k2q_idx", _p), ("k2q_num", _p), ("vbs", _p), ("order", _p), ("dq", _p),
-                ("dk", _p), ("dv", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
-                ("batch", ctypes.c_int), ("heads", ctypes.c_int), ("seqlen", ctypes.c_int),
-                ("head_dim", ctypes.c_int), ("num_kv_blocks", ctypes.c_int),
-                ("max_q_blocks", ctypes.c_int), ("sm_scale", ctypes.c_float)]
+                ("k2q_idx", _p), ("k2q_num", _p), ("q2k_idx", _p), ("q2k_num", _p), ("vbs", _p),
+                ("order", _p), ("dq", _p), ("dk", _p), ("dv", _p), ("workspace", _p),
+                ("workspace_bytes", ctypes.c_size_t), ("batch", ctypes.c_int),
+                ("heads", ctypes.c_int), ("seqlen", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("num_kv_blocks", ctypes.c_int), ("max_q_blocks", ctypes.c_int),
+                ("q2k_stride", ctypes.c_int), ("sm_scale", ctypes.c_float)]
+
+
+# workspace regions of the backward (vsa_bwd_ws_region)
+WS_DELTA, WS_KV_ORDER, WS_Q_ORDER, WS_Q2K_NUM, WS_Q2K_IDX, WS_BITMAP, WS_END = range(7)
 
 
 # name -> (restype, argtypes); exactly the symbols include/vsa.h declares
@@ -70,8 +75,8 @@ _SIGNATURES = {
                                           ctypes.c_size_t, _p]),
     "vsa_fwd_check": (ctypes.c_int, [ctypes.POINTER(_FwdArgs)]),
     "vsa_fwd": (ctypes.c_int, [ctypes.POINTER(_FwdArgs), _p]),
-    "vsa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 3),
-    "vsa_bwd_workspace_layout": (None, [ctypes.c_int] * 3 + [ctypes.POINTER(ctypes.c_size_t)] * 3),
+    "vsa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "vsa_bwd_workspace_offset": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "vsa_bwd_check": (ctypes.c_int, [ctypes.POINTER(_BwdArgs)]),
     "vsa_bwd": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), _p]),
     "vsa_bwd_stage": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), ctypes.c_int, _p]),
@@ -223,15 +228,13 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
     return o, lse
 
 
-def bwd_workspace_bytes(batch: int, heads: int, seqlen: int) -> int:
-    return int(lib().vsa_bwd_workspace_bytes(batch, heads, seqlen))
+def bwd_workspace_bytes(batch: int, heads: int, seqlen: int, derive_q2k: bool = True) -> int:
+    return int(lib().vsa_bwd_workspace_bytes(batch, heads, seqlen, int(bool(derive_q2k))))
 
 
-def bwd_workspace_layout(batch: int, heads: int, seqlen: int):
-    """Byte offsets (dq accumulator, Delta, order) inside the backward workspace."""
-    offs = [ctypes.c_size_t() for _ in range(3)]
-    lib().vsa_bwd_workspace_layout(batch, heads, seqlen, *[ctypes.byref(o) for o in offs])
-    return tuple(int(o.value) for o in offs)
+def bwd_workspace_offset(batch: int, heads: int, seqlen: int, region: int) -> int:
+    """Byte offset of a backward workspace region (WS_DELTA, WS_KV_ORDER, ...)."""
+    return int(lib().vsa_bwd_workspace_offset(batch, heads, seqlen, region))
 
 
 def bwd_order(k2q_num: torch.Tensor, bin_width: int = 8,
@@ -252,14 +255,16 @@ class BwdPlan:
     """A checked, ready-to-launch backward call over fixed tensors (argument marshalling only).
 
     ``run()`` enqueues the whole backward (``vsa_bwd``); ``stage(i)`` enqueues one of its stages
-    (``vsa_bwd_stage``: PREPROCESS=0, ORDER=1, MAIN=2, POSTPROCESS=3), all on the current stream.
-    The plan keeps references to every tensor it points at.
+    (``vsa_bwd_stage``: PREPROCESS=0, INDEX=1, DKDV=2, DQ=3), all on the current stream. With
+    ``q2k_idx``/``q2k_num`` (the forward's metadata, the same selection as k2q) the library skips
+    deriving them. The plan keeps references to every tensor it points at.
     """
 
-    PREPROCESS, ORDER, MAIN, POSTPROCESS = 0, 1, 2, 3
+    PREPROCESS, INDEX, DKDV, DQ = 0, 1, 2, 3
 
     def __init__(self, grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
-                 sm_scale=None, order=None, workspace=None, out=None):
+                 sm_scale=None, order=None, workspace=None, out=None, q2k_idx=None,
+                 q2k_num=None):
         _need_gpu(q, "q")
         if q.dim() != 4:
             raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
@@ -285,23 +290,32 @@ class BwdPlan:
             order = _idx(order, "order")
             if order.numel() != B * H * nb:
                 raise RuntimeError(f"order must hold {B * H * nb} item ids")
+        qidx = qnum = None
+        if (q2k_idx is None) != (q2k_num is None):
+            raise RuntimeError("give both q2k_idx and q2k_num, or neither")
+        if q2k_idx is not None:
+            qidx = _idx(q2k_idx, "q2k_idx")
+            qnum = _idx(q2k_num, "q2k_num")
+            if qidx.numel() != B * H * nb * qidx.shape[-1] or qnum.numel() != B * H * nb:
+                raise RuntimeError(f"q2k metadata must be [{B},{H},{nb},stride] and [{B},{H},{nb}]")
         if sm_scale is None:
             sm_scale = 1.0 / math.sqrt(D)
         if out is None:
             out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         if workspace is None:
-            workspace = torch.empty(bwd_workspace_bytes(B, H, S), dtype=torch.uint8,
+            workspace = torch.empty(bwd_workspace_bytes(B, H, S, qidx is None), dtype=torch.uint8,
                                     device=q.device)
         self.dq, self.dk, self.dv = out
         self.workspace = workspace
         self.device = q.device
-        self._keep = (grad_o, q, k, v, o, lse, idx, num, vbs, order)
+        self._keep = (grad_o, q, k, v, o, lse, idx, num, qidx, qnum, vbs, order)
         self.args = _BwdArgs(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              grad_o.data_ptr(), lse.data_ptr(), idx.data_ptr(), num.data_ptr(),
-                             vbs.data_ptr(), _ptr(order), self.dq.data_ptr(), self.dk.data_ptr(),
-                             self.dv.data_ptr(), workspace.data_ptr(),
-                             workspace.numel() * workspace.element_size(), B, H, S, D, nb,
-                             idx.shape[-1], float(sm_scale))
+                             _ptr(qidx), _ptr(qnum), vbs.data_ptr(), _ptr(order),
+                             self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             B, H, S, D, nb, idx.shape[-1],
+                             qidx.shape[-1] if qidx is not None else 0, float(sm_scale))
         self._ref = ctypes.byref(self.args)
         _check(lib().vsa_bwd_check(self._ref), "vsa_bwd")
 
@@ -312,12 +326,18 @@ class BwdPlan:
     def stage(self, i: int):
         _check(lib().vsa_bwd_stage(self._ref, i, _stream(self.device)), "vsa_bwd_stage")
 
+    def region(self, r: int, count: int, dtype=torch.int32) -> torch.Tensor:
+        """``count`` elements of workspace region ``r`` (WS_DELTA, WS_KV_ORDER, ...)."""
+        a = self.args
+        off = bwd_workspace_offset(a.batch, a.heads, a.seqlen, r)
+        nbytes = count * torch.empty(0, dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype)
+
     def delta(self) -> torch.Tensor:
         """The workspace's Delta region as fp32 [B, H, S] (valid after PREPROCESS)."""
         a = self.args
-        _, off, _ = bwd_workspace_layout(a.batch, a.heads, a.seqlen)
         n = a.batch * a.heads * a.seqlen
-        return self.workspace[off:off + 4 * n].view(torch.float32).view(a.batch, a.heads, a.seqlen)
+        return self.region(WS_DELTA, n, torch.float32).view(a.batch, a.heads, a.seqlen)
 
 
 def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -325,17 +345,21 @@ def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
                       k2q_num: torch.Tensor, variable_block_sizes: torch.Tensor,
                       sm_scale: Optional[float] = None, order: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
-                      out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+                      out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                      q2k_idx: Optional[torch.Tensor] = None,
+                      q2k_num: Optional[torch.Tensor] = None):
     """Backward from k2q metadata (``[B, H, nb, max_q_blocks]`` or ``[B*H*nb, max_q_blocks]``
     plus ``[B, H, nb]`` counts). Returns ``(dq, dk, dv)`` bf16."""
     return BwdPlan(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
-                   sm_scale=sm_scale, order=order, workspace=workspace, out=out).run()
+                   sm_scale=sm_scale, order=order, workspace=workspace, out=out,
+                   q2k_idx=q2k_idx, q2k_num=q2k_num).run()
 
 
 def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
              sm_scale: Optional[float] = None):
-    """Backward from the forward's q2k metadata: inverts to k2q on the GPU, then runs
-    :func:`backward_from_k2q`. Returns ``(dq, dk, dv)``."""
+    """Backward from the forward's q2k metadata: inverts to k2q on the GPU, then runs the
+    backward with both lists (the q-major dQ kernel walks q2k, the kv-major kernel k2q). The q2k
+    rows must not repeat a kv block. Returns ``(dq, dk, dv)``."""
     B, H = q.shape[0], q.shape[1]
     idx = _idx(q2k_idx, "q2k_idx")
     num = _idx(q2k_num, "q2k_num")
@@ -346,4 +370,4 @@ def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
     nb = variable_block_sizes.numel()
     k2q_idx, k2q_num = invert_indices(idx, num, nb)
     return backward_from_k2q(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
-                             sm_scale=sm_scale)
+                             sm_scale=sm_scale, q2k_idx=idx, q2k_num=num)

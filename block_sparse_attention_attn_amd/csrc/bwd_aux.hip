@@ -1,14 +1,13 @@
 // bwd_aux.hip -- the streaming kernels around the backward's main kernel (gfx950):
-//   preprocess  Delta = rowsum(bf16(o) * dO) in fp32, zero the fp32 dQ accumulator, and write the
-//               exact-zero dK/dV rows of kv blocks that no q block selects (FastVideo sm_100a
-//               backward commit message, the preprocess sentence; launch header, the delta and
-//               dqaccum fields of the argument struct);
-//   order       the per-(b, h) length-binned permutation of kv work items that the launch header
+//   preprocess  Delta = rowsum(bf16(o) * dO) in fp32, and the exact-zero dK/dV rows of kv blocks
+//               that no q block selects (FastVideo sm_100a backward commit message, the
+//               preprocess sentence; launch header, the delta field of the argument struct);
+//   order       the per-(b, h) length-binned permutation of work items that the launch header
 //               computes on device from 1024 kv blocks on (its order-kernel launch and the
-//               ORDER_MIN_KV_BLOCKS comment);
-//   postprocess dq = bf16(sm_scale * dQ accumulator) (commit message: dQ postprocess + sm_scale).
-// All three are HBM-streaming; they use 16-byte accesses with consecutive lanes on consecutive
-// 16-byte chunks of a row.
+//               ORDER_MIN_KV_BLOCKS comment); used for the kv-major and the q-major kernel.
+// The preprocess streams with 16-byte accesses, consecutive lanes on consecutive 16-byte chunks
+// of a row. (The pages' dQ postprocess -- scale by sm_scale, round to bf16 -- is fused into the
+// q-major dQ kernel's epilogue here.)
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -37,9 +36,6 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdPreParams p) {
     acc += __shfl_xor(acc, 2, 64);
     acc += __shfl_xor(acc, 1, 64);
     if (c == 0) p.delta[row] = acc;
-    f32x4* dq = (f32x4*)(p.dqaccum + row * HEAD_DIM + c * 8);
-    dq[0] = f32x4{};
-    dq[1] = f32x4{};
     if (empty) {
       *(bf16x8*)(p.dk + row * HEAD_DIM + c * 8) = bf16x8{};
       *(bf16x8*)(p.dv + row * HEAD_DIM + c * 8) = bf16x8{};
@@ -54,7 +50,7 @@ void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream) {
 // One workgroup per (b, h): bitonic sort of 32-bit keys (inverted bin << 14 | kv) in LDS, so the
 // result is larger bins first and ascending kv inside a bin -- a deterministic permutation.
 // bin = k2q_num / bin_width, clamped to 18 bits.
-__global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ k2q_num, int nb,
+__global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ num_in, int nb,
                                                          int bin_width, int32_t* __restrict__ order) {
   __shared__ uint32_t keys[ORDER_MAX_KV_BLOCKS];
   const int bh = blockIdx.x;
@@ -64,7 +60,7 @@ __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restri
   for (int i = tid; i < P; i += 1024) {
     uint32_t key = 0xFFFFFFFFu;
     if (i < nb) {
-      int num = k2q_num[(size_t)bh * nb + i];
+      int num = num_in[(size_t)bh * nb + i];
       num = num < 0 ? 0 : num;
       uint32_t bin = (uint32_t)(num / bin_width);
       bin = bin > 0x3FFFFu ? 0x3FFFFu : bin;
@@ -93,32 +89,9 @@ __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restri
     order[(size_t)bh * nb + r] = bh * nb + (int)(keys[r] & 0x3FFFu);
 }
 
-void launch_bwd_order(const int32_t* k2q_num, int BH, int nb, int bin_width, int32_t* order,
+void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
                       hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_order_kernel, dim3(BH), dim3(1024), 0, stream, k2q_num, nb, bin_width,
-                     order);
-}
-
-// 8 fp32 accumulator values -> 8 bf16 per thread, grid-stride.
-__global__ void __launch_bounds__(256) bwd_post_kernel(const float* __restrict__ acc,
-                                                       bf16* __restrict__ dq, size_t n8,
-                                                       float sm_scale) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
-    const f32x4 a = ((const f32x4*)acc)[2 * i];
-    const f32x4 b = ((const f32x4*)acc)[2 * i + 1];
-    ((bf16x8*)dq)[i] = pack8(a[0] * sm_scale, a[1] * sm_scale, a[2] * sm_scale, a[3] * sm_scale,
-                             b[0] * sm_scale, b[1] * sm_scale, b[2] * sm_scale, b[3] * sm_scale);
-  }
-}
-
-void launch_bwd_post(const float* dqaccum, bf16* dq, size_t n_elems, float sm_scale,
-                     hipStream_t stream) {
-  const size_t n8 = n_elems / 8;
-  size_t blocks = (n8 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks == 0) return;
-  hipLaunchKernelGGL(bwd_post_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dqaccum, dq, n8,
-                     sm_scale);
+  hipLaunchKernelGGL(bwd_order_kernel, dim3(BH), dim3(1024), 0, stream, num, nb, bin_width, order);
 }
 
 }  // namespace vsa

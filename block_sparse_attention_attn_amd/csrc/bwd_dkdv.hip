@@ -1,36 +1,35 @@
-// bwd_main.hip -- the hot loop of the 64-token block-sparse attention backward on gfx950.
+// bwd_dkdv.hip -- dK and dV of the 64-token block-sparse attention backward on gfx950 (the kv-major
+// half of the backward's main step).
 //
-// What it computes (FastVideo sm_100a backward commit message, the "one kernel per (batch, head,
-// kv64 block)" paragraph, and the backward launch header's argument struct; the gradient itself
-// is the textbook softmax-attention gradient of the backward test page's reference):
-// for one work item (b, h, kv block j) and every q block i in the item's k2q list,
-//     S^T  = K_j Q_i^T                       (recomputed scores, 64 x 64)
-//     P^T  = exp2(S^T * scale_log2 - lse_i)   (lse in base-2 "M form"; kv rows >= vbs[j] -> 0)
-//     dV_j += P^T dO_i
-//     dP^T = V_j dO_i^T
-//     dS^T = P^T * (dP^T - Delta_i)
-//     dK_j += dS^T Q_i
-//     dQ_i += dS K_j            (fp32 partials added atomically into the dQ accumulator)
-// and at the end dk_j = bf16(sm_scale * dK_j), dv_j = bf16(dV_j). Items whose list is empty do no
-// work here; the preprocess has written their zero rows.
+// What it computes (FastVideo sm_100a backward commit message: one work item per (batch, head,
+// kv64 block); launch header argument struct: k2q lists, variable_block_sizes, dk carries
+// sm_scale and dv does not; the gradient is the textbook softmax-attention gradient of the
+// backward test page's reference): for one item (b, h, kv block j) and every q block i in its
+// k2q list,
+//     S    = Q_i K_j^T                       (recomputed scores, 64 x 64)
+//     P    = exp2(S * scale_log2 - lse_i)     (lse in base-2 "M form"; kv rows >= vbs[j] -> 0)
+//     dP   = dO_i V_j^T
+//     dS   = P * (dP - Delta_i)
+//     dV_j += P^T dO_i,   dK_j += dS^T Q_i
+// then dk_j = bf16(sm_scale * dK_j), dv_j = bf16(dV_j). Items with an empty list do no work here:
+// the preprocess wrote their zero rows. dQ is computed by the q-major kernel (bwd_dq.hip), so
+// this kernel issues no atomics and its results are bitwise reproducible.
 //
-// gfx950 design (not a translation of the page's warp-specialised tcgen05 kernel):
-//   * one 256-thread workgroup (4 waves, one per SIMD) per item; the waves form a 2 x 2 grid:
-//     wave w owns q rows 32*(w&1).. of every q block and kv rows 32*(w>>1).. of the item, so
-//     each of the five 64x64x128 GEMMs is eight v_mfma_f32_32x32x16_bf16 per wave;
-//   * K_j and V_j fragments for S and dP live in registers for the whole item, and so does the
-//     transposed K_j fragment for dQ; padded kv rows are zeroed there (no 0 * NaN leaks);
+// gfx950 design:
+//   * one 256-thread workgroup (4 waves, one per SIMD) per item; wave w owns q rows 32*(w&1)..
+//     of every q block and kv rows 32*(w>>1).. of the item, so each 64x64x128 GEMM is eight
+//     v_mfma_f32_32x32x16_bf16 per wave;
+//   * K_j and V_j fragments (the B operands of S and dP) live in registers for the whole item,
+//     with padded kv rows zeroed there;
 //   * Q_i, dO_i (and lse_i, Delta_i) stream through XOR-swizzled LDS tiles filled by
-//     global_load_lds_dwordx4, double-buffered: the next q block's tiles load while this one
-//     computes;
-//   * P and dS stay in registers between GEMMs (the D layout of one MFMA is fed back as the A
-//     operand of the next by permuting the contraction index); the partner operands dO_i^T, Q_i^T
-//     and dS come from ds_read_b64_tr_b16 transposed reads; dS^T crosses waves through LDS;
-//   * dV and dK are accumulated per q half and the two halves are summed through LDS once per
-//     item;
-//   * work ids are mapped XCD-first: consecutive workgroup ids go round-robin over the 8 XCDs,
-//     so XCD x runs a contiguous slice of the (ordered) item list -- one head per XCD when
-//     B*H = 8 -- and that head's Q/dO/dQ-accumulator traffic stays in one XCD's L2.
+//     global_load_lds_dwordx4, double-buffered: the next q block loads while this one computes;
+//   * P and dS never leave registers: the D layout of S/dP feeds the A operand of dV/dK directly
+//     (the contraction index is permuted to match), the partner operands dO_i^T and Q_i^T come
+//     from ds_read_b64_tr_b16 transposed reads;
+//   * dV and dK are accumulated per q half and the halves are summed through LDS once per item;
+//   * work ids map XCD-first: workgroup ids go round-robin over the 8 XCDs, so XCD x runs a
+//     contiguous slice of the (ordered) item list -- one head per XCD when B*H = 8 -- and that
+//     head's Q/dO traffic stays in one XCD's L2.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -38,16 +37,9 @@ namespace vsa {
 
 namespace {
 
-// s_waitcnt immediate that waits until at most `n` vector memory operations are outstanding
-// (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt left at max).
-constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (7 << 4) | (n & 15); }
-
-// Atomic dQ partials each wave issues per q block: 2 n-tiles x 16 accumulator elements.
-constexpr int ATOMICS_PER_PAIR = 32;
-
 __device__ __forceinline__ void barrier_lds() {
-  // Wait for this wave's LDS traffic, then meet the other waves. No vmcnt wait: atomics and
-  // prefetches stay in flight across the barrier.
+  // Wait for this wave's LDS traffic, then meet the other waves. Vector memory traffic (the next
+  // tile's DMA) stays in flight across the barrier.
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -73,30 +65,30 @@ __device__ __forceinline__ void prefetch(const bf16* __restrict__ qh, const bf16
 }  // namespace
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-bwd_main_kernel(BwdMainParams p) {
+bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char q_s0[16384];
   __shared__ __attribute__((aligned(1024))) char q_s1[16384];
   __shared__ __attribute__((aligned(1024))) char do_s0[16384];
   __shared__ __attribute__((aligned(1024))) char do_s1[16384];
-  __shared__ __attribute__((aligned(1024))) char k_s[16384];
-  __shared__ __attribute__((aligned(1024))) char ds_s[8192];
   __shared__ __attribute__((aligned(16))) float ld_s0[128];
   __shared__ __attribute__((aligned(16))) float ld_s1[128];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int wq = w & 1;   // q half of every q block
-  const int wk = w >> 1;  // kv half of the item (and d half of dQ)
+  const int wk = w >> 1;  // kv half of the item
   const int g = lane >> 5;
   const int l32 = lane & 31;
+  const int grp = lane >> 4;  // 16-lane group
+  const int t16 = lane & 15;  // lane inside the group
 
   // XCD-first work id: blockIdx.x % 8 is the XCD the dispatcher sends the workgroup to.
   const int wid = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);
   if (wid >= p.total_items) return;
-  const int item = p.order ? ld_const(p.order, wid) : wid;
+  const int item = p.kv_order ? ld_const(p.kv_order, wid) : wid;
   if (item < 0 || item >= p.total_items) return;  // a malformed order entry: skip, never fault
   int n = ld_const(p.k2q_num, item);
-  n = n > p.max_q_blocks ? p.max_q_blocks : n;
+  n = n > p.k2q_stride ? p.k2q_stride : n;
   if (n <= 0) return;
   const int bh = item / p.nb;
   const int j = item - bh * p.nb;
@@ -106,8 +98,7 @@ bwd_main_kernel(BwdMainParams p) {
   const bf16* __restrict__ doh = p.dout + head;
   const float* __restrict__ lseh = p.lse + (size_t)bh * p.S;
   const float* __restrict__ deltah = p.delta + (size_t)bh * p.S;
-  float* __restrict__ dqh = p.dqaccum + head;
-  const int* __restrict__ list = p.k2q_idx + (size_t)item * p.max_q_blocks;
+  const int* __restrict__ list = p.k2q_idx + (size_t)item * p.k2q_stride;
   // q block ids outside [0, nb) violate the caller contract; clamp them so no access leaves the
   // tensors (the result is then unspecified, but nothing faults)
   auto qblock = [&](int t) {
@@ -119,19 +110,15 @@ bwd_main_kernel(BwdMainParams p) {
   // buffer statically
   const Pipe pipe0{(VSA_LDS char*)q_s0, (VSA_LDS char*)do_s0, (VSA_LDS float*)ld_s0};
   const Pipe pipe1{(VSA_LDS char*)q_s1, (VSA_LDS char*)do_s1, (VSA_LDS float*)ld_s1};
-  VSA_LDS char* kls = (VSA_LDS char*)k_s;
-  VSA_LDS char* dsl = (VSA_LDS char*)ds_s;
-
-  // ---- item set-up: K tile to LDS, K/V fragments to registers, first q block prefetch ----
-  const bf16* kj = p.k + head + (size_t)j * BLOCK * HEAD_DIM;
-  const bf16* vj = p.v + head + (size_t)j * BLOCK * HEAD_DIM;
-  tile_load_async<4>(kj, kls, lane, w);
   prefetch(qh, doh, lseh, deltah, qblock(0), pipe0, lane, w);
 
   // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
   const int kv_l = 32 * wk + l32;
+  const bool kv_valid = kv_l < vb;
   bf16x8 kf[8], vf[8];
   {
+    const bf16* kj = p.k + head + (size_t)j * BLOCK * HEAD_DIM;
+    const bf16* vj = p.v + head + (size_t)j * BLOCK * HEAD_DIM;
     const bf16x8* kr = (const bf16x8*)(kj + (size_t)kv_l * HEAD_DIM);
     const bf16x8* vr = (const bf16x8*)(vj + (size_t)kv_l * HEAD_DIM);
 #pragma unroll
@@ -139,37 +126,12 @@ bwd_main_kernel(BwdMainParams p) {
       kf[s] = kr[2 * s + g];
       vf[s] = vr[2 * s + g];
     }
-    if (kv_l >= vb) {
+    if (!kv_valid) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         kf[s] = bf16x8{};
         vf[s] = bf16x8{};
       }
-    }
-  }
-  const bool kv_valid = kv_l < vb;
-
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  barrier_lds();
-
-  // B operand of dQ = dS K: lane holds d = 64*wk + 32*nt + l32, kv = 16*s + 8*g + 0..7,
-  // read transposed from the K tile; padded kv rows zeroed.
-  const int grp = lane >> 4;   // 16-lane group
-  const int t16 = lane & 15;   // lane inside the group
-  bf16x8 ktf[2][4];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kv0 = 16 * s + 8 * (grp >> 1);
-      const int col = 64 * wk + 32 * nt + 16 * (grp & 1) + 4 * (t16 & 3);
-      s16x4 lo = lds_read_tr(kls + tile_elem_byte(kv0 + (t16 >> 2), col));
-      s16x4 hi = lds_read_tr(kls + tile_elem_byte(kv0 + 4 + (t16 >> 2), col));
-      bf16x8 f = join(lo, hi);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (kv0 + e >= vb) f[e] = (bf16)0.0f;
-      ktf[nt][s] = f;
     }
   }
 
@@ -183,9 +145,8 @@ bwd_main_kernel(BwdMainParams p) {
   const float scale_log2 = p.scale_log2;
 
   auto step = [&](int t, const Pipe cu, const Pipe nx) __attribute__((always_inline)) {
-    const int qb = qblock(t);
-    if (t > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(ATOMICS_PER_PAIR));
-    barrier_lds();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this q block's tiles have landed (own DMAs)
+    barrier_lds();                               // ... and everyone else's; buffer nx is free
     if (t + 1 < n) prefetch(qh, doh, lseh, deltah, qblock(t + 1), nx, lane, w);
     VSA_LDS char* qt = cu.q;
     VSA_LDS char* dt = cu.d;
@@ -218,20 +179,6 @@ bwd_main_kernel(BwdMainParams p) {
       }
     }
 
-    // ---- dS^T to LDS for the dQ GEMM: 4 consecutive q per lane -> one 8-byte write ----
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      s16x4 pk;
-      union {
-        bf16 b[4];
-        s16x4 s;
-      } u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u.b[e] = (bf16)dsv[4 * c + e];
-      pk = u.s;
-      *(VSA_LDS s16x4*)(dsl + ds_elem_byte(kv_l, 32 * wq + 8 * c + 4 * g)) = pk;
-    }
-
     // ---- dV += P^T dO and dK += dS^T Q over this wave's q half ----
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -251,30 +198,6 @@ bwd_main_kernel(BwdMainParams p) {
         dk_acc[nt] = mfma32(sa, qbv, dk_acc[nt]);
       }
     }
-
-    barrier_lds();  // dS^T complete
-
-    // ---- dQ rows 32*wq.. x d 64*wk.. = dS K, atomically added ----
-    f32x16 dq_acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kv0 = 16 * s + 8 * (grp >> 1) + (t16 >> 2);
-      const int col = 32 * wq + 16 * (grp & 1) + 4 * (t16 & 3);
-      const bf16x8 a = join(lds_read_tr(dsl + ds_elem_byte(kv0, col)),
-                            lds_read_tr(dsl + ds_elem_byte(kv0 + 4, col)));
-      dq_acc[0] = mfma32(a, ktf[0][s], dq_acc[0]);
-      dq_acc[1] = mfma32(a, ktf[1][s], dq_acc[1]);
-    }
-    float* dqb = dqh + (size_t)qb * BLOCK * HEAD_DIM;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int d = 64 * wk + 32 * nt + l32;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = 32 * wq + 8 * (i >> 2) + 4 * g + (i & 3);
-        atomicAdd(dqb + qr * HEAD_DIM + d, dq_acc[nt][i]);
-      }
-    }
   };
   for (int t = 0; t < n; t += 2) {
     step(t, pipe0, pipe1);
@@ -282,7 +205,6 @@ bwd_main_kernel(BwdMainParams p) {
   }
 
   // ---- sum the two q halves of dV/dK through LDS, scale, round, store ----
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(ATOMICS_PER_PAIR));
   barrier_lds();  // every wave is past its last LDS read of the q/dO buffers
   // wave wq=1 hands over its dV half, wave wq=0 its dK half (16 KiB each, lane-native order);
   // kv half 0 uses the q buffers, kv half 1 the dO buffers
@@ -317,9 +239,8 @@ bwd_main_kernel(BwdMainParams p) {
   }
 }
 
-void launch_bwd_main(const BwdMainParams& p, hipStream_t stream) {
-  const int grid = p.items_per_xcd * 8;
-  hipLaunchKernelGGL(bwd_main_kernel, dim3(grid), dim3(256), 0, stream, p);
+void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.items_per_xcd * 8), dim3(256), 0, stream, p);
 }
 
 }  // namespace vsa

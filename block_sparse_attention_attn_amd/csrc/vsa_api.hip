@@ -4,9 +4,11 @@
 //
 // The backward chain follows the FastVideo backward launch header (its launch function:
 // support check -> preprocess -> order when nb >= 1024 and no order was given -> main ->
-// postprocess, every launch on the caller's stream and checked right after), minus the TMA
-// descriptor set-up and the transposed Q/dO copies, which gfx950 does not need: its main kernel
-// reads transposed operands from LDS with ds_read_b64_tr_b16.
+// postprocess, every launch on the caller's stream and checked right after), with three
+// differences made for gfx950: no TMA descriptors or transposed Q/dO copies (the kernels read
+// transposed operands from LDS with ds_read_b64_tr_b16); the main step is two atomic-free
+// kernels (kv-major dK/dV, q-major dQ) because fp32 atomics cannot carry the per-pair dQ
+// partials at MFMA speed on this chip; and the dQ postprocess is the q-major kernel's epilogue.
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -132,23 +134,26 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
 // backward
 // ------------------------------------------------------------------------------------------------
 
-void vsa_bwd_workspace_layout(int batch, int heads, int seqlen, size_t* dqacc_off,
-                              size_t* delta_off, size_t* order_off) {
-  const size_t rows = (size_t)(batch < 0 ? 0 : batch) * (size_t)(heads < 0 ? 0 : heads) *
-                      (size_t)(seqlen < 0 ? 0 : seqlen);
-  const size_t dq = align256(rows * vsa::HEAD_DIM * sizeof(float));
-  const size_t delta = align256(rows * sizeof(float));
-  if (dqacc_off) *dqacc_off = 0;
-  if (delta_off) *delta_off = dq;
-  if (order_off) *order_off = dq + delta;
+size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int region) {
+  if (batch < 1 || heads < 1 || seqlen < vsa::BLOCK || region < VSA_WS_DELTA || region > VSA_WS_END)
+    return 0;
+  const size_t bh = (size_t)batch * (size_t)heads;
+  const size_t nb = (size_t)seqlen / vsa::BLOCK;
+  const size_t sizes[VSA_WS_END] = {
+      align256(bh * (size_t)seqlen * sizeof(float)),                          // delta
+      align256(bh * nb * sizeof(int32_t)),                                    // kv order
+      align256(bh * nb * sizeof(int32_t)),                                    // q order
+      align256(bh * nb * sizeof(int32_t)),                                    // q2k_num
+      align256(bh * nb * nb * sizeof(int32_t)),                               // q2k_idx
+      align256(vsa::invert_bitmap_bytes((int)bh, (int)nb, (int)nb)),          // bitmap
+  };
+  size_t off = 0;
+  for (int r = 0; r < region; ++r) off += sizes[r];
+  return off;
 }
 
-size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen) {
-  if (batch < 1 || heads < 1 || seqlen < vsa::BLOCK) return 0;
-  size_t order_off = 0;
-  vsa_bwd_workspace_layout(batch, heads, seqlen, nullptr, nullptr, &order_off);
-  const size_t items = (size_t)batch * heads * (size_t)(seqlen / vsa::BLOCK);
-  return order_off + align256(items * sizeof(int32_t));
+size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int derive_q2k) {
+  return vsa_bwd_workspace_offset(batch, heads, seqlen, derive_q2k ? VSA_WS_END : VSA_WS_Q2K_NUM);
 }
 
 int vsa_bwd_check(const vsa_bwd_args* a) {
@@ -160,16 +165,21 @@ int vsa_bwd_check(const vsa_bwd_args* a) {
                             "num_kv_blocks (got seqlen " + std::to_string(a->seqlen) +
                                 ", num_kv_blocks " + std::to_string(a->num_kv_blocks) + ")");
   if (a->max_q_blocks < 1) return fail(VSA_EINVAL, "vsa_bwd: max_q_blocks must be >= 1");
-  if ((size_t)a->batch * a->heads * (size_t)a->num_kv_blocks * (size_t)a->max_q_blocks >= kMaxElems)
-    return fail(VSA_EINVAL, "vsa_bwd: k2q_idx too large");
+  const size_t items = (size_t)a->batch * a->heads * (size_t)a->num_kv_blocks;
+  if (items * (size_t)a->max_q_blocks >= kMaxElems || items * (size_t)a->num_kv_blocks >= kMaxElems)
+    return fail(VSA_EINVAL, "vsa_bwd: index metadata too large");
   if (!std::isfinite(a->sm_scale)) return fail(VSA_EINVAL, "vsa_bwd: sm_scale must be finite");
   if (!a->q || !a->k || !a->v || !a->o || !a->dout || !a->lse)
     return fail(VSA_EINVAL, "vsa_bwd: null input pointer");
   if (!a->k2q_idx || !a->k2q_num || !a->vbs)
     return fail(VSA_EINVAL, "vsa_bwd: null index pointer");
+  if ((a->q2k_idx == nullptr) != (a->q2k_num == nullptr))
+    return fail(VSA_EINVAL, "vsa_bwd: give both q2k_idx and q2k_num, or neither");
+  if (a->q2k_idx && a->q2k_stride < 1)
+    return fail(VSA_EINVAL, "vsa_bwd: q2k_stride must be >= 1 when q2k lists are given");
   if (!a->dq || !a->dk || !a->dv) return fail(VSA_EINVAL, "vsa_bwd: null output pointer");
   if (!a->workspace) return fail(VSA_EINVAL, "vsa_bwd: null workspace");
-  const size_t need = vsa_bwd_workspace_bytes(a->batch, a->heads, a->seqlen);
+  const size_t need = vsa_bwd_workspace_bytes(a->batch, a->heads, a->seqlen, a->q2k_idx == nullptr);
   if (a->workspace_bytes < need)
     return fail(VSA_EINVAL, "vsa_bwd: workspace of " + std::to_string(a->workspace_bytes) +
                                 " bytes, need " + std::to_string(need));
@@ -194,28 +204,67 @@ int vsa_bwd_order(const int32_t* k2q_num, int batch, int heads, int num_kv_block
 namespace {
 
 bool uses_device_order(const vsa_bwd_args* a) {
-  return !a->order && a->num_kv_blocks >= VSA_ORDER_MIN_KV_BLOCKS &&
-         a->num_kv_blocks <= VSA_ORDER_MAX_KV_BLOCKS;
+  return a->num_kv_blocks >= VSA_ORDER_MIN_KV_BLOCKS && a->num_kv_blocks <= VSA_ORDER_MAX_KV_BLOCKS;
+}
+
+struct WsView {
+  float* delta;
+  int32_t* kv_order;
+  int32_t* q_order;
+  int32_t* q2k_num;
+  int32_t* q2k_idx;
+  uint32_t* bitmap;
+};
+
+WsView ws_view(const vsa_bwd_args* a) {
+  char* ws = (char*)a->workspace;
+  auto at = [&](int r) { return ws + vsa_bwd_workspace_offset(a->batch, a->heads, a->seqlen, r); };
+  return WsView{(float*)at(VSA_WS_DELTA), (int32_t*)at(VSA_WS_KV_ORDER), (int32_t*)at(VSA_WS_Q_ORDER),
+                (int32_t*)at(VSA_WS_Q2K_NUM), (int32_t*)at(VSA_WS_Q2K_IDX),
+                (uint32_t*)at(VSA_WS_BITMAP)};
+}
+
+vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
+  vsa::BwdParams m;
+  const bool derive = a->q2k_idx == nullptr;
+  m.q = (const vsa::bf16*)a->q;
+  m.k = (const vsa::bf16*)a->k;
+  m.v = (const vsa::bf16*)a->v;
+  m.dout = (const vsa::bf16*)a->dout;
+  m.lse = a->lse;
+  m.delta = ws.delta;
+  m.k2q_idx = a->k2q_idx;
+  m.k2q_num = a->k2q_num;
+  m.q2k_idx = derive ? ws.q2k_idx : a->q2k_idx;
+  m.q2k_num = derive ? ws.q2k_num : a->q2k_num;
+  m.vbs = a->vbs;
+  m.kv_order = a->order ? a->order : (uses_device_order(a) ? ws.kv_order : nullptr);
+  m.q_order = uses_device_order(a) ? ws.q_order : nullptr;
+  m.dq = (vsa::bf16*)a->dq;
+  m.dk = (vsa::bf16*)a->dk;
+  m.dv = (vsa::bf16*)a->dv;
+  m.S = a->seqlen;
+  m.nb = a->num_kv_blocks;
+  m.k2q_stride = a->max_q_blocks;
+  m.q2k_stride = derive ? a->num_kv_blocks : a->q2k_stride;
+  m.total_items = a->batch * a->heads * a->num_kv_blocks;
+  m.items_per_xcd = (m.total_items + 7) / 8;
+  m.sm_scale = a->sm_scale;
+  m.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  return m;
 }
 
 int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
   const int BH = a->batch * a->heads;
   const int nb = a->num_kv_blocks;
-  size_t dq_off, delta_off, order_off;
-  vsa_bwd_workspace_layout(a->batch, a->heads, a->seqlen, &dq_off, &delta_off, &order_off);
-  char* ws = (char*)a->workspace;
-  float* dqaccum = (float*)(ws + dq_off);
-  float* delta = (float*)(ws + delta_off);
-  int32_t* order_ws = (int32_t*)(ws + order_off);
-
+  const WsView ws = ws_view(a);
   switch (stage) {
     case VSA_BWD_PREPROCESS: {
       vsa::BwdPreParams pre;
       pre.o = (const vsa::bf16*)a->o;
       pre.dout = (const vsa::bf16*)a->dout;
       pre.k2q_num = a->k2q_num;
-      pre.delta = delta;
-      pre.dqaccum = dqaccum;
+      pre.delta = ws.delta;
       pre.dk = (vsa::bf16*)a->dk;
       pre.dv = (vsa::bf16*)a->dv;
       pre.BH = BH;
@@ -224,39 +273,32 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       vsa::launch_bwd_pre(pre, s);
       return launch_status("vsa_bwd preprocess");
     }
-    case VSA_BWD_ORDER:
-      if (!uses_device_order(a)) return VSA_OK;
-      vsa::launch_bwd_order(a->k2q_num, BH, nb, 8, order_ws, s);
-      return launch_status("vsa_bwd order");
-    case VSA_BWD_MAIN: {
-      vsa::BwdMainParams m;
-      m.q = (const vsa::bf16*)a->q;
-      m.k = (const vsa::bf16*)a->k;
-      m.v = (const vsa::bf16*)a->v;
-      m.dout = (const vsa::bf16*)a->dout;
-      m.lse = a->lse;
-      m.delta = delta;
-      m.k2q_idx = a->k2q_idx;
-      m.k2q_num = a->k2q_num;
-      m.vbs = a->vbs;
-      m.order = a->order ? a->order : (uses_device_order(a) ? order_ws : nullptr);
-      m.dqaccum = dqaccum;
-      m.dk = (vsa::bf16*)a->dk;
-      m.dv = (vsa::bf16*)a->dv;
-      m.S = a->seqlen;
-      m.nb = nb;
-      m.max_q_blocks = a->max_q_blocks;
-      m.total_items = BH * nb;
-      m.items_per_xcd = (m.total_items + 7) / 8;
-      m.sm_scale = a->sm_scale;
-      m.scale_log2 = a->sm_scale * 1.4426950408889634f;
-      vsa::launch_bwd_main(m, s);
-      return launch_status("vsa_bwd main");
+    case VSA_BWD_INDEX: {
+      const bool derive = a->q2k_idx == nullptr;
+      if (derive) {
+        // k2q rows list q blocks per kv block; inverting them lists kv blocks per q block
+        vsa::launch_invert(a->k2q_idx, a->k2q_num, BH, nb, a->max_q_blocks, nb, ws.q2k_idx,
+                           ws.q2k_num, ws.bitmap, s);
+        const int r = launch_status("vsa_bwd q2k derivation");
+        if (r != VSA_OK) return r;
+      }
+      if (uses_device_order(a)) {
+        if (!a->order) {
+          vsa::launch_bwd_order(a->k2q_num, BH, nb, 8, ws.kv_order, s);
+          const int r = launch_status("vsa_bwd kv order");
+          if (r != VSA_OK) return r;
+        }
+        vsa::launch_bwd_order(derive ? ws.q2k_num : a->q2k_num, BH, nb, 8, ws.q_order, s);
+        return launch_status("vsa_bwd q order");
+      }
+      return VSA_OK;
     }
-    case VSA_BWD_POSTPROCESS:
-      vsa::launch_bwd_post(dqaccum, (vsa::bf16*)a->dq, (size_t)BH * a->seqlen * vsa::HEAD_DIM,
-                           a->sm_scale, s);
-      return launch_status("vsa_bwd postprocess");
+    case VSA_BWD_DKDV:
+      vsa::launch_bwd_dkdv(main_params(a, ws), s);
+      return launch_status("vsa_bwd dk/dv kernel");
+    case VSA_BWD_DQ:
+      vsa::launch_bwd_dq(main_params(a, ws), s);
+      return launch_status("vsa_bwd dq kernel");
     default:
       return fail(VSA_EINVAL, "vsa_bwd_stage: unknown stage " + std::to_string(stage));
   }
@@ -267,7 +309,7 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
 int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream) {
   const int st = vsa_bwd_check(a);
   if (st != VSA_OK) return st;
-  if (stage < VSA_BWD_PREPROCESS || stage > VSA_BWD_POSTPROCESS)
+  if (stage < VSA_BWD_PREPROCESS || stage > VSA_BWD_DQ)
     return fail(VSA_EINVAL, "vsa_bwd_stage: unknown stage " + std::to_string(stage));
   return run_stage(a, stage, (hipStream_t)stream);
 }
@@ -275,7 +317,7 @@ int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream) {
 int vsa_bwd(const vsa_bwd_args* a, void* stream) {
   const int st = vsa_bwd_check(a);
   if (st != VSA_OK) return st;
-  for (int stage = VSA_BWD_PREPROCESS; stage <= VSA_BWD_POSTPROCESS; ++stage) {
+  for (int stage = VSA_BWD_PREPROCESS; stage <= VSA_BWD_DQ; ++stage) {
     const int r = run_stage(a, stage, (hipStream_t)stream);
     if (r != VSA_OK) return r;
   }

@@ -104,6 +104,10 @@ __device__ __forceinline__ int ds_elem_byte(int r, int c) {
   return (r * 8 + ((c >> 3) ^ swz64(r))) * 16 + (c & 7) * 2;
 }
 
+// s_waitcnt immediate that waits until at most `n` vector memory operations are outstanding
+// (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt left at max).
+constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (7 << 4) | (n & 15); }
+
 // Read-only metadata (index lists, counts, block sizes) through the constant address space, so
 // the compiler issues scalar loads: they count against lgkmcnt, not vmcnt, and a read of a list
 // entry never waits for the vector memory traffic (atomics, prefetches) in flight.

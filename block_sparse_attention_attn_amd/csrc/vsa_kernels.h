@@ -32,47 +32,46 @@ struct FwdParams {
 };
 void launch_fwd(const FwdParams& p, hipStream_t stream);
 
-// ---- backward preprocess: Delta, dQ accumulator zeroing, zero dK/dV rows of empty kv blocks ----
+// ---- backward preprocess: Delta, zero dK/dV rows of empty kv blocks ----
 struct BwdPreParams {
   const bf16* o;
   const bf16* dout;
   const int32_t* k2q_num;  // [BH, nb]
   float* delta;            // [BH, S]
-  float* dqaccum;          // [BH, S, 128]
   bf16* dk;
   bf16* dv;
   int BH, S, nb;
 };
 void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream);
 
-// ---- backward work order: per (b, h) a length-binned permutation of its kv items ----
+// ---- work order: per (b, h) a length-binned permutation of its items ----
 constexpr int ORDER_MIN_KV_BLOCKS = 1024;  // below: identity order
-constexpr int ORDER_MAX_KV_BLOCKS = 16384; // LDS holds one 32-bit key per kv block
-void launch_bwd_order(const int32_t* k2q_num, int BH, int nb, int bin_width, int32_t* order,
+constexpr int ORDER_MAX_KV_BLOCKS = 16384; // LDS holds one 32-bit key per block
+void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
                       hipStream_t stream);
 
-// ---- backward main kernel ----
-struct BwdMainParams {
+// ---- the two main backward kernels (kv-major dK/dV, q-major dQ) ----
+struct BwdParams {
   const bf16* q;
   const bf16* k;
   const bf16* v;
   const bf16* dout;
   const float* lse;
   const float* delta;
-  const int32_t* k2q_idx;
-  const int32_t* k2q_num;
+  const int32_t* k2q_idx;  // [BH*nb, k2q_stride]
+  const int32_t* k2q_num;  // [BH*nb]
+  const int32_t* q2k_idx;  // [BH*nb, q2k_stride]
+  const int32_t* q2k_num;  // [BH*nb]
   const int32_t* vbs;
-  const int32_t* order;  // nullptr: identity
-  float* dqaccum;
+  const int32_t* kv_order;  // nullptr: identity
+  const int32_t* q_order;   // nullptr: identity
+  bf16* dq;
   bf16* dk;
   bf16* dv;
-  int S, nb, max_q_blocks, total_items, items_per_xcd;
+  int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
   float scale_log2, sm_scale;
 };
-void launch_bwd_main(const BwdMainParams& p, hipStream_t stream);
-
-// ---- backward postprocess: dq = bf16(sm_scale * dqaccum) ----
-void launch_bwd_post(const float* dqaccum, bf16* dq, size_t n_elems, float sm_scale,
-                     hipStream_t stream);
+void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
+void launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 
 }  // namespace vsa

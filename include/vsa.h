@@ -89,19 +89,42 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  * block selects get exact-zero dk/dv rows, and so do kv rows at or past vbs. lse is the forward's
  * M-form log-sum-exp; o is the forward's bf16 output (Delta = rowsum(o * dout) uses it).
  *
- * Work order: `order` (optional, [B*H*num_kv_blocks] int32 item ids (b*H + h)*nb + kv, a
- * permutation) fixes the order in which items are launched. NULL lets the library choose: the
- * identity below VSA_ORDER_MIN_KV_BLOCKS kv blocks per sequence, else the length-binned order
- * (vsa_bwd_order with bin width 8) computed into the workspace. Any order gives the same dk/dv
- * bits; dq differs only by fp32 summation order.
+ * The main step runs as two kernels without atomics: a kv-major one (one work item per
+ * (b, h, kv block), walking the k2q list) for dk and dv, and a q-major one (one item per
+ * (b, h, q block), walking the q2k list) for dq, which recomputes the scores. All three outputs
+ * are bitwise reproducible run to run, whatever the work order.
  *
- * Workspace (device, vsa_bwd_workspace_bytes() bytes, contents on entry irrelevant):
- *   [0, dqacc)        fp32 dQ accumulator [B, H, S, 128]
- *   [dqacc, +delta)   fp32 Delta [B, H, S]   (left holding Delta after the call)
- *   [.., +order)      int32 work order [B*H*nb] (when the library computes it)
- * each region starting at a 256-byte boundary; vsa_bwd_workspace_layout() gives the offsets. */
+ * q2k lists (optional): the forward's q2k_idx [B, H, num_kv_blocks, q2k_stride] / q2k_num, which
+ * must describe the same selection as k2q (each pair once). NULL: the library derives them from
+ * k2q into the workspace (the inversion kernel of vsa_invert_indices).
+ *
+ * Work order: `order` (optional, [B*H*num_kv_blocks] int32 item ids (b*H + h)*nb + kv, a
+ * permutation) fixes the launch order of the kv-major items. NULL lets the library choose: the
+ * identity below VSA_ORDER_MIN_KV_BLOCKS kv blocks per sequence, else the length-binned order
+ * (vsa_bwd_order, bin width 8) computed into the workspace; the q-major items get the same
+ * treatment from the q2k counts.
+ *
+ * Workspace (device, vsa_bwd_workspace_bytes() bytes, contents on entry irrelevant), regions in
+ * this order, each at a 256-byte boundary (vsa_bwd_workspace_offset() gives the offsets):
+ *   VSA_WS_DELTA     fp32 Delta [B, H, S]   (left holding Delta after the call)
+ *   VSA_WS_KV_ORDER  int32 [B*H*nb] kv-major work order (when the library computes it)
+ *   VSA_WS_Q_ORDER   int32 [B*H*nb] q-major work order (when the library computes it)
+ * and only when the q2k lists are derived (derive_q2k != 0):
+ *   VSA_WS_Q2K_NUM   int32 [B, H, nb]
+ *   VSA_WS_Q2K_IDX   int32 [B, H, nb, nb]
+ *   VSA_WS_BITMAP    the inversion's bitmap */
 #define VSA_ORDER_MIN_KV_BLOCKS 1024
 #define VSA_ORDER_MAX_KV_BLOCKS 16384
+
+typedef enum {
+  VSA_WS_DELTA = 0,
+  VSA_WS_KV_ORDER = 1,
+  VSA_WS_Q_ORDER = 2,
+  VSA_WS_Q2K_NUM = 3,
+  VSA_WS_Q2K_IDX = 4,
+  VSA_WS_BITMAP = 5,
+  VSA_WS_END = 6
+} vsa_bwd_ws_region;
 
 typedef struct {
   const void* q;          /* bf16 [B, H, S, 128] */
@@ -112,36 +135,38 @@ typedef struct {
   const float* lse;       /* fp32 [B, H, S], M form */
   const int32_t* k2q_idx; /* [B, H, num_kv_blocks, max_q_blocks] ascending q block ids */
   const int32_t* k2q_num; /* [B, H, num_kv_blocks], 0 allowed */
+  const int32_t* q2k_idx; /* optional [B, H, num_kv_blocks, q2k_stride] kv block ids */
+  const int32_t* q2k_num; /* optional [B, H, num_kv_blocks] */
   const int32_t* vbs;     /* [num_kv_blocks] valid kv tokens per block, in [0, 64] */
-  const int32_t* order;   /* optional work order, see above; NULL = library's choice */
+  const int32_t* order;   /* optional kv-major work order, see above; NULL = library's choice */
   void* dq;               /* bf16 outputs [B, H, S, 128] */
   void* dk;
   void* dv;
   void* workspace;
   size_t workspace_bytes;
-  int batch, heads, seqlen, head_dim, num_kv_blocks, max_q_blocks;
+  int batch, heads, seqlen, head_dim, num_kv_blocks, max_q_blocks, q2k_stride;
   float sm_scale;
 } vsa_bwd_args;
 
-size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen);
-/* Byte offsets of the dQ accumulator, Delta and order regions inside the workspace. */
-void vsa_bwd_workspace_layout(int batch, int heads, int seqlen, size_t* dqacc_off,
-                              size_t* delta_off, size_t* order_off);
+/* Bytes of workspace for a backward call; derive_q2k != 0 when q2k_idx/q2k_num are NULL. */
+size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int derive_q2k);
+/* Byte offset of a workspace region (vsa_bwd_ws_region); VSA_WS_END is the derive_q2k size. */
+size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int region);
 /* Host-only validation of a backward call; reads no device memory. */
 int vsa_bwd_check(const vsa_bwd_args* a);
 int vsa_bwd(const vsa_bwd_args* a, void* stream);
 
 /* The backward's stages one at a time, for callers that time or interleave them. Each call
- * validates like vsa_bwd. Run on one stream in the order PREPROCESS, ORDER, MAIN, POSTPROCESS,
- * they enqueue exactly the kernels vsa_bwd enqueues and produce the same results. ORDER is a no-op
- * when a->order is given or num_kv_blocks is outside [VSA_ORDER_MIN_KV_BLOCKS,
- * VSA_ORDER_MAX_KV_BLOCKS]; MAIN then uses a->order, the workspace order, or the identity, as
- * vsa_bwd does. */
+ * validates like vsa_bwd. Run on one stream in the order PREPROCESS, INDEX, DKDV, DQ, they
+ * enqueue exactly the kernels vsa_bwd enqueues and produce the same results. INDEX derives the
+ * q2k lists when they are not given and computes the work orders when num_kv_blocks is in
+ * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS]; otherwise it enqueues nothing. DKDV and DQ
+ * only read what PREPROCESS and INDEX wrote, so they may run in either order. */
 typedef enum {
-  VSA_BWD_PREPROCESS = 0,  /* Delta, dQ accumulator zeroing, zero dk/dv rows of empty kv blocks */
-  VSA_BWD_ORDER = 1,       /* length-binned work order into the workspace */
-  VSA_BWD_MAIN = 2,        /* dk, dv and the dQ partials */
-  VSA_BWD_POSTPROCESS = 3  /* dq = bf16(sm_scale * dQ accumulator) */
+  VSA_BWD_PREPROCESS = 0,  /* Delta; zero dk/dv rows of kv blocks with an empty k2q list */
+  VSA_BWD_INDEX = 1,       /* q2k derivation (if needed) and the length-binned work orders */
+  VSA_BWD_DKDV = 2,        /* kv-major kernel: dk, dv */
+  VSA_BWD_DQ = 3           /* q-major kernel: dq = bf16(sm_scale * dS K) */
 } vsa_bwd_stage_id;
 int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream);
 

@@ -42,14 +42,19 @@ def test_status_strings():
 
 def test_workspace_sizes_and_layout():
     B, H, S = 1, 8, 32768
-    dq_off, delta_off, order_off = V.bwd_workspace_layout(B, H, S)
-    assert dq_off == 0
-    assert delta_off == B * H * S * 128 * 4
-    assert order_off == delta_off + B * H * S * 4
-    assert V.bwd_workspace_bytes(B, H, S) == order_off + B * H * (S // 64) * 4
-    # 256-byte alignment of every region with an odd size
-    d, de, o = V.bwd_workspace_layout(1, 1, 64)
-    assert de % 256 == 0 and o % 256 == 0
+    nb = S // 64
+    offs = [V.bwd_workspace_offset(B, H, S, r) for r in range(V.WS_END + 1)]
+    assert offs[V.WS_DELTA] == 0
+    assert offs[V.WS_KV_ORDER] == B * H * S * 4
+    assert offs[V.WS_Q_ORDER] == offs[V.WS_KV_ORDER] + B * H * nb * 4
+    assert offs[V.WS_Q2K_NUM] == offs[V.WS_Q_ORDER] + B * H * nb * 4
+    assert offs[V.WS_Q2K_IDX] == offs[V.WS_Q2K_NUM] + B * H * nb * 4
+    assert offs[V.WS_BITMAP] == offs[V.WS_Q2K_IDX] + B * H * nb * nb * 4
+    assert offs[V.WS_END] == offs[V.WS_BITMAP] + B * H * nb * ((nb + 31) // 32) * 4
+    assert V.bwd_workspace_bytes(B, H, S, False) == offs[V.WS_Q2K_NUM]
+    assert V.bwd_workspace_bytes(B, H, S, True) == offs[V.WS_END]
+    # every region starts on a 256-byte boundary, also for odd sizes
+    assert all(V.bwd_workspace_offset(1, 3, 64 * 5, r) % 256 == 0 for r in range(V.WS_END + 1))
     assert V.bwd_workspace_bytes(0, 1, 64) == 0
     assert V.invert_workspace_bytes(2, 3, 100, 50) == ((2 * 3 * 50 * 4 * 4 + 255) // 256) * 256
     assert V.invert_workspace_bytes(1, 1, 0, 1) == 0
@@ -58,9 +63,10 @@ def test_workspace_sizes_and_layout():
 def _bwd_args(**over):
     fake = 0x10000  # never dereferenced: validation fails or we do not launch
     a = dict(q=fake, k=fake, v=fake, o=fake, dout=fake, lse=fake, k2q_idx=fake, k2q_num=fake,
-             vbs=fake, order=None, dq=fake, dk=fake, dv=fake, workspace=fake,
-             workspace_bytes=V.bwd_workspace_bytes(1, 2, 256), batch=1, heads=2, seqlen=256,
-             head_dim=128, num_kv_blocks=4, max_q_blocks=4, sm_scale=0.088)
+             q2k_idx=None, q2k_num=None, vbs=fake, order=None, dq=fake, dk=fake, dv=fake,
+             workspace=fake, workspace_bytes=V.bwd_workspace_bytes(1, 2, 256, True), batch=1,
+             heads=2, seqlen=256, head_dim=128, num_kv_blocks=4, max_q_blocks=4, q2k_stride=0,
+             sm_scale=0.088)
     a.update(over)
     return V._BwdArgs(**a)
 
@@ -71,7 +77,14 @@ def _check(args):
 
 def test_bwd_check_accepts_a_valid_call():
     assert _check(_bwd_args()) == VSA_OK
-    assert _check(_bwd_args(num_kv_blocks=3, seqlen=192, workspace_bytes=V.bwd_workspace_bytes(1, 2, 192))) == VSA_OK  # odd nb ok
+    # odd block counts are fine
+    assert _check(_bwd_args(num_kv_blocks=3, seqlen=192,
+                            workspace_bytes=V.bwd_workspace_bytes(1, 2, 192, True))) == VSA_OK
+    # given q2k lists need less workspace
+    small = V.bwd_workspace_bytes(1, 2, 256, False)
+    assert _check(_bwd_args(q2k_idx=0x10000, q2k_num=0x10000, q2k_stride=2,
+                            workspace_bytes=small)) == VSA_OK
+    assert _check(_bwd_args(workspace_bytes=small)) == VSA_EINVAL
 
 
 @pytest.mark.parametrize("over,status", [
@@ -90,6 +103,8 @@ def test_bwd_check_accepts_a_valid_call():
     (dict(dv=None), VSA_EINVAL),
     (dict(workspace=None), VSA_EINVAL),
     (dict(workspace_bytes=1024), VSA_EINVAL),
+    (dict(q2k_idx=0x10000), VSA_EINVAL),
+    (dict(q2k_idx=0x10000, q2k_num=0x10000, q2k_stride=0), VSA_EINVAL),
 ])
 def test_bwd_check_rejects(over, status):
     assert _check(_bwd_args(**over)) == status
@@ -101,7 +116,8 @@ def test_bwd_and_stage_fail_before_launch_on_bad_args():
     a = _bwd_args(head_dim=96)
     assert L.vsa_bwd(ctypes.byref(a), None) == VSA_EUNSUPPORTED
     assert L.vsa_bwd_stage(ctypes.byref(a), 2, None) == VSA_EUNSUPPORTED
-    assert L.vsa_bwd_stage(ctypes.byref(_bwd_args()), 7, None) == VSA_EINVAL
+    assert L.vsa_bwd_stage(ctypes.byref(_bwd_args()), 4, None) == VSA_EINVAL
+    assert L.vsa_bwd_stage(ctypes.byref(_bwd_args()), -1, None) == VSA_EINVAL
 
 
 def test_fwd_check():

@@ -171,13 +171,21 @@ def _bwd_small(c, label):
     ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
     k2q_idx = torch.from_numpy(ridx).to(DEV)
     k2q_num = torch.from_numpy(rnum).to(DEV)
-    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S),), 0xFF, dtype=torch.uint8, device=DEV)
+    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S, True),), 0xFF, dtype=torch.uint8,
+                    device=DEV)
     out = (nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"]))
-    say(f"[backward] {label}")
+    say(f"[backward] {label} (q2k derived from k2q)")
     plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
                      workspace=ws, out=out)
     dq, dk, dv = plan.run()
     torch.cuda.synchronize()
+    # the same call with the forward's q2k lists given: bit-identical results
+    say(f"[backward] {label} (q2k given)")
+    given = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num,
+                                d["vbs"], q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"])
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), given):
+        assert torch.equal(a, b)
     rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
     for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
         assert got.dtype == torch.bfloat16
@@ -234,9 +242,8 @@ def test_backward_edge_cases(name):
         assert np.all(got.float().cpu().numpy()[zero] == 0)
 
 
-def test_backward_user_order_gives_identical_dk_dv():
-    """Any work order: the same dk/dv bits (fixed per-item summation order); dq within fp32
-    summation noise."""
+def test_backward_any_order_gives_identical_bits():
+    """Any kv work order: the same dq, dk, dv bits (fixed per-item summation order, no atomics)."""
     c = workloads.config(2)
     d = to_dev(c)
     o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
@@ -247,9 +254,8 @@ def test_backward_user_order_gives_identical_dk_dv():
     b = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
                             order=rev)
     torch.cuda.synchronize()
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    rel = (a[0].float() - b[0].float()).abs().max() / a[0].float().abs().max()
-    assert rel <= 2e-2
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 def test_nondefault_stream():
@@ -279,13 +285,14 @@ def _end_to_end(c):
     lse = nan_like(torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=DEV))
     V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"], out=(o, lse))
     k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
-    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S),), 0xFF, dtype=torch.uint8, device=DEV)
+    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S, True),), 0xFF, dtype=torch.uint8,
+                    device=DEV)
     out = (nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"]))
     plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
                      workspace=ws, out=out)
     dq, dk, dv = plan.run()
     torch.cuda.synchronize()
-    return d, o, lse, k2q_num, plan, (dq, dk, dv)
+    return d, o, lse, (k2q_idx, k2q_num), plan, (dq, dk, dv)
 
 
 def _sampled_checks(c, o, lse, grads, qblocks, kvblocks):
@@ -319,7 +326,7 @@ def _invariants(c, grads):
 def test_config3_32k_end_to_end_sampled():
     c = workloads.config(3)
     say("[end-to-end] config 3 (B=1 H=8 S=32768, 25%)")
-    d, o, lse, k2q_num, plan, grads = _end_to_end(c)
+    d, o, lse, _, plan, grads = _end_to_end(c)
     _invariants(c, grads)
     _sampled_checks(c, o, lse, grads, qblocks=[(0, 0, 0), (0, 3, 200), (0, 7, 511)],
                     kvblocks=[(0, 0, 1), (0, 5, 300), (0, 7, 511)])
@@ -328,22 +335,22 @@ def test_config3_32k_end_to_end_sampled():
 def test_config4_65k_order_stability_sampled():
     c = workloads.config(4)
     say("[end-to-end] config 4 (B=1 H=8 S=65536, 12.5%, device work order)")
-    d, o, lse, k2q_num, plan, grads = _end_to_end(c)
-    # the library computed the length-binned order into the workspace; it matches the oracle's
-    _, _, order_off = V.bwd_workspace_layout(c.B, c.H, c.S)
+    d, o, lse, (k2q_idx, k2q_num), plan, grads = _end_to_end(c)
+    # the library computed the length-binned orders (kv-major from k2q counts, q-major from the
+    # derived q2k counts) and the q2k lists into the workspace; all match the oracle's
     n = c.B * c.H * c.nb
-    got_order = plan.workspace[order_off:order_off + 4 * n].view(torch.int32).cpu().numpy()
-    assert np.array_equal(got_order, O.work_order(k2q_num.cpu(), 8))
+    ridx, rnum = O.invert_indices(k2q_idx.cpu(), k2q_num.cpu(), c.nb)
+    assert np.array_equal(plan.region(V.WS_Q2K_NUM, n).cpu().numpy().reshape(rnum.shape), rnum)
+    assert np.array_equal(plan.region(V.WS_Q2K_IDX, n * c.nb).cpu().numpy().reshape(ridx.shape), ridx)
+    assert np.array_equal(plan.region(V.WS_KV_ORDER, n).cpu().numpy(), O.work_order(k2q_num.cpu(), 8))
+    assert np.array_equal(plan.region(V.WS_Q_ORDER, n).cpu().numpy(), O.work_order(rnum, 8))
     _invariants(c, grads)
-    # run-to-run: dk, dv bitwise; dq within summation-order noise
+    # run-to-run: every output bitwise equal (no atomics anywhere)
     grads = tuple(t.clone() for t in grads)
     again = plan.run()
     torch.cuda.synchronize()
+    for x, y in zip(grads, again):
+        assert torch.equal(x, y)
     dq, dk, dv = grads
-    assert torch.equal(dk, again[1]) and torch.equal(dv, again[2])
-    diff = (dq.float() - again[0].float()).abs()
-    rel = float(diff.max() / dq.float().abs().max())
-    say(f"  run-to-run dq rel_max={rel:.3e} mean={float(diff.mean()):.3e}")
-    assert rel <= 2e-2 and float(diff.mean()) <= 1e-4
     _sampled_checks(c, o, lse, grads, qblocks=[(0, 1, 7), (0, 6, 1023)],
                     kvblocks=[(0, 2, 0), (0, 7, 777)])
