@@ -162,6 +162,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=(3, 4))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy (a known byte count for "
+                         "scaling hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -172,6 +175,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
     log(f"[bench] workload {args.workload}: steps={args.steps} warmup={args.warmup}")
     res, case = run_workload(args.workload, args.steps, args.warmup)
     log(f"[bench] {json.dumps(res)}")

@@ -21,10 +21,14 @@
 //     v_mfma_f32_32x32x16_bf16 per wave;
 //   * K_j and V_j fragments (the B operands of S and dP) live in registers for the whole item,
 //     with padded kv rows zeroed there;
-//   * Q_i, dO_i (and lse_i, Delta_i) stream through XOR-swizzled LDS tiles filled by
-//     global_load_lds_dwordx4, double-buffered: the next q block loads while this one computes;
+//   * Q_i, dO_i, lse_i, Delta_i stream through a four-stage ring of XOR-swizzled LDS tiles filled
+//     by global_load_lds_dwordx4 three q blocks ahead; one barrier per q block;
+//   * software pipeline across q blocks: step t runs the S/dP MFMAs of q block t+1 interleaved
+//     with the exp2/convert work of q block t, then the dV/dK MFMAs of q block t; every MFMA's LDS
+//     operands are requested one phase before it issues, so LDS latency and bandwidth overlap the
+//     matrix cores;
 //   * P and dS never leave registers: the D layout of S/dP feeds the A operand of dV/dK directly
-//     (the contraction index is permuted to match), the partner operands dO_i^T and Q_i^T come
+//     (the contraction index is permuted to match); the partner operands dO_i^T and Q_i^T come
 //     from ds_read_b64_tr_b16 transposed reads;
 //   * dV and dK are accumulated per q half and the halves are summed through LDS once per item;
 //   * work ids map XCD-first: workgroup ids go round-robin over the 8 XCDs, so XCD x runs a
@@ -37,28 +41,31 @@ namespace vsa {
 
 namespace {
 
+constexpr int STAGES = 4;           // ring depth: stage t%4 holds q block t
+constexpr int STAGE_BYTES = 16384;  // one [64][128] bf16 tile
+constexpr int LD_BYTES = 512;       // lse[64] then Delta[64], fp32
+
 __device__ __forceinline__ void barrier_lds() {
   // Wait for this wave's LDS traffic, then meet the other waves. Vector memory traffic (the next
-  // tile's DMA) stays in flight across the barrier.
+  // tiles' DMA) stays in flight across the barrier.
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-struct Pipe {
-  VSA_LDS char* q;
-  VSA_LDS char* d;
-  VSA_LDS float* ld;
-};
-
+// DMA of q block qb's Q, dO tiles and lse, Delta rows into one ring stage. Every wave issues
+// nine DMAs (four 1-KiB slices of each tile, one 128-byte quarter of lse/Delta), so the
+// outstanding-DMA count is the same in every wave. `off` holds the wave's per-lane tile offsets.
 __device__ __forceinline__ void prefetch(const bf16* __restrict__ qh, const bf16* __restrict__ doh,
                                          const float* __restrict__ lseh,
-                                         const float* __restrict__ deltah, int qb, Pipe p, int lane,
-                                         int w) {
-  const size_t off = (size_t)qb * BLOCK * HEAD_DIM;
-  tile_load_async<4>(qh + off, p.q, lane, w);
-  tile_load_async<4>(doh + off, p.d, lane, w);
-  if (w == 0 && lane < 32) {
-    const float* src = lane < 16 ? lseh + qb * BLOCK + lane * 4 : deltah + qb * BLOCK + (lane - 16) * 4;
-    dma16(src, lds_addr(p.ld));
+                                         const float* __restrict__ deltah, int qb,
+                                         VSA_LDS char* qs, VSA_LDS char* ds, VSA_LDS char* ls,
+                                         const uint32_t* off, int lane, int w) {
+  const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
+  tile_load_async_off<4>(qh + tile, qs, off, w);
+  tile_load_async_off<4>(doh + tile, ds, off, w);
+  if (lane < 8) {
+    // wave 0, 1: lse[0..31], lse[32..63]; wave 2, 3: Delta[0..31], Delta[32..63]
+    const float* src = (w < 2 ? lseh : deltah) + qb * BLOCK + 32 * (w & 1);
+    dma16_sb(src, (uint32_t)(16 * lane), lds_addr(ls + 128 * w));
   }
 }
 
@@ -66,12 +73,9 @@ __device__ __forceinline__ void prefetch(const bf16* __restrict__ qh, const bf16
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char q_s0[16384];
-  __shared__ __attribute__((aligned(1024))) char q_s1[16384];
-  __shared__ __attribute__((aligned(1024))) char do_s0[16384];
-  __shared__ __attribute__((aligned(1024))) char do_s1[16384];
-  __shared__ __attribute__((aligned(16))) float ld_s0[128];
-  __shared__ __attribute__((aligned(16))) float ld_s1[128];
+  __shared__ __attribute__((aligned(1024))) char q_ring[STAGES * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char do_ring[STAGES * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char ld_ring[STAGES * LD_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -105,12 +109,20 @@ bwd_dkdv_kernel(BwdParams p) {
     const int qb = ld_const(list, t);
     return qb < 0 ? 0 : (qb >= p.nb ? p.nb - 1 : qb);
   };
+  VSA_LDS char* const qr = (VSA_LDS char*)q_ring;
+  VSA_LDS char* const dr = (VSA_LDS char*)do_ring;
+  VSA_LDS char* const lr = (VSA_LDS char*)ld_ring;
+  uint32_t toff[4];
+  tile_offsets<4>(toff, lane, w);
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    prefetch(qh, doh, lseh, deltah, qblock(t), qr + st * STAGE_BYTES, dr + st * STAGE_BYTES,
+             lr + st * LD_BYTES, toff, lane, w);
+  };
 
-  // the two pipeline stages; the loop below is unrolled by two so every LDS access names its
-  // buffer statically
-  const Pipe pipe0{(VSA_LDS char*)q_s0, (VSA_LDS char*)do_s0, (VSA_LDS float*)ld_s0};
-  const Pipe pipe1{(VSA_LDS char*)q_s1, (VSA_LDS char*)do_s1, (VSA_LDS float*)ld_s1};
-  prefetch(qh, doh, lseh, deltah, qblock(0), pipe0, lane, w);
+  // q blocks 0, 1, 2 into stages 0, 1, 2
+  issue(0, 0);
+  if (n > 1) issue(1, 1);
+  if (n > 2) issue(2, 2);
 
   // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
   const int kv_l = 32 * wk + l32;
@@ -141,75 +153,145 @@ bwd_dkdv_kernel(BwdParams p) {
     dv_acc[nt] = f32x16{};
     dk_acc[nt] = f32x16{};
   }
-
   const float scale_log2 = p.scale_log2;
+  const int qrow = 32 * wq + l32;
 
-  auto step = [&](int t, const Pipe cu, const Pipe nx) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this q block's tiles have landed (own DMAs)
-    barrier_lds();                               // ... and everyone else's; buffer nx is free
-    if (t + 1 < n) prefetch(qh, doh, lseh, deltah, qblock(t + 1), nx, lane, w);
-    VSA_LDS char* qt = cu.q;
-    VSA_LDS char* dt = cu.d;
-    VSA_LDS float* ld = cu.ld;
-
-    // ---- S = Q K^T and dP = dO V^T for q rows 32*wq.. x kv rows 32*wk.. ----
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-    const int qrow = 32 * wq + l32;
+  // A operands of S = Q K^T and dP = dO V^T for the q block in stage st: q rows 32*wq + l32,
+  // d = 16*s + 8*g + 0..7
+  auto load_rows = [&](int st, bf16x8* qa, bf16x8* da) __attribute__((always_inline)) {
+    VSA_LDS char* qt = qr + st * STAGE_BYTES;
+    VSA_LDS char* dt = dr + st * STAGE_BYTES;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 qa = *(const VSA_LDS bf16x8*)(qt + tile_byte(qrow, 2 * s + g));
-      const bf16x8 da = *(const VSA_LDS bf16x8*)(dt + tile_byte(qrow, 2 * s + g));
-      sacc = mfma32(qa, kf[s], sacc);
-      pacc = mfma32(da, vf[s], pacc);
+      qa[s] = *(const VSA_LDS bf16x8*)(qt + tile_byte(qrow, 2 * s + g));
+      da[s] = *(const VSA_LDS bf16x8*)(dt + tile_byte(qrow, 2 * s + g));
     }
+  };
 
-    // ---- P and dS in registers; element i is q row 32*wq + 8*(i/4) + 4*g + i%4, kv kv_l ----
-    float pv[16], dsv[16];
+  // Prologue: S/dP of q block 0, and the row operands of q block 1, in registers.
+  f32x16 s0, p0, s1, p1;
+  bf16x8 qa0[8], da0[8], qa1[8], da1[8];
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stages 0..2 landed (own DMAs)
+  barrier_lds();
+  load_rows(0, qa0, da0);
+  s0 = f32x16{};
+  p0 = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    s0 = mfma32(qa0[s], kf[s], s0);
+    p0 = mfma32(da0[s], vf[s], p0);
+  }
+  load_rows(1, qa1, da1);  // stale but in bounds when n == 1
+
+  // Step t (q block t in stage st, t+1 in st1, t+2 in st2; q block t+3 is fetched into st3):
+  //   on entry S/dP of t are in (sc, pc) and the row operands of t+1 in (qa, da);
+  //   phase B: S/dP MFMAs of t+1 from (qa, da), interleaved with P, dS of t (lse/Delta reads
+  //            first) and the transposed dO^T, Q^T reads of t;
+  //   phase C: dV/dK MFMAs of t, interleaved with the row-operand reads of t+2 into (qn, dn).
+  // Every MFMA's LDS operands were requested a phase earlier. The last steps compute throwaway
+  // S/dP and rows from stale (in-bounds, quiescent) stages, which keeps the body free of
+  // branches. The loop is unrolled by four so every stage offset is a compile-time constant.
+  auto step = [&](int t, int st, int st2, int st3, f32x16& sc, f32x16& pc, f32x16& sn,
+                  f32x16& pn, bf16x8* qa, bf16x8* da, bf16x8* qn, bf16x8* dn)
+                  __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stage t+2 landed (own DMAs)
+    barrier_lds();  // ... everyone's; and everyone is done with stage st3 (q block t-1)
+    if (t + 3 < n) issue(t + 3, st3);
+    VSA_LDS char* qt = qr + st * STAGE_BYTES;
+    VSA_LDS char* dt = dr + st * STAGE_BYTES;
+    VSA_LDS float* ld = (VSA_LDS float*)(lr + st * LD_BYTES);
+
+    // ---- phase B ----
+    // element i of S is q row 32*wq + 8*(i/4) + 4*g + i%4
+    f32x4 lse4[4], del4[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int qr = 32 * wq + 8 * c + 4 * g;
-      const f32x4 lse4 = *(const VSA_LDS f32x4*)(ld + qr);
-      const f32x4 del4 = *(const VSA_LDS f32x4*)(ld + 64 + qr);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * c + e;
-        const float pe = __builtin_amdgcn_exp2f(sacc[i] * scale_log2 - lse4[e]);
-        pv[i] = kv_valid ? pe : 0.0f;
-        dsv[i] = pv[i] * (pacc[i] - del4[e]);
-      }
+      const int q = 32 * wq + 8 * c + 4 * g;
+      lse4[c] = *(const VSA_LDS f32x4*)(ld + q);
+      del4[c] = *(const VSA_LDS f32x4*)(ld + 64 + q);
     }
-
-    // ---- dV += P^T dO and dK += dS^T Q over this wave's q half ----
+    // transposed B operands of dV/dK for q block t: k slot jj of step s2 is q row
+    // 32*wq + 16*s2 + 8*(jj/4) + 4*g + jj%4, matching the D layout of S
+    bf16x8 db[2][4], qbt[2][4];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 pa = pack8(pv[8 * s2 + 0], pv[8 * s2 + 1], pv[8 * s2 + 2], pv[8 * s2 + 3],
-                              pv[8 * s2 + 4], pv[8 * s2 + 5], pv[8 * s2 + 6], pv[8 * s2 + 7]);
-      const bf16x8 sa = pack8(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
-                              dsv[8 * s2 + 4], dsv[8 * s2 + 5], dsv[8 * s2 + 6], dsv[8 * s2 + 7]);
       const int q0 = 32 * wq + 16 * s2 + 4 * (grp >> 1) + (t16 >> 2);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int col = 32 * nt + 16 * (grp & 1) + 4 * (t16 & 3);
-        const bf16x8 db = join(lds_read_tr(dt + tile_elem_byte(q0, col)),
-                               lds_read_tr(dt + tile_elem_byte(q0 + 8, col)));
-        const bf16x8 qbv = join(lds_read_tr(qt + tile_elem_byte(q0, col)),
-                                lds_read_tr(qt + tile_elem_byte(q0 + 8, col)));
-        dv_acc[nt] = mfma32(pa, db, dv_acc[nt]);
-        dk_acc[nt] = mfma32(sa, qbv, dk_acc[nt]);
+        db[s2][nt] = join(lds_read_tr(dt + tile_elem_byte(q0, col)),
+                          lds_read_tr(dt + tile_elem_byte(q0 + 8, col)));
+        qbt[s2][nt] = join(lds_read_tr(qt + tile_elem_byte(q0, col)),
+                           lds_read_tr(qt + tile_elem_byte(q0 + 8, col)));
       }
     }
+    sn = f32x16{};
+    pn = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      sn = mfma32(qa[s], kf[s], sn);
+      pn = mfma32(da[s], vf[s], pn);
+    }
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * c + e;
+        const float pe = __builtin_amdgcn_exp2f(sc[i] * scale_log2 - lse4[c][e]);
+        pv[i] = kv_valid ? pe : 0.0f;
+        dsv[i] = pv[i] * (pc[i] - del4[c][e]);
+      }
+    }
+    bf16x8 pa[2], sa[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      pa[s2] = pack8(pv[8 * s2 + 0], pv[8 * s2 + 1], pv[8 * s2 + 2], pv[8 * s2 + 3],
+                     pv[8 * s2 + 4], pv[8 * s2 + 5], pv[8 * s2 + 6], pv[8 * s2 + 7]);
+      sa[s2] = pack8(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
+                     dsv[8 * s2 + 4], dsv[8 * s2 + 5], dsv[8 * s2 + 6], dsv[8 * s2 + 7]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // lse/Delta reads
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase C ----
+    load_rows(st2, qn, dn);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        dv_acc[nt] = mfma32(pa[s2], db[s2][nt], dv_acc[nt]);
+        dk_acc[nt] = mfma32(sa[s2], qbt[s2][nt], dk_acc[nt]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one row read
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  for (int t = 0; t < n; t += 2) {
-    step(t, pipe0, pipe1);
-    if (t + 1 < n) step(t + 1, pipe1, pipe0);
+  for (int t = 0; t < n; t += 4) {
+    step(t, 0, 2, 3, s0, p0, s1, p1, qa1, da1, qa0, da0);
+    if (t + 1 < n) step(t + 1, 1, 3, 0, s1, p1, s0, p0, qa0, da0, qa1, da1);
+    if (t + 2 < n) step(t + 2, 2, 0, 1, s0, p0, s1, p1, qa1, da1, qa0, da0);
+    if (t + 3 < n) step(t + 3, 3, 1, 2, s1, p1, s0, p0, qa0, da0, qa1, da1);
   }
 
   // ---- sum the two q halves of dV/dK through LDS, scale, round, store ----
-  barrier_lds();  // every wave is past its last LDS read of the q/dO buffers
+  barrier_lds();  // every wave is past its last LDS read of the rings
   // wave wq=1 hands over its dV half, wave wq=0 its dK half (16 KiB each, lane-native order);
-  // kv half 0 uses the q buffers, kv half 1 the dO buffers
-  VSA_LDS f32x4* dv_x = (VSA_LDS f32x4*)(wk == 0 ? (VSA_LDS char*)q_s0 : (VSA_LDS char*)do_s0);
-  VSA_LDS f32x4* dk_x = (VSA_LDS f32x4*)(wk == 0 ? (VSA_LDS char*)q_s1 : (VSA_LDS char*)do_s1);
+  // kv half 0 uses the first two q stages, kv half 1 the first two dO stages
+  VSA_LDS char* xbase = wk == 0 ? qr : dr;
+  VSA_LDS f32x4* dv_x = (VSA_LDS f32x4*)xbase;
+  VSA_LDS f32x4* dk_x = (VSA_LDS f32x4*)(xbase + STAGE_BYTES);
   VSA_LDS f32x4* mine_out = wq == 1 ? dv_x : dk_x;
   VSA_LDS f32x4* theirs = wq == 1 ? dk_x : dv_x;
 #pragma unroll

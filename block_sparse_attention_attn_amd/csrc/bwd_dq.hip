@@ -107,12 +107,16 @@ bwd_dq_kernel(BwdParams p) {
     // ---- S^T = K Q^T and dP^T = V dO^T: kv rows 32*wk.., q columns 32*wq.. ----
     f32x16 sacc = f32x16{}, pacc = f32x16{};
     const int kvrow = 32 * wk + l32;
+    bf16x8 ka[8], va[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 ka = *(const VSA_LDS bf16x8*)(kt + tile_byte(kvrow, 2 * s + g));
-      const bf16x8 va = *(const VSA_LDS bf16x8*)(vt + tile_byte(kvrow, 2 * s + g));
-      sacc = mfma32(ka, qf[s], sacc);
-      pacc = mfma32(va, df[s], pacc);
+      ka[s] = *(const VSA_LDS bf16x8*)(kt + tile_byte(kvrow, 2 * s + g));
+      va[s] = *(const VSA_LDS bf16x8*)(vt + tile_byte(kvrow, 2 * s + g));
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      sacc = mfma32(ka[s], qf[s], sacc);
+      pacc = mfma32(va[s], df[s], pacc);
     }
 
     // ---- dS^T; element e is kv 32*wk + 8*(e/4) + 4*g + e%4. Masked kv rows are selected to 0

@@ -77,31 +77,22 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
 // ---------------------------------------------------------------------------------------------
 // LDS tile formats
 // ---------------------------------------------------------------------------------------------
-// A [64 rows][128] bf16 tile (Q, dO, K, V) occupies 16 KiB = 64 rows x 16 chunks of 16 bytes.
-// Chunk cc of row r is stored at chunk slot r*16 + (cc ^ swz128(r)). swz128 permutes the low
-// four row bits (b3 b2 b1 b0) -> (b3 b1 b0 b2): a bijection on any 16 aligned rows, so 16 lanes
-// reading the same chunk of 16 consecutive rows hit 16 different bank groups; and for 4 aligned
-// rows it XORs the row's low two bits into chunk bits 1..2, so a transposed read of two adjacent
-// chunks of 4 aligned rows touches 8 different bank groups.
-__device__ __forceinline__ int swz128(int r) {
-  return (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1);
-}
+// A [64 rows][128] bf16 tile (Q, dO, K, V) occupies 16 KiB = 64 rows x 16 chunks of 16 bytes; a
+// row is exactly the 64 banks x 4 bytes of LDS, so the bank group of a chunk is its slot in the
+// row. Chunk cc of row r is stored at chunk slot r*16 + (cc ^ swz128(r)) with
+// swz128(r) = ((r >> 2) & 3) | ((r & 3) << 2), a swap of the row's two low bit pairs:
+//   * 16 lanes reading the same chunk of 16 aligned rows (an MFMA operand read, ds_read_b128)
+//     see swz128 take all 16 values: 16 different bank groups;
+//   * 32 lanes of a transposed read (ds_read_b64_tr_b16) cover 4 aligned rows x 4 aligned chunks:
+//     the chunk's low bits XOR a row constant, its high bits XOR the row's low bits, so the 16
+//     (row, chunk) pairs land in 16 different bank groups.
+__device__ __forceinline__ int swz128(int r) { return ((r >> 2) & 3) | ((r & 3) << 2); }
 __device__ __forceinline__ int tile_byte(int r, int cc) {  // byte offset of chunk cc of row r
   return (r * 16 + (cc ^ swz128(r))) * 16;
 }
 // Byte offset of element (r, c) (c = column 0..127, a multiple of 4 for 8-byte accesses).
 __device__ __forceinline__ int tile_elem_byte(int r, int c) {
   return tile_byte(r, c >> 3) + (c & 7) * 2;
-}
-
-// A [64 rows][64] bf16 tile (dS^T) occupies 8 KiB = 64 rows x 8 chunks. Chunk cc of row r is at
-// slot r*8 + (cc ^ swz64(r)); swz64 maps row bits (b3 b2 b1) -> chunk bits (2 0 1). Rows of one
-// parity share bank halves (128-byte rows), so the permutation runs on r >> 1.
-__device__ __forceinline__ int swz64(int r) {
-  return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2);
-}
-__device__ __forceinline__ int ds_elem_byte(int r, int c) {
-  return (r * 8 + ((c >> 3) ^ swz64(r))) * 16 + (c & 7) * 2;
 }
 
 // s_waitcnt immediate that waits until at most `n` vector memory operations are outstanding
@@ -121,7 +112,7 @@ __device__ __forceinline__ T ld_const(const T* p, size_t i) {
 // it; callers wait with an explicit s_waitcnt vmcnt before a barrier that publishes the tile.
 // M0 is saved and restored around the DMA (the compiler does not allow it on a clobber list).
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -135,6 +126,48 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 
 // Index of the calling wave inside its workgroup, as a value the compiler knows to be uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// The same DMA with a uniform 64-bit base (SGPRs) and a per-lane 32-bit byte offset, so issuing it
+// costs no vector address arithmetic.
+__device__ __forceinline__ void dma16_sb(const void* base_ptr, uint32_t voff, uint32_t lds_base) {
+  const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base);
+  // readfirstlane returns a signed int: go through uint32_t so the low half is zero-extended
+  const uint64_t b = (uint64_t)(uintptr_t)base_ptr;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lb)
+      : "memory");
+}
+
+// Per-lane byte offsets inside a [64][128] bf16 tile for the slices part, part + NPARTS, ... that
+// tile_load_async<NPARTS> would issue (the same for every tile).
+template <int NPARTS>
+__device__ __forceinline__ void tile_offsets(uint32_t* off, int lane, int part) {
+#pragma unroll
+  for (int i = 0; i < 16 / NPARTS; ++i) {
+    const int slot = (part + i * NPARTS) * 64 + lane;
+    const int r = slot >> 4;
+    const int cc = (slot & 15) ^ swz128(r);
+    off[i] = (uint32_t)((r * HEAD_DIM + cc * 8) * 2);
+  }
+}
+
+// Copy one tile with precomputed offsets: slice part + i*NPARTS goes to LDS lds + (part+i*NPARTS) KiB.
+template <int NPARTS>
+__device__ __forceinline__ void tile_load_async_off(const bf16* g, VSA_LDS char* lds,
+                                                    const uint32_t* off, int part) {
+#pragma unroll
+  for (int i = 0; i < 16 / NPARTS; ++i)
+    dma16_sb(g, off[i], (uint32_t)(uintptr_t)(lds + (part + i * NPARTS) * 1024));
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const VSA_LDS void* p) {
   return (uint32_t)(uintptr_t)p;
