@@ -232,14 +232,15 @@ bwd_dkdv_kernel(BwdParams p) {
       sn = mfma32(qa[s], kf[s], sn);
       pn = mfma32(da[s], vf[s], pn);
     }
+    // P and dS of q block t. A padded kv column (zero K/V fragment) gets some finite or
+    // non-finite P; it only feeds that kv row of dV/dK, which the epilogue overwrites with 0.
     float pv[16], dsv[16];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * c + e;
-        const float pe = __builtin_amdgcn_exp2f(sc[i] * scale_log2 - lse4[c][e]);
-        pv[i] = kv_valid ? pe : 0.0f;
+        pv[i] = __builtin_amdgcn_exp2f(sc[i] * scale_log2 - lse4[c][e]);
         dsv[i] = pv[i] * (pc[i] - del4[c][e]);
       }
     }
@@ -315,7 +316,8 @@ bwd_dkdv_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e) {
         const float mine = wq == 0 ? dv_acc[nt][4 * c + e] : dk_acc[nt][4 * c + e];
         const int kv = 32 * wk + 8 * c + 4 * g + e;
-        outp[(size_t)kv * HEAD_DIM + d] = (bf16)((mine + o[e]) * oscale);
+        // padded kv rows are exactly zero by definition
+        outp[(size_t)kv * HEAD_DIM + d] = kv < vb ? (bf16)((mine + o[e]) * oscale) : (bf16)0.0f;
       }
     }
   }

@@ -19,15 +19,21 @@
 // gfx950 layout: one 256-thread workgroup per q block; wave w owns q rows 32*(w&1).. and kv rows
 // 32*(w>>1).. of every kv block. Q_i and dO_i live in registers as the B operands of S^T = K Q^T
 // and dP^T = V dO^T (v_mfma_f32_32x32x16_bf16), so lse and Delta are one scalar per lane. K_j,
-// V_j stream through swizzled, double-buffered LDS tiles (global_load_lds_dwordx4). dS^T stays in
-// registers as the B operand of dQ^T += K^T dS^T, with K^T from ds_read_b64_tr_b16. The two kv
-// halves' partial dQ^T are summed through LDS once per q block.
+// V_j stream through a four-stage ring of swizzled LDS tiles fetched three kv blocks ahead
+// (global_load_lds_dwordx4). Step t runs the S^T/dP^T MFMAs of kv block t+1 interleaved with the
+// exp2/convert work of kv block t and its K^T transposed reads (ds_read_b64_tr_b16), then the
+// dQ^T += K^T dS^T MFMAs of kv block t interleaved with the K/V row reads of kv block t+2: every
+// MFMA's LDS operands are requested a phase before it issues. dS^T stays in registers as the B
+// operand. The two kv halves' partial dQ^T are summed through LDS once per q block.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
 namespace vsa {
 
 namespace {
+
+constexpr int STAGES = 4;
+constexpr int STAGE_BYTES = 16384;
 
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -37,10 +43,8 @@ __device__ __forceinline__ void barrier_lds() {
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char k_s0[16384];
-  __shared__ __attribute__((aligned(1024))) char k_s1[16384];
-  __shared__ __attribute__((aligned(1024))) char v_s0[16384];
-  __shared__ __attribute__((aligned(1024))) char v_s1[16384];
+  __shared__ __attribute__((aligned(1024))) char k_ring[STAGES * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_ring[STAGES * STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -60,25 +64,41 @@ bwd_dq_kernel(BwdParams p) {
   const int bh = item / p.nb;
   const int i = item - bh * p.nb;
   const size_t head = (size_t)bh * p.S * HEAD_DIM;
+  const bf16* __restrict__ kh = p.k + head;
+  const bf16* __restrict__ vh = p.v + head;
   const int* __restrict__ list = p.q2k_idx + (size_t)item * p.q2k_stride;
   auto kvblock = [&](int t) {
     const int kb = ld_const(list, t);
     return kb < 0 ? 0 : (kb >= p.nb ? p.nb - 1 : kb);
   };
+  VSA_LDS char* const kr = (VSA_LDS char*)k_ring;
+  VSA_LDS char* const vr = (VSA_LDS char*)v_ring;
+  uint32_t toff[4];
+  tile_offsets<4>(toff, lane, w);
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    const size_t tile = (size_t)kvblock(t) * BLOCK * HEAD_DIM;
+    tile_load_async_off<4>(kh + tile, kr + st * STAGE_BYTES, toff, w);
+    tile_load_async_off<4>(vh + tile, vr + st * STAGE_BYTES, toff, w);
+  };
+  if (n > 0) issue(0, 0);
+  if (n > 1) issue(1, 1);
+  if (n > 2) issue(2, 2);
 
   // B operands: lane holds q row 32*wq + l32, d = 16*s + 8*g + 0..7
   const int qrow = i * BLOCK + 32 * wq + l32;
   bf16x8 qf[8], df[8];
   {
-    const bf16x8* qr = (const bf16x8*)(p.q + head + (size_t)qrow * HEAD_DIM);
-    const bf16x8* dr = (const bf16x8*)(p.dout + head + (size_t)qrow * HEAD_DIM);
+    const bf16x8* qrp = (const bf16x8*)(p.q + head + (size_t)qrow * HEAD_DIM);
+    const bf16x8* drp = (const bf16x8*)(p.dout + head + (size_t)qrow * HEAD_DIM);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      qf[s] = qr[2 * s + g];
-      df[s] = dr[2 * s + g];
+      qf[s] = qrp[2 * s + g];
+      df[s] = drp[2 * s + g];
     }
   }
-  const float lse_q = p.lse[(size_t)bh * p.S + qrow];
+  // a q row with no valid key has lse = -inf; +inf makes its P exactly 0 (no inf * 0)
+  float lse_q = p.lse[(size_t)bh * p.S + qrow];
+  lse_q = lse_q == -__builtin_inff() ? __builtin_inff() : lse_q;
   const float delta_q = p.delta[(size_t)bh * p.S + qrow];
   const float scale_log2 = p.scale_log2;
 
@@ -87,89 +107,141 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) dq_acc[mt] = f32x16{};
 
-  if (n > 0) {
-    const size_t off = (size_t)kvblock(0) * BLOCK * HEAD_DIM;
-    tile_load_async<4>(p.k + head + off, (VSA_LDS char*)k_s0, lane, w);
-    tile_load_async<4>(p.v + head + off, (VSA_LDS char*)v_s0, lane, w);
-  }
-
-  auto step = [&](int t, VSA_LDS char* kt, VSA_LDS char* vt, VSA_LDS char* kn_s,
-                  VSA_LDS char* vn_s) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    barrier_lds();
-    if (t + 1 < n) {
-      const size_t off = (size_t)kvblock(t + 1) * BLOCK * HEAD_DIM;
-      tile_load_async<4>(p.k + head + off, kn_s, lane, w);
-      tile_load_async<4>(p.v + head + off, vn_s, lane, w);
-    }
-    const int vb = ld_const(p.vbs, kvblock(t));
-
-    // ---- S^T = K Q^T and dP^T = V dO^T: kv rows 32*wk.., q columns 32*wq.. ----
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-    const int kvrow = 32 * wk + l32;
-    bf16x8 ka[8], va[8];
+  const int kvrow = 32 * wk + l32;
+  // A operands of S^T = K Q^T and dP^T = V dO^T: kv row 32*wk + l32, d = 16*s + 8*g + 0..7
+  auto load_rows = [&](int st, bf16x8* ka, bf16x8* va) __attribute__((always_inline)) {
+    VSA_LDS char* kt = kr + st * STAGE_BYTES;
+    VSA_LDS char* vt = vr + st * STAGE_BYTES;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       ka[s] = *(const VSA_LDS bf16x8*)(kt + tile_byte(kvrow, 2 * s + g));
       va[s] = *(const VSA_LDS bf16x8*)(vt + tile_byte(kvrow, 2 * s + g));
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      sacc = mfma32(ka[s], qf[s], sacc);
-      pacc = mfma32(va[s], df[s], pacc);
-    }
+  };
 
-    // ---- dS^T; element e is kv 32*wk + 8*(e/4) + 4*g + e%4. Masked kv rows are selected to 0
-    // (never multiplied: a padded V row may hold anything) ----
-    float dsv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kv = 32 * wk + 8 * (e >> 2) + 4 * g + (e & 3);
-      const float pe = __builtin_amdgcn_exp2f(sacc[e] * scale_log2 - lse_q);
-      const float ds = pe * (pacc[e] - delta_q);
-      dsv[e] = kv < vb ? ds : 0.0f;
-    }
-
-    // ---- dQ^T += K^T dS^T; k slot jj of step s2 is kv 32*wk + 16*s2 + 8*(jj/4) + 4*g + jj%4 ----
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 b = pack8(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
-                             dsv[8 * s2 + 4], dsv[8 * s2 + 5], dsv[8 * s2 + 6], dsv[8 * s2 + 7]);
-      const int kv0 = 32 * wk + 16 * s2 + 4 * (grp >> 1) + (t16 >> 2);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int col = 32 * mt + 16 * (grp & 1) + 4 * (t16 & 3);
-        bf16x8 a = join(lds_read_tr(kt + tile_elem_byte(kv0, col)),
-                        lds_read_tr(kt + tile_elem_byte(kv0 + 8, col)));
-        if (vb < BLOCK) {  // padded K rows may hold anything: zero them (0 * NaN = NaN)
-          const int kvb = 32 * wk + 16 * s2 + 4 * g;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            if (kvb + 8 * (jj >> 2) + (jj & 3) >= vb) a[jj] = (bf16)0.0f;
-        }
-        dq_acc[mt] = mfma32(a, b, dq_acc[mt]);
+  // A kv block with padded rows (vbs < 64): once its tiles have landed, zero those K and V rows
+  // in LDS (they may hold anything), then meet at a barrier before anyone reads them. Rare: a
+  // uniform branch taken only for ragged blocks.
+  auto zero_padding = [&](int t, int st) __attribute__((always_inline)) {
+    const int vb = ld_const(p.vbs, kvblock(t));
+    if (vb < BLOCK) {
+      const int first = vb < 0 ? 0 : vb;
+      for (int c = first * 16 + (int)threadIdx.x; c < BLOCK * 16; c += 256) {
+        *(VSA_LDS i32x4*)(kr + st * STAGE_BYTES + c * 16) = i32x4{};
+        *(VSA_LDS i32x4*)(vr + st * STAGE_BYTES + c * 16) = i32x4{};
       }
+      barrier_lds();
     }
   };
-  for (int t = 0; t < n; t += 2) {
-    step(t, (VSA_LDS char*)k_s0, (VSA_LDS char*)v_s0, (VSA_LDS char*)k_s1, (VSA_LDS char*)v_s1);
-    if (t + 1 < n)
-      step(t + 1, (VSA_LDS char*)k_s1, (VSA_LDS char*)v_s1, (VSA_LDS char*)k_s0, (VSA_LDS char*)v_s0);
+
+  if (n > 0) {
+    f32x16 s0, p0, s1, p1;
+    bf16x8 ka0[8], va0[8], ka1[8], va1[8];
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stages 0..2 landed (own DMAs)
+    barrier_lds();
+    zero_padding(0, 0);
+    if (n > 1) zero_padding(1, 1);
+    load_rows(0, ka0, va0);
+    s0 = f32x16{};
+    p0 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      s0 = mfma32(ka0[s], qf[s], s0);
+      p0 = mfma32(va0[s], df[s], p0);
+    }
+    load_rows(1, ka1, va1);  // stale but in bounds when n == 1
+
+    // Step t (kv block t in stage st, t+2 in st2; kv block t+3 is fetched into st3): on entry
+    // S^T/dP^T of t are in (sc, pc) and the row operands of t+1 in (ka, va). The last steps use
+    // stale (in-bounds, quiescent) stages for throwaway work, keeping the body branch-free.
+    auto step = [&](int t, int st, int st2, int st3, f32x16& sc, f32x16& pc, f32x16& sn,
+                    f32x16& pn, bf16x8* ka, bf16x8* va, bf16x8* kn, bf16x8* vn)
+                    __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stage t+2 landed (own DMAs)
+      barrier_lds();  // ... everyone's; everyone is done with stage st3 (kv block t-1)
+      if (t + 3 < n) issue(t + 3, st3);
+      if (t + 2 < n) zero_padding(t + 2, st2);  // before anyone reads kv block t+2
+      VSA_LDS char* kt = kr + st * STAGE_BYTES;
+
+      // ---- phase B: S^T/dP^T of kv block t+1; dS^T of kv block t; K^T reads of t ----
+      // K^T A operand of dQ: lane holds d = 32*mt + l32, k slot jj of step s2 is kv
+      // 32*wk + 16*s2 + 8*(jj/4) + 4*g + jj%4, matching the D layout of S^T
+      bf16x8 kt_op[2][4];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kv0 = 32 * wk + 16 * s2 + 4 * (grp >> 1) + (t16 >> 2);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int col = 32 * mt + 16 * (grp & 1) + 4 * (t16 & 3);
+          kt_op[s2][mt] = join(lds_read_tr(kt + tile_elem_byte(kv0, col)),
+                               lds_read_tr(kt + tile_elem_byte(kv0 + 8, col)));
+        }
+      }
+      sn = f32x16{};
+      pn = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sn = mfma32(ka[s], qf[s], sn);
+        pn = mfma32(va[s], df[s], pn);
+      }
+      // dS^T of kv block t. Padded kv rows need no mask here: their K and V rows are zero in
+      // LDS, so dP^T is 0, dS^T is finite, and their K^T rows add nothing to dQ.
+      float dsv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sc[e] * scale_log2 - lse_q);
+        dsv[e] = pe * (pc[e] - delta_q);
+      }
+      bf16x8 b[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        b[s2] = pack8(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
+                      dsv[8 * s2 + 4], dsv[8 * s2 + 5], dsv[8 * s2 + 6], dsv[8 * s2 + 7]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one transposed read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- phase C: dQ^T += K^T dS^T of kv block t; row reads of kv block t+2 ----
+      load_rows(st2, kn, vn);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) dq_acc[mt] = mfma32(kt_op[s2][mt], b[s2], dq_acc[mt]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two row reads
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int t = 0; t < n; t += 4) {
+      step(t, 0, 2, 3, s0, p0, s1, p1, ka1, va1, ka0, va0);
+      if (t + 1 < n) step(t + 1, 1, 3, 0, s1, p1, s0, p0, ka0, va0, ka1, va1);
+      if (t + 2 < n) step(t + 2, 2, 0, 1, s0, p0, s1, p1, ka1, va1, ka0, va0);
+      if (t + 3 < n) step(t + 3, 3, 1, 2, s1, p1, s0, p0, ka0, va0, ka1, va1);
+    }
   }
 
   // ---- sum the two kv halves: wave wk=0 finishes d tiles 0,1, wave wk=1 tiles 2,3 ----
-  barrier_lds();  // all LDS reads of the K/V tiles are done
-  VSA_LDS f32x4* xch = (VSA_LDS f32x4*)(wq == 0 ? (VSA_LDS char*)k_s0 : (VSA_LDS char*)k_s1);
+  barrier_lds();  // all LDS reads of the K/V ring are done
+  VSA_LDS f32x4* xch = (VSA_LDS f32x4*)(kr + wq * STAGE_BYTES);
   // region r holds the tiles that wave (wq, r) finishes, written by its partner (wq, 1 - r)
   VSA_LDS f32x4* give = xch + (wk == 0 ? 512 : 0);
   VSA_LDS f32x4* take = xch + (wk == 0 ? 0 : 512);
+  // (tiles are picked with selects, not a runtime index: that would move dq_acc to scratch)
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int mt = (wk == 0 ? 2 : 0) + u;  // the partner's tiles
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      give[(u * 4 + c) * 64 + lane] =
-          f32x4{dq_acc[mt][4 * c], dq_acc[mt][4 * c + 1], dq_acc[mt][4 * c + 2], dq_acc[mt][4 * c + 3]};
+    for (int c = 0; c < 4; ++c) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = wk == 0 ? dq_acc[2 + u][4 * c + e] : dq_acc[u][4 * c + e];
+      give[(u * 4 + c) * 64 + lane] = v;  // the partner's tiles
+    }
   }
   barrier_lds();
   bf16* dqrow = p.dq + head + (size_t)qrow * HEAD_DIM;
@@ -185,7 +257,10 @@ bwd_dq_kernel(BwdParams p) {
         s16x4 s;
       } r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r.b[e] = (bf16)((dq_acc[mt][4 * c + e] + o[e]) * sc);
+      for (int e = 0; e < 4; ++e) {
+        const float mine = wk == 0 ? dq_acc[u][4 * c + e] : dq_acc[2 + u][4 * c + e];
+        r.b[e] = (bf16)((mine + o[e]) * sc);
+      }
       *(s16x4*)(dqrow + 32 * mt + 8 * c + 4 * g) = r.s;
     }
   }
