@@ -3,16 +3,22 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4] [--no-cpu-baseline]
 
 One step runs the whole path once over one batch of synthetic input already resident in HBM:
-invert_indices (q2k -> k2q), the forward (o, lse), and the backward chain (preprocess, work order,
-main kernel, postprocess). Every stage is bracketed by HIP events on the stream it runs on.
+invert_indices (q2k -> k2q), the forward (o, lse), and the backward chain (preprocess; index stage =
+work order; kv-major dK/dV kernel; q-major dQ kernel with the dQ scale/convert fused). Every stage is
+bracketed by HIP events on the stream it runs on (torch's current stream, which the binding passes).
 
   value       = selected-block FLOPs of the backward / time of the backward chain, where
                 selected-block FLOPs = pairs * 5 GEMMs * 2*64*64*128 (the FastVideo commit
                 message's "TFLOPS on selected blocks", kernels-only window: preprocess -> order ->
                 main -> postprocess);
   ms_per_step = mean time of a whole step (invert + forward + backward);
-  roofline    = the main backward kernel: its selected-block FLOPs / its mean launch duration,
-                against the MI355X dense bf16 MFMA peak (2.5 PFLOP/s);
+  roofline    = the dominant backward kernel, bwd_dkdv_kernel (kv-major dK/dV): its algorithmic
+                FLOPs (4 GEMMs of 2*64*64*128 per selected pair: S, dP, dV, dK) / its mean launch
+                duration measured with HIP events on its stream, against the MI355X dense bf16 MFMA
+                peak (2.5 PFLOP/s). `traffic` is the bytes per launch that rocprofv3's FETCH_SIZE and
+                WRITE_SIZE counters gave (scaled by a plain copy's reading), taken from the committed
+                summary in profiles/ while the kernel's sources still hash to the value recorded
+                there, else null;
   cpu_baseline= the float64 CPU oracle's backward on a bounded sample of the same workload.
 
 The headline workload is B=1 H=8 S=32768 D=128, 25 % density (default); --workload 4 selects
@@ -42,6 +48,32 @@ WORKLOAD_TEXT = {
     4: "VSA 64-token block-sparse attention backward, B=1 H=8 S=65536 D=128 bf16, 12.5% density "
        "(top-k 128 of 1024 kv blocks per q block), all blocks full, device work order",
 }
+
+
+PROFILE = {3: "profiles/backward_S32768_H8_topk128of512.md"}
+KERNEL_SOURCES = ("bwd_dkdv.hip", "vsa_device.h", "vsa_kernels.h")
+
+
+def counter_traffic(workload, kernel="bwd_dkdv_kernel"):
+    """Bytes per launch of `kernel` from the committed rocprofv3 summary, or None when there is no
+    summary for this workload or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, PROFILE.get(workload, "-"))
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_attn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    section, traffic, sha = None, None, None
+    for line in open(path):
+        if line.startswith("### "):
+            section = line[4:].strip()
+        elif section == kernel and line.startswith("- traffic_bytes_per_launch:"):
+            traffic = int(line.split(":")[1])
+        elif section == kernel and line.startswith("- source_sha256:"):
+            sha = line.split(":")[1].split()[0]
+    return traffic if sha == h.hexdigest() else None
 
 
 def log(msg):
@@ -235,7 +267,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(args.workload),
+            "traffic_unit": "bytes per launch (FETCH_SIZE x copy factor + WRITE_SIZE)",
         },
         "secondary": secondary,
         "cpu_baseline": cpu,

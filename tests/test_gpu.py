@@ -6,6 +6,11 @@ Gates (per tensor):
     beyond the irreducible rounding of the bf16 outputs, i.e.
     mean|gpu - ref| <= 1e-3 * mean|ref| + mean|bf16(ref) - ref|  (ref = unrounded oracle);
     the absolute mean of the FastVideo test page (mean|diff| <= 1e-3) is reported too;
+  * o (the forward's output, not a gradient): the same rel-max; its mean bound also allows for the
+    bf16 rounding of the P operand of o = P V (relative error <= 2^-9 per element, independent
+    across keys, so the error of an element of o has rms <= 2^-9 * sqrt(sum_j P_ij^2 v_jd^2) =
+    2^-9 * sigma): mean|gpu - ref| <= max(1e-3 * mean|ref|, 2^-8 * mean sigma) + rounding. At
+    524288 tokens o sums 131072 values of either sign and mean|o| is small against sigma;
   * lse: max|gpu - ref| <= 1e-4 (absolute, base-2 units);
   * exact zeros where the method defines them (unselected kv blocks, padded kv rows, empty q rows).
 Small workloads are compared in full; the 32k and 65k-token workloads on sampled blocks, each
@@ -55,8 +60,9 @@ def nan_like(t):
     return out
 
 
-def check_close(name, got, ref, report=None):
-    """got: GPU tensor (any float dtype); ref: float64 numpy array of the same shape."""
+def check_close(name, got, ref, report=None, operand_allowance=0.0):
+    """got: GPU tensor (any float dtype); ref: float64 numpy array of the same shape.
+    operand_allowance: a mean bound to use instead of 1e-3 * mean|ref| when larger."""
     g = got.detach().to("cpu", torch.float64).numpy()
     assert g.shape == ref.shape, f"{name}: shape {g.shape} vs {ref.shape}"
     assert np.isfinite(g).all(), f"{name}: non-finite values"
@@ -70,13 +76,15 @@ def check_close(name, got, ref, report=None):
                 mean_ref=float(mean_ref), mean_rel=float(mean_abs / max(mean_ref, 1e-30)),
                 mean_rel_vs_bf16_ref=float(np.abs(g - O.bf16_rne(ref)).mean() / max(mean_ref, 1e-30)),
                 page_abs_mean_ok=bool(mean_abs <= 1e-3))
+    if operand_allowance:
+        line["operand_allowance"] = float(operand_allowance)
     say("  " + json.dumps(line))
     if report is not None:
         report.append(line)
     assert rel_max <= REL_MAX_TOL, f"{name}: max|diff|/max|ref| = {rel_max:.3e}"
-    assert mean_abs <= MEAN_REL_TOL * mean_ref + rounding, (
-        f"{name}: mean|diff| = {mean_abs:.3e} > 1e-3*mean|ref| ({mean_ref:.3e}) + bf16 rounding "
-        f"{rounding:.3e}")
+    assert mean_abs <= max(MEAN_REL_TOL * mean_ref, operand_allowance) + rounding, (
+        f"{name}: mean|diff| = {mean_abs:.3e} > max(1e-3*mean|ref| ({mean_ref:.3e}), "
+        f"{operand_allowance:.3e}) + bf16 rounding {rounding:.3e}")
 
 
 # -----------------------------------------------------------------------------------------------
@@ -131,10 +139,27 @@ def test_order_bit_exact(B, H, nb, bw):
 # forward
 # -----------------------------------------------------------------------------------------------
 
+def _o_operand_allowance(c, qblocks):
+    """2^-8 * the mean over the q blocks' o elements of sqrt(sum_j P_ij^2 v_jd^2), P and v from
+    the oracle (twice the rms bound of the error that bf16 rounding of P puts into o = P V)."""
+    Q, K, Vv = O.f64(c.q), O.f64(c.k), O.f64(c.v)
+    total, count = 0.0, 0
+    for b, h, qb in qblocks:
+        keys = O.kept_keys(c.q2k_idx, c.q2k_num, c.vbs, b, h, qb)
+        count += 64 * Q.shape[-1]
+        if keys.size == 0:
+            continue
+        _, _, p = O.qblock_forward(Q[b, h, qb * 64:(qb + 1) * 64], K[b, h, keys], Vv[b, h, keys],
+                                   c.sm_scale)
+        total += np.sqrt((p * p) @ (Vv[b, h, keys] ** 2)).sum()
+    return 2.0 ** -8 * total / count
+
+
 def _fwd_compare(c, d, o, lse, qblocks=None):
     ro, rl = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale, qblocks=qblocks)
     if qblocks is None:
-        check_close("o", o, ro)
+        allq = [(b, h, qb) for b in range(c.B) for h in range(c.H) for qb in range(c.nb)]
+        check_close("o", o, ro, operand_allowance=_o_operand_allowance(c, allq))
         got_l = lse.cpu().double().numpy()
         fin = np.isfinite(rl)
         assert np.array_equal(np.isfinite(got_l), fin)
@@ -143,7 +168,8 @@ def _fwd_compare(c, d, o, lse, qblocks=None):
     else:
         for b, h, qb in qblocks:
             rows = slice(qb * 64, (qb + 1) * 64)
-            check_close(f"o[{b},{h},{qb}]", o[b, h, rows], ro[b, h, rows])
+            check_close(f"o[{b},{h},{qb}]", o[b, h, rows], ro[b, h, rows],
+                        operand_allowance=_o_operand_allowance(c, [(b, h, qb)]))
             assert np.abs(lse[b, h, rows].cpu().double().numpy() - rl[b, h, rows]).max() <= LSE_ABS_TOL
 
 
@@ -354,3 +380,40 @@ def test_config4_65k_order_stability_sampled():
     dq, dk, dv = grads
     _sampled_checks(c, o, lse, grads, qblocks=[(0, 1, 7), (0, 6, 1023)],
                     kvblocks=[(0, 2, 0), (0, 7, 777)])
+
+
+def _head(c, h):
+    """Head h of a case as a one-head case (the oracle then converts one head, not eight)."""
+    import dataclasses
+    sl = slice(h, h + 1)
+    return dataclasses.replace(c, H=1, q=c.q[:, sl], k=c.k[:, sl], v=c.v[:, sl], do=c.do[:, sl],
+                               q2k_idx=c.q2k_idx[:, sl], q2k_num=c.q2k_num[:, sl])
+
+
+def test_config5_524k_end_to_end_sampled():
+    """524288 tokens, 8192 kv blocks, top-k 2048, inputs x0.5, last kv block 40 valid tokens.
+    o, lse and dq on sampled q blocks against the oracle (each one q block of one head); dk and dv
+    through the invariants and the exact zeros of the ragged block (one kv block's dk needs the
+    softmax of the ~2048 q blocks that select it, out of the oracle's reach here)."""
+    c = workloads.config(5)
+    say("[end-to-end] config 5 (B=1 H=8 S=524288, 25%, ragged last block)")
+    d, o, lse, _, plan, grads = _end_to_end(c)
+    dq, dk, dv = grads
+    _invariants(c, grads)
+    last = (c.nb - 1) * 64
+    assert torch.all(dk[:, :, last + 40:] == 0) and torch.all(dv[:, :, last + 40:] == 0)
+    assert torch.any(dk[:, :, last:last + 40] != 0)
+    for h, qb in ((0, 0), (4, 4096), (7, c.nb - 1)):
+        ch = _head(c, h)
+        sub = (o[:, h:h + 1], lse[:, h:h + 1], (dq[:, h:h + 1], dk[:, h:h + 1], dv[:, h:h + 1]))
+        say(f"  sampled q block (h={h}, qb={qb})")
+        _sampled_checks(ch, sub[0], sub[1], sub[2], qblocks=[(0, 0, qb)], kvblocks=[])
+    # the reported time of the whole backward chain at this size
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    plan.run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    say(f"  backward chain {ms:.1f} ms, {c.pairs * 5 * 2 * 64 * 64 * 128 / ms / 1e9:.1f} TFLOPS "
+        f"on selected blocks")

@@ -12,6 +12,9 @@ unselected) and its 65536-token stability case (1024 kv blocks, 12.5 % density, 
 Draw order (fixed, so a case is reproducible from its seed): q, k, v, dO as fp32 ``randn`` on a
 CPU ``torch.Generator`` rounded to bf16 (round-to-nearest-even), then per (b, h, q-block) the
 top-k size (only where it varies), then the selection ``randperm(pool)[:topk]`` sorted ascending.
+Activation tensors above 2**27 elements (the 524k-token workload) are drawn in 2**24-element
+chunks, chunk c of tensor t (q, k, v, dO = 0..3) from its own generator seeded
+seed * 1000003 + t * 65536 + c, so they can be drawn in parallel.
 """
 from __future__ import annotations
 
@@ -62,11 +65,41 @@ CONFIG_TEXT = {
 }
 
 
-def _randn_bf16(shape, gen: torch.Generator, scale: float = 1.0) -> torch.Tensor:
-    x = torch.randn(shape, generator=gen, dtype=torch.float32)
-    if scale != 1.0:
-        x.mul_(scale)  # a power of two: exact, so rounding before or after is the same
-    return x.to(torch.bfloat16)
+# Tensors with more elements than this are drawn in fixed chunks, each from its own generator,
+# on a thread pool (the single-stream draw runs at ~5e7 samples/s, a minute for 524k tokens).
+CHUNKED_ABOVE = 1 << 27
+CHUNK = 1 << 24
+
+
+def _randn_bf16(shape, gen: torch.Generator, scale: float = 1.0, *, seed: int = 0,
+                tensor: int = 0) -> torch.Tensor:
+    numel = 1
+    for d in shape:
+        numel *= d
+    if numel <= CHUNKED_ABOVE:
+        x = torch.randn(shape, generator=gen, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)  # a power of two: exact, so rounding before or after is the same
+        return x.to(torch.bfloat16)
+    # chunk c of tensor t comes from generator seed * 1000003 + t * 65536 + c: the result does
+    # not depend on the number of threads
+    from concurrent.futures import ThreadPoolExecutor
+    out = torch.empty(numel, dtype=torch.bfloat16)
+
+    def draw(c):
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed * 1000003 + tensor * 65536 + c)
+        lo = c * CHUNK
+        n = min(CHUNK, numel - lo)
+        x = torch.randn(n, generator=g, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        out[lo:lo + n] = x.to(torch.bfloat16)
+
+    chunks = (numel + CHUNK - 1) // CHUNK
+    with ThreadPoolExecutor(max_workers=min(16, torch.get_num_threads(), chunks)) as ex:
+        list(ex.map(draw, range(chunks)))
+    return out.view(shape)
 
 
 def _select(gen: torch.Generator, rows: int, pool: torch.Tensor, topk: Sequence[int] | int,
@@ -95,10 +128,10 @@ def make_case(B: int, H: int, nb: int, topk, *, seed: int, kv_pool: Optional[Seq
     gen.manual_seed(seed)
     S = nb * BLOCK
     shape = (B, H, S, HEAD_DIM)
-    q = _randn_bf16(shape, gen, scale)
-    k = _randn_bf16(shape, gen, scale)
-    v = _randn_bf16(shape, gen, scale)
-    do = _randn_bf16(shape, gen, scale)
+    q = _randn_bf16(shape, gen, scale, seed=seed, tensor=0)
+    k = _randn_bf16(shape, gen, scale, seed=seed, tensor=1)
+    v = _randn_bf16(shape, gen, scale, seed=seed, tensor=2)
+    do = _randn_bf16(shape, gen, scale, seed=seed, tensor=3)
     pool = torch.arange(nb) if kv_pool is None else torch.as_tensor(list(kv_pool))
     rows = B * H * nb
     if topk is None:
