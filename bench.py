@@ -51,7 +51,8 @@ WORKLOAD_TEXT = {
 
 
 PROFILE = {3: "profiles/backward_S32768_H8_topk128of512.md"}
-KERNEL_SOURCES = ("bwd_dkdv.hip", "vsa_device.h", "vsa_kernels.h")
+# the kernel and its launch (grid, work order) from include/vsa.h and vsa_api.hip
+KERNEL_SOURCES = ("bwd_dkdv.hip", "vsa_device.h", "vsa_kernels.h", "vsa_api.hip", "../../../include/vsa.h")
 
 
 def counter_traffic(workload, kernel="bwd_dkdv_kernel"):
@@ -63,7 +64,8 @@ def counter_traffic(workload, kernel="bwd_dkdv_kernel"):
         return None
     h = hashlib.sha256()
     for n in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_attention_attn_amd", "csrc", n), "rb") as f:
+        with open(os.path.normpath(os.path.join(ROOT, "block_sparse_attention_attn_amd", "csrc", n)),
+                  "rb") as f:
             h.update(f.read())
     section, traffic, sha = None, None, None
     for line in open(path):

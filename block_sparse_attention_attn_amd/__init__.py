@@ -25,14 +25,15 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "library_path", "is_built", "is_supported",
+    "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "ORDER_BIN_WIDTH", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
 ]
 
 BLOCK = 64
 HEAD_DIM = 128
-ORDER_MIN_KV_BLOCKS = 1024
+ORDER_MIN_KV_BLOCKS = 64   # VSA_ORDER_MIN_KV_BLOCKS
+ORDER_BIN_WIDTH = 4        # VSA_ORDER_BIN_WIDTH
 ORDER_MAX_KV_BLOCKS = 16384
 _LOG2E = 1.4426950408889634
 
@@ -237,7 +238,7 @@ def bwd_workspace_offset(batch: int, heads: int, seqlen: int, region: int) -> in
     return int(lib().vsa_bwd_workspace_offset(batch, heads, seqlen, region))
 
 
-def bwd_order(k2q_num: torch.Tensor, bin_width: int = 8,
+def bwd_order(k2q_num: torch.Tensor, bin_width: int = ORDER_BIN_WIDTH,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Length-binned work order ``[B*H*nb]`` int32 of item ids (b*H + h)*nb + kv."""
     num = _idx(k2q_num, "k2q_num")

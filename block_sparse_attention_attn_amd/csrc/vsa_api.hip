@@ -4,11 +4,13 @@
 //
 // The backward chain follows the FastVideo backward launch header (its launch function:
 // support check -> preprocess -> order when nb >= 1024 and no order was given -> main ->
-// postprocess, every launch on the caller's stream and checked right after), with three
+// postprocess, every launch on the caller's stream and checked right after), with four
 // differences made for gfx950: no TMA descriptors or transposed Q/dO copies (the kernels read
 // transposed operands from LDS with ds_read_b64_tr_b16); the main step is two atomic-free
 // kernels (kv-major dK/dV, q-major dQ) because fp32 atomics cannot carry the per-pair dQ
-// partials at MFMA speed on this chip; and the dQ postprocess is the q-major kernel's epilogue.
+// partials at MFMA speed on this chip; the dQ postprocess is the q-major kernel's epilogue; and
+// the length-binned order starts at VSA_ORDER_MIN_KV_BLOCKS with bin VSA_ORDER_BIN_WIDTH (it
+// keeps the items running together on one XCD in step, for L2 reuse of Q/dO).
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -284,11 +286,12 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       }
       if (uses_device_order(a)) {
         if (!a->order) {
-          vsa::launch_bwd_order(a->k2q_num, BH, nb, 8, ws.kv_order, s);
+          vsa::launch_bwd_order(a->k2q_num, BH, nb, VSA_ORDER_BIN_WIDTH, ws.kv_order, s);
           const int r = launch_status("vsa_bwd kv order");
           if (r != VSA_OK) return r;
         }
-        vsa::launch_bwd_order(derive ? ws.q2k_num : a->q2k_num, BH, nb, 8, ws.q_order, s);
+        vsa::launch_bwd_order(derive ? ws.q2k_num : a->q2k_num, BH, nb, VSA_ORDER_BIN_WIDTH,
+                              ws.q_order, s);
         return launch_status("vsa_bwd q order");
       }
       return VSA_OK;

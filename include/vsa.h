@@ -101,8 +101,13 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  * Work order: `order` (optional, [B*H*num_kv_blocks] int32 item ids (b*H + h)*nb + kv, a
  * permutation) fixes the launch order of the kv-major items. NULL lets the library choose: the
  * identity below VSA_ORDER_MIN_KV_BLOCKS kv blocks per sequence, else the length-binned order
- * (vsa_bwd_order, bin width 8) computed into the workspace; the q-major items get the same
- * treatment from the q2k counts.
+ * (vsa_bwd_order, bin width VSA_ORDER_BIN_WIDTH) computed into the workspace; the q-major items
+ * get the same treatment from the q2k counts. The pages sort from 1024 kv blocks with bin
+ * parameter 8 (the launch header's order kernel). Here the order also keeps the items that run
+ * together on one XCD at equal list lengths, so their ascending walks over Q/dO stay in step and
+ * share that XCD's L2; on MI355X that pays from a few hundred kv blocks on, and a narrower bin
+ * keeps the walks closer. The order never changes the results, which are bitwise identical for
+ * any order.
  *
  * Workspace (device, vsa_bwd_workspace_bytes() bytes, contents on entry irrelevant), regions in
  * this order, each at a 256-byte boundary (vsa_bwd_workspace_offset() gives the offsets):
@@ -113,7 +118,8 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *   VSA_WS_Q2K_NUM   int32 [B, H, nb]
  *   VSA_WS_Q2K_IDX   int32 [B, H, nb, nb]
  *   VSA_WS_BITMAP    the inversion's bitmap */
-#define VSA_ORDER_MIN_KV_BLOCKS 1024
+#define VSA_ORDER_MIN_KV_BLOCKS 64
+#define VSA_ORDER_BIN_WIDTH 4
 #define VSA_ORDER_MAX_KV_BLOCKS 16384
 
 typedef enum {

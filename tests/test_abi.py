@@ -33,6 +33,14 @@ def test_library_exports_every_declared_function():
     assert sorted(V._SIGNATURES) == names
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    for name, value in (("VSA_ORDER_MIN_KV_BLOCKS", V.ORDER_MIN_KV_BLOCKS),
+                        ("VSA_ORDER_BIN_WIDTH", V.ORDER_BIN_WIDTH)):
+        m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
+        assert m and int(m.group(1)) == value, name
+
+
 def test_status_strings():
     L = V.lib()
     for st, word in ((0, b"OK"), (1, b"EINVAL"), (2, b"EUNSUPPORTED"), (3, b"ELAUNCH")):

@@ -352,7 +352,11 @@ def _invariants(c, grads):
 def test_config3_32k_end_to_end_sampled():
     c = workloads.config(3)
     say("[end-to-end] config 3 (B=1 H=8 S=32768, 25%)")
-    d, o, lse, _, plan, grads = _end_to_end(c)
+    d, o, lse, (k2q_idx, k2q_num), plan, grads = _end_to_end(c)
+    # 512 kv blocks: the library computed the length-binned kv-major order into the workspace
+    n = c.B * c.H * c.nb
+    assert np.array_equal(plan.region(V.WS_KV_ORDER, n).cpu().numpy(),
+                          O.work_order(k2q_num.cpu(), V.ORDER_BIN_WIDTH))
     _invariants(c, grads)
     _sampled_checks(c, o, lse, grads, qblocks=[(0, 0, 0), (0, 3, 200), (0, 7, 511)],
                     kvblocks=[(0, 0, 1), (0, 5, 300), (0, 7, 511)])
@@ -368,8 +372,9 @@ def test_config4_65k_order_stability_sampled():
     ridx, rnum = O.invert_indices(k2q_idx.cpu(), k2q_num.cpu(), c.nb)
     assert np.array_equal(plan.region(V.WS_Q2K_NUM, n).cpu().numpy().reshape(rnum.shape), rnum)
     assert np.array_equal(plan.region(V.WS_Q2K_IDX, n * c.nb).cpu().numpy().reshape(ridx.shape), ridx)
-    assert np.array_equal(plan.region(V.WS_KV_ORDER, n).cpu().numpy(), O.work_order(k2q_num.cpu(), 8))
-    assert np.array_equal(plan.region(V.WS_Q_ORDER, n).cpu().numpy(), O.work_order(rnum, 8))
+    bw = V.ORDER_BIN_WIDTH
+    assert np.array_equal(plan.region(V.WS_KV_ORDER, n).cpu().numpy(), O.work_order(k2q_num.cpu(), bw))
+    assert np.array_equal(plan.region(V.WS_Q_ORDER, n).cpu().numpy(), O.work_order(rnum, bw))
     _invariants(c, grads)
     # run-to-run: every output bitwise equal (no atomics anywhere)
     grads = tuple(t.clone() for t in grads)
