@@ -52,7 +52,7 @@ WORKLOAD_TEXT = {
 
 PROFILE = {3: "profiles/backward_S32768_H8_topk128of512.md"}
 # the kernel and its launch (grid, work order) from include/vsa.h and vsa_api.hip
-KERNEL_SOURCES = ("bwd_dkdv.hip", "vsa_device.h", "vsa_kernels.h", "vsa_api.hip", "../../../include/vsa.h")
+KERNEL_SOURCES = ("bwd_dkdv.hip", "vsa_device.h", "vsa_kernels.h", "vsa_api.hip", "../../include/vsa.h")
 
 
 def counter_traffic(workload, kernel="bwd_dkdv_kernel"):
