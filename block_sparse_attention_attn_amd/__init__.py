@@ -63,7 +63,7 @@ class _BwdArgs(ctypes.Structure):
 
 
 # workspace regions of the backward (vsa_bwd_ws_region)
-WS_DELTA, WS_KV_ORDER, WS_Q_ORDER, WS_Q2K_NUM, WS_Q2K_IDX, WS_BITMAP, WS_END = range(7)
+WS_LSE_DELTA, WS_KV_ORDER, WS_Q_ORDER, WS_Q2K_NUM, WS_Q2K_IDX, WS_BITMAP, WS_END = range(7)
 
 
 # name -> (restype, argtypes); exactly the symbols include/vsa.h declares
@@ -234,7 +234,7 @@ def bwd_workspace_bytes(batch: int, heads: int, seqlen: int, derive_q2k: bool = 
 
 
 def bwd_workspace_offset(batch: int, heads: int, seqlen: int, region: int) -> int:
-    """Byte offset of a backward workspace region (WS_DELTA, WS_KV_ORDER, ...)."""
+    """Byte offset of a backward workspace region (WS_LSE_DELTA, WS_KV_ORDER, ...)."""
     return int(lib().vsa_bwd_workspace_offset(batch, heads, seqlen, region))
 
 
@@ -328,17 +328,30 @@ class BwdPlan:
         _check(lib().vsa_bwd_stage(self._ref, i, _stream(self.device)), "vsa_bwd_stage")
 
     def region(self, r: int, count: int, dtype=torch.int32) -> torch.Tensor:
-        """``count`` elements of workspace region ``r`` (WS_DELTA, WS_KV_ORDER, ...)."""
+        """``count`` elements of workspace region ``r`` (WS_LSE_DELTA, WS_KV_ORDER, ...)."""
         a = self.args
         off = bwd_workspace_offset(a.batch, a.heads, a.seqlen, r)
         nbytes = count * torch.empty(0, dtype=dtype).element_size()
         return self.workspace[off:off + nbytes].view(dtype)
 
-    def delta(self) -> torch.Tensor:
-        """The workspace's Delta region as fp32 [B, H, S] (valid after PREPROCESS)."""
+    def lse_delta(self) -> torch.Tensor:
+        """The workspace's per-q-block statistics records as fp32 [B, H, nb, 2, 64] (valid after
+        PREPROCESS): -lse / scale_log2 of the block's 64 rows, then -Delta of its 64 rows, where
+        scale_log2 = fp32(sm_scale * log2 e)."""
         a = self.args
-        n = a.batch * a.heads * a.seqlen
-        return self.region(WS_DELTA, n, torch.float32).view(a.batch, a.heads, a.seqlen)
+        nb = a.seqlen // BLOCK
+        n = a.batch * a.heads * a.seqlen * 2
+        return self.region(WS_LSE_DELTA, n, torch.float32).view(a.batch, a.heads, nb, 2, BLOCK)
+
+    def scale_log2(self) -> float:
+        """fp32(sm_scale * log2 e), the factor the records divide lse by."""
+        return float(torch.tensor(self.args.sm_scale, dtype=torch.float32)
+                     * torch.tensor(1.4426950408889634, dtype=torch.float32))
+
+    def delta(self) -> torch.Tensor:
+        """Delta as fp32 [B, H, S], read out of the records (valid after PREPROCESS)."""
+        a = self.args
+        return -self.lse_delta()[:, :, :, 1, :].reshape(a.batch, a.heads, a.seqlen)
 
 
 def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -1,7 +1,10 @@
 // bwd_aux.hip -- the streaming kernels around the backward's main kernel (gfx950):
 //   preprocess  Delta = rowsum(bf16(o) * dO) in fp32, and the exact-zero dK/dV rows of kv blocks
 //               that no q block selects (FastVideo sm_100a backward commit message, the
-//               preprocess sentence; launch header, the delta field of the argument struct);
+//               preprocess sentence; launch header, the delta field of the argument struct).
+//               Delta is stored in a 512-byte record per q block: -lse/scale_log2 of its 64
+//               rows, then -Delta of its 64 rows, the initial accumulator values of the
+//               kv-major kernel's S and dP MFMAs;
 //   order       the per-(b, h) length-binned permutation of work items that the launch header
 //               computes on device from 1024 kv blocks on (its order-kernel launch and the
 //               ORDER_MIN_KV_BLOCKS comment); used for the kv-major and the q-major kernel.
@@ -35,7 +38,12 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdPreParams p) {
     acc += __shfl_xor(acc, 4, 64);
     acc += __shfl_xor(acc, 2, 64);
     acc += __shfl_xor(acc, 1, 64);
-    if (c == 0) p.delta[row] = acc;
+    if (c == 0) {
+      float* rec = p.lse_delta + ((size_t)bh * p.nb + blk) * LD_RECORD_FLOATS;
+      const int r = pass * 16 + rr;
+      rec[r] = -(p.lse[row] / p.scale_log2);  // IEEE division: a fixed, testable rounding
+      rec[BLOCK + r] = -acc;
+    }
     if (empty) {
       *(bf16x8*)(p.dk + row * HEAD_DIM + c * 8) = bf16x8{};
       *(bf16x8*)(p.dv + row * HEAD_DIM + c * 8) = bf16x8{};

@@ -20,13 +20,19 @@
 //     of every q block and kv rows 32*(w>>1).. of the item, so each 64x64x128 GEMM is eight
 //     v_mfma_f32_32x32x16_bf16 per wave;
 //   * K_j and V_j fragments (the B operands of S and dP) live in registers for the whole item,
-//     with padded kv rows zeroed there;
-//   * Q_i, dO_i, lse_i, Delta_i stream through a four-stage ring of XOR-swizzled LDS tiles filled
-//     by global_load_lds_dwordx4 three q blocks ahead; one barrier per q block;
-//   * software pipeline across q blocks: step t runs the S/dP MFMAs of q block t+1 interleaved
-//     with the exp2/convert work of q block t, then the dV/dK MFMAs of q block t; every MFMA's LDS
-//     operands are requested one phase before it issues, so LDS latency and bandwidth overlap the
-//     matrix cores;
+//     with padded kv rows zeroed there. They arrive by DMA through LDS like everything else, so
+//     every vector memory operation of the kernel is an LDS DMA whose completion is counted by
+//     hand;
+//   * Q_i, dO_i and the q block's 512-byte statistics record (-lse_i / scale_log2 and -Delta_i,
+//     written by the preprocess) stream through a four-stage ring of XOR-swizzled LDS tiles,
+//     fetched by global_load_lds_dwordx4 two steps before their first use; one barrier per q
+//     block, between the two phases of a step;
+//   * the S and dP accumulators start from the record's values, so the MFMAs deliver
+//     S - lse/scale_log2 and dP - Delta directly: P = exp2(scale_log2 * acc), dS = P * acc';
+//   * software pipeline across q blocks: phase B of step t runs the S/dP MFMAs of q block t+1
+//     interleaved with the exp2/convert work of q block t and its transposed reads; phase C runs
+//     the dV/dK MFMAs of q block t interleaved with the row and record reads of q block t+2, so
+//     every MFMA's LDS operands were requested a phase before it issues;
 //   * P and dS never leave registers: the D layout of S/dP feeds the A operand of dV/dK directly
 //     (the contraction index is permuted to match); the partner operands dO_i^T and Q_i^T come
 //     from ds_read_b64_tr_b16 transposed reads;
@@ -41,9 +47,10 @@ namespace vsa {
 
 namespace {
 
-constexpr int STAGES = 4;           // ring depth: stage t%4 holds q block t
-constexpr int STAGE_BYTES = 16384;  // one [64][128] bf16 tile
-constexpr int LD_BYTES = 512;       // lse[64] then Delta[64], fp32
+constexpr int STAGES = 4;                        // ring depth: stage t%4 holds q block t
+constexpr int STAGE_BYTES = 16384;               // one [64][128] bf16 tile
+constexpr int LD_BYTES = LD_RECORD_FLOATS * 4;   // one q block's statistics record
+constexpr int DMA_PER_BLOCK = 9;                 // vector memory operations per wave per q block
 
 __device__ __forceinline__ void barrier_lds() {
   // Wait for this wave's LDS traffic, then meet the other waves. Vector memory traffic (the next
@@ -51,22 +58,10 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// DMA of q block qb's Q, dO tiles and lse, Delta rows into one ring stage. Every wave issues
-// nine DMAs (four 1-KiB slices of each tile, one 128-byte quarter of lse/Delta), so the
-// outstanding-DMA count is the same in every wave. `off` holds the wave's per-lane tile offsets.
-__device__ __forceinline__ void prefetch(const bf16* __restrict__ qh, const bf16* __restrict__ doh,
-                                         const float* __restrict__ lseh,
-                                         const float* __restrict__ deltah, int qb,
-                                         VSA_LDS char* qs, VSA_LDS char* ds, VSA_LDS char* ls,
-                                         const uint32_t* off, int lane, int w) {
-  const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
-  tile_load_async_off<4>(qh + tile, qs, off, w);
-  tile_load_async_off<4>(doh + tile, ds, off, w);
-  if (lane < 8) {
-    // wave 0, 1: lse[0..31], lse[32..63]; wave 2, 3: Delta[0..31], Delta[32..63]
-    const float* src = (w < 2 ? lseh : deltah) + qb * BLOCK + 32 * (w & 1);
-    dma16_sb(src, (uint32_t)(16 * lane), lds_addr(ls + 128 * w));
-  }
+// The same barrier, with `v` (a scalar load's result) required in its register first: the load
+// is issued just before and waited for by the barrier's own lgkmcnt(0).
+__device__ __forceinline__ void barrier_lds_with(int v) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(v) : "memory");
 }
 
 }  // namespace
@@ -100,50 +95,61 @@ bwd_dkdv_kernel(BwdParams p) {
   const size_t head = (size_t)bh * p.S * HEAD_DIM;
   const bf16* __restrict__ qh = p.q + head;
   const bf16* __restrict__ doh = p.dout + head;
-  const float* __restrict__ lseh = p.lse + (size_t)bh * p.S;
-  const float* __restrict__ deltah = p.delta + (size_t)bh * p.S;
+  const float* __restrict__ recs = p.lse_delta + (size_t)bh * p.nb * LD_RECORD_FLOATS;
   const int* __restrict__ list = p.k2q_idx + (size_t)item * p.k2q_stride;
   // q block ids outside [0, nb) violate the caller contract; clamp them so no access leaves the
   // tensors (the result is then unspecified, but nothing faults)
-  auto qblock = [&](int t) {
-    const int qb = ld_const(list, t);
-    return qb < 0 ? 0 : (qb >= p.nb ? p.nb - 1 : qb);
-  };
+  auto clampq = [&](int qb) { return qb < 0 ? 0 : (qb >= p.nb ? p.nb - 1 : qb); };
+  auto entry = [&](int t) { return ld_const(list, t < n ? t : n - 1); };  // raw, in the list
+
   VSA_LDS char* const qr = (VSA_LDS char*)q_ring;
   VSA_LDS char* const dr = (VSA_LDS char*)do_ring;
   VSA_LDS char* const lr = (VSA_LDS char*)ld_ring;
   uint32_t toff[4];
   tile_offsets<4>(toff, lane, w);
-  auto issue = [&](int t, int st) __attribute__((always_inline)) {
-    prefetch(qh, doh, lseh, deltah, qblock(t), qr + st * STAGE_BYTES, dr + st * STAGE_BYTES,
-             lr + st * LD_BYTES, toff, lane, w);
+  const uint32_t roff = 16 * lane + 128 * w;  // this wave's quarter of a record (lanes 0..7)
+  const uint32_t q_lds = lds_addr(qr) + 1024 * w;
+  const uint32_t do_lds = lds_addr(dr) + 1024 * w;
+  const uint32_t ld_lds = lds_addr(lr) + 128 * w;
+  auto issue = [&](int qb, int st) __attribute__((always_inline)) {
+    const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
+    dma_tile_pair_rec(qh + tile, doh + tile, recs + (size_t)qb * LD_RECORD_FLOATS, toff, roff,
+                      q_lds + st * STAGE_BYTES, do_lds + st * STAGE_BYTES, ld_lds + st * LD_BYTES);
   };
 
-  // q blocks 0, 1, 2 into stages 0, 1, 2
-  issue(0, 0);
-  if (n > 1) issue(1, 1);
-  if (n > 2) issue(2, 2);
+  // ---- prologue ----
+  // K_j, V_j into stage 3 of the rings; q blocks 0, 1, 2 into stages 0, 1, 2.
+  {
+    const size_t tile = (size_t)j * BLOCK * HEAD_DIM;
+    dma_tile_pair(p.k + head + tile, p.v + head + tile, toff, q_lds + 3 * STAGE_BYTES,
+                  do_lds + 3 * STAGE_BYTES);
+  }
+  {
+    const int e0 = entry(0), e1 = entry(1), e2 = entry(2);
+    issue(clampq(e0), 0);
+    issue(clampq(e1), 1);  // (past the end of the list: repeats of the last q block)
+    issue(clampq(e2), 2);
+  }
+  const int e3 = entry(3);
+  // K/V and q blocks 0, 1 landed (own DMAs); q block 2's may still be in flight
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK));
+  barrier_lds_with(e3);  // ... everyone's
 
   // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
   const int kv_l = 32 * wk + l32;
   const bool kv_valid = kv_l < vb;
   bf16x8 kf[8], vf[8];
-  {
-    const bf16* kj = p.k + head + (size_t)j * BLOCK * HEAD_DIM;
-    const bf16* vj = p.v + head + (size_t)j * BLOCK * HEAD_DIM;
-    const bf16x8* kr = (const bf16x8*)(kj + (size_t)kv_l * HEAD_DIM);
-    const bf16x8* vr = (const bf16x8*)(vj + (size_t)kv_l * HEAD_DIM);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int b = 3 * STAGE_BYTES + tile_byte(kv_l, 2 * s + g);
+    kf[s] = *(const VSA_LDS bf16x8*)(qr + b);
+    vf[s] = *(const VSA_LDS bf16x8*)(dr + b);
+  }
+  if (!kv_valid) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      kf[s] = kr[2 * s + g];
-      vf[s] = vr[2 * s + g];
-    }
-    if (!kv_valid) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        kf[s] = bf16x8{};
-        vf[s] = bf16x8{};
-      }
+      kf[s] = bf16x8{};
+      vf[s] = bf16x8{};
     }
   }
 
@@ -158,7 +164,8 @@ bwd_dkdv_kernel(BwdParams p) {
 
   // A operands of S = Q K^T and dP = dO V^T for the q block in stage st: q rows 32*wq + l32,
   // d = 16*s + 8*g + 0..7
-  auto load_rows = [&](int st, bf16x8* qa, bf16x8* da) __attribute__((always_inline)) {
+  bf16x8 qa[8], da[8];
+  auto load_rows = [&](int st) __attribute__((always_inline)) {
     VSA_LDS char* qt = qr + st * STAGE_BYTES;
     VSA_LDS char* dt = dr + st * STAGE_BYTES;
 #pragma unroll
@@ -167,49 +174,53 @@ bwd_dkdv_kernel(BwdParams p) {
       da[s] = *(const VSA_LDS bf16x8*)(dt + tile_byte(qrow, 2 * s + g));
     }
   };
-
-  // Prologue: S/dP of q block 0, and the row operands of q block 1, in registers.
-  f32x16 s0, p0, s1, p1;
-  bf16x8 qa0[8], da0[8], qa1[8], da1[8];
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stages 0..2 landed (own DMAs)
-  barrier_lds();
-  load_rows(0, qa0, da0);
-  s0 = f32x16{};
-  p0 = f32x16{};
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    s0 = mfma32(qa0[s], kf[s], s0);
-    p0 = mfma32(da0[s], vf[s], p0);
-  }
-  load_rows(1, qa1, da1);  // stale but in bounds when n == 1
-
-  // Step t (q block t in stage st, t+1 in st1, t+2 in st2; q block t+3 is fetched into st3):
-  //   on entry S/dP of t are in (sc, pc) and the row operands of t+1 in (qa, da);
-  //   phase B: S/dP MFMAs of t+1 from (qa, da), interleaved with P, dS of t (lse/Delta reads
-  //            first) and the transposed dO^T, Q^T reads of t;
-  //   phase C: dV/dK MFMAs of t, interleaved with the row-operand reads of t+2 into (qn, dn).
-  // Every MFMA's LDS operands were requested a phase earlier. The last steps compute throwaway
-  // S/dP and rows from stale (in-bounds, quiescent) stages, which keeps the body free of
-  // branches. The loop is unrolled by four so every stage offset is a compile-time constant.
-  auto step = [&](int t, int st, int st2, int st3, f32x16& sc, f32x16& pc, f32x16& sn,
-                  f32x16& pn, bf16x8* qa, bf16x8* da, bf16x8* qn, bf16x8* dn)
-                  __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stage t+2 landed (own DMAs)
-    barrier_lds();  // ... everyone's; and everyone is done with stage st3 (q block t-1)
-    if (t + 3 < n) issue(t + 3, st3);
-    VSA_LDS char* qt = qr + st * STAGE_BYTES;
-    VSA_LDS char* dt = dr + st * STAGE_BYTES;
-    VSA_LDS float* ld = (VSA_LDS float*)(lr + st * LD_BYTES);
-
-    // ---- phase B ----
-    // element i of S is q row 32*wq + 8*(i/4) + 4*g + i%4
-    f32x4 lse4[4], del4[4];
+  // Initial accumulators of the q block in stage st from its record: element i of S / dP is
+  // q row 32*wq + 8*(i/4) + 4*g + i%4.
+  auto load_init = [&](int st, f32x16& sa_, f32x16& pa_) __attribute__((always_inline)) {
+    const VSA_LDS float* ld = (const VSA_LDS float*)(lr + st * LD_BYTES);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int q = 32 * wq + 8 * c + 4 * g;
-      lse4[c] = *(const VSA_LDS f32x4*)(ld + q);
-      del4[c] = *(const VSA_LDS f32x4*)(ld + 64 + q);
+      const f32x4 a = *(const VSA_LDS f32x4*)(ld + q);
+      const f32x4 b = *(const VSA_LDS f32x4*)(ld + BLOCK + q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa_[4 * c + e] = a[e];
+        pa_[4 * c + e] = b[e];
+      }
     }
+  };
+
+  f32x16 s0, p0, s1, p1;
+  load_rows(0);
+  load_init(0, s0, p0);
+  barrier_lds();  // everyone has read K/V out of stage 3
+  issue(clampq(e3), 3);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    s0 = mfma32(qa[s], kf[s], s0);
+    p0 = mfma32(da[s], vf[s], p0);
+  }
+  load_rows(1);  // a repeat of q block 0 when n == 1
+  load_init(1, s1, p1);
+
+  // Step t (q block t in stage st = t % 4): on entry (sc, pc) hold S - lse/scale_log2 and
+  // dP - Delta of q block t, (sn, pn) the initial values of q block t+1 and (qa, da) its rows.
+  //   phase B: S/dP MFMAs of t+1, interleaved with P, dS of t and the transposed dO^T, Q^T reads
+  //            of t;
+  //   mid:     q block t+2 has landed (own DMAs, then the barrier: everyone's) and everyone is
+  //            done with stage st, which then receives q block t+4;
+  //   phase C: dV/dK MFMAs of t, interleaved with the row and record reads of t+2 into
+  //            (qa, da) and (sc, pc).
+  // The last steps compute throwaway S/dP from repeated q blocks, which keeps the body free of
+  // branches. The loop is unrolled by four so stage offsets are constants.
+  auto step = [&](int t, int st, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn)
+                  __attribute__((always_inline)) {
+    const int st2 = (st + 2) & 3;
+    VSA_LDS char* qt = qr + st * STAGE_BYTES;
+    VSA_LDS char* dt = dr + st * STAGE_BYTES;
+
+    // ---- phase B ----
     // transposed B operands of dV/dK for q block t: k slot jj of step s2 is q row
     // 32*wq + 16*s2 + 8*(jj/4) + 4*g + jj%4, matching the D layout of S
     bf16x8 db[2][4], qbt[2][4];
@@ -225,8 +236,6 @@ bwd_dkdv_kernel(BwdParams p) {
                            lds_read_tr(qt + tile_elem_byte(q0 + 8, col)));
       }
     }
-    sn = f32x16{};
-    pn = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       sn = mfma32(qa[s], kf[s], sn);
@@ -236,13 +245,9 @@ bwd_dkdv_kernel(BwdParams p) {
     // non-finite P; it only feeds that kv row of dV/dK, which the epilogue overwrites with 0.
     float pv[16], dsv[16];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * c + e;
-        pv[i] = __builtin_amdgcn_exp2f(sc[i] * scale_log2 - lse4[c][e]);
-        dsv[i] = pv[i] * (pc[i] - del4[c][e]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sc[i] * scale_log2);
+      dsv[i] = pv[i] * pc[i];
     }
     bf16x8 pa[2], sa[2];
 #pragma unroll
@@ -252,17 +257,26 @@ bwd_dkdv_kernel(BwdParams p) {
       sa[s2] = pack8(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
                      dsv[8 * s2 + 4], dsv[8 * s2 + 5], dsv[8 * s2 + 6], dsv[8 * s2 + 7]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // lse/Delta reads
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // ---- mid ----
+    // Every step issues one q block's DMA group (past the end of the list: a repeat of the last
+    // q block, into a stage nobody reads again), so the group of t+3 is always the newest and
+    // nine outstanding operations mean q block t+2 has landed. No branch splits the step.
+    const int raw = entry(t + 4);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK));
+    barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
+    issue(clampq(raw), st);
+
     // ---- phase C ----
-    load_rows(st2, qn, dn);
+    load_rows(st2);
+    load_init(st2, sc, pc);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
@@ -272,21 +286,23 @@ bwd_dkdv_kernel(BwdParams p) {
       }
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 8; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one row read
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three row / record reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int t = 0; t < n; t += 4) {
-    step(t, 0, 2, 3, s0, p0, s1, p1, qa1, da1, qa0, da0);
-    if (t + 1 < n) step(t + 1, 1, 3, 0, s1, p1, s0, p0, qa0, da0, qa1, da1);
-    if (t + 2 < n) step(t + 2, 2, 0, 1, s0, p0, s1, p1, qa1, da1, qa0, da0);
-    if (t + 3 < n) step(t + 3, 3, 1, 2, s1, p1, s0, p0, qa0, da0, qa1, da1);
+    step(t, 0, s0, p0, s1, p1);
+    if (t + 1 < n) step(t + 1, 1, s1, p1, s0, p0);
+    if (t + 2 < n) step(t + 2, 2, s0, p0, s1, p1);
+    if (t + 3 < n) step(t + 3, 3, s1, p1, s0, p0);
   }
 
   // ---- sum the two q halves of dV/dK through LDS, scale, round, store ----
+  // the repeats issued by the last four steps are still in flight: wait, then meet
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   barrier_lds();  // every wave is past its last LDS read of the rings
   // wave wq=1 hands over its dV half, wave wq=0 its dK half (16 KiB each, lane-native order);
   // kv half 0 uses the first two q stages, kv half 1 the first two dO stages

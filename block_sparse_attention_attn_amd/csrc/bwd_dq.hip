@@ -99,7 +99,9 @@ bwd_dq_kernel(BwdParams p) {
   // a q row with no valid key has lse = -inf; +inf makes its P exactly 0 (no inf * 0)
   float lse_q = p.lse[(size_t)bh * p.S + qrow];
   lse_q = lse_q == -__builtin_inff() ? __builtin_inff() : lse_q;
-  const float delta_q = p.delta[(size_t)bh * p.S + qrow];
+  // -Delta of this q row, from the preprocess record of q block i
+  const float ndelta_q =
+      p.lse_delta[((size_t)bh * p.nb + i) * LD_RECORD_FLOATS + BLOCK + 32 * wq + l32];
   const float scale_log2 = p.scale_log2;
 
   // dQ^T tiles: element e of tile mt is d = 32*mt + 8*(e/4) + 4*g + e%4, q = 32*wq + l32
@@ -190,7 +192,7 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pe = __builtin_amdgcn_exp2f(sc[e] * scale_log2 - lse_q);
-        dsv[e] = pe * (pc[e] - delta_q);
+        dsv[e] = pe * (pc[e] + ndelta_q);
       }
       bf16x8 b[2];
 #pragma unroll

@@ -36,6 +36,9 @@ int launch_status(const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// sm_scale * log2(e) in fp32: the factor that turns q.k into the base-2 exponent of the softmax
+float scale_log2(float sm_scale) { return sm_scale * 1.4426950408889634f; }
+
 constexpr size_t kMaxElems = (size_t)1 << 40;  // guard against size_t overflow in products
 
 bool dims_ok(int batch, int heads, int seqlen, int nb) {
@@ -127,7 +130,7 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
   p.S = a->seqlen;
   p.nb = a->num_kv_blocks;
   p.q2k_stride = a->q2k_stride;
-  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  p.scale_log2 = scale_log2(a->sm_scale);
   vsa::launch_fwd(p, (hipStream_t)stream);
   return launch_status("vsa_fwd");
 }
@@ -137,12 +140,12 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
 // ------------------------------------------------------------------------------------------------
 
 size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int region) {
-  if (batch < 1 || heads < 1 || seqlen < vsa::BLOCK || region < VSA_WS_DELTA || region > VSA_WS_END)
+  if (batch < 1 || heads < 1 || seqlen < vsa::BLOCK || region < VSA_WS_LSE_DELTA || region > VSA_WS_END)
     return 0;
   const size_t bh = (size_t)batch * (size_t)heads;
   const size_t nb = (size_t)seqlen / vsa::BLOCK;
   const size_t sizes[VSA_WS_END] = {
-      align256(bh * (size_t)seqlen * sizeof(float)),                          // delta
+      align256(bh * (size_t)seqlen * 2 * sizeof(float)),                      // lse, Delta
       align256(bh * nb * sizeof(int32_t)),                                    // kv order
       align256(bh * nb * sizeof(int32_t)),                                    // q order
       align256(bh * nb * sizeof(int32_t)),                                    // q2k_num
@@ -210,7 +213,7 @@ bool uses_device_order(const vsa_bwd_args* a) {
 }
 
 struct WsView {
-  float* delta;
+  float* lse_delta;
   int32_t* kv_order;
   int32_t* q_order;
   int32_t* q2k_num;
@@ -221,7 +224,7 @@ struct WsView {
 WsView ws_view(const vsa_bwd_args* a) {
   char* ws = (char*)a->workspace;
   auto at = [&](int r) { return ws + vsa_bwd_workspace_offset(a->batch, a->heads, a->seqlen, r); };
-  return WsView{(float*)at(VSA_WS_DELTA), (int32_t*)at(VSA_WS_KV_ORDER), (int32_t*)at(VSA_WS_Q_ORDER),
+  return WsView{(float*)at(VSA_WS_LSE_DELTA), (int32_t*)at(VSA_WS_KV_ORDER), (int32_t*)at(VSA_WS_Q_ORDER),
                 (int32_t*)at(VSA_WS_Q2K_NUM), (int32_t*)at(VSA_WS_Q2K_IDX),
                 (uint32_t*)at(VSA_WS_BITMAP)};
 }
@@ -234,7 +237,7 @@ vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
   m.v = (const vsa::bf16*)a->v;
   m.dout = (const vsa::bf16*)a->dout;
   m.lse = a->lse;
-  m.delta = ws.delta;
+  m.lse_delta = ws.lse_delta;
   m.k2q_idx = a->k2q_idx;
   m.k2q_num = a->k2q_num;
   m.q2k_idx = derive ? ws.q2k_idx : a->q2k_idx;
@@ -252,7 +255,7 @@ vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
   m.total_items = a->batch * a->heads * a->num_kv_blocks;
   m.items_per_xcd = (m.total_items + 7) / 8;
   m.sm_scale = a->sm_scale;
-  m.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  m.scale_log2 = scale_log2(a->sm_scale);
   return m;
 }
 
@@ -266,12 +269,14 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       pre.o = (const vsa::bf16*)a->o;
       pre.dout = (const vsa::bf16*)a->dout;
       pre.k2q_num = a->k2q_num;
-      pre.delta = ws.delta;
+      pre.lse = a->lse;
+      pre.lse_delta = ws.lse_delta;
       pre.dk = (vsa::bf16*)a->dk;
       pre.dv = (vsa::bf16*)a->dv;
       pre.BH = BH;
       pre.S = a->seqlen;
       pre.nb = nb;
+      pre.scale_log2 = scale_log2(a->sm_scale);
       vsa::launch_bwd_pre(pre, s);
       return launch_status("vsa_bwd preprocess");
     }

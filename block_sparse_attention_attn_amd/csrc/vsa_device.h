@@ -110,13 +110,16 @@ __device__ __forceinline__ T ld_const(const T* p, size_t i) {
 // One global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes land at
 // LDS byte address lds_base + 16*l. Issued through inline assembly so the compiler does not track
 // it; callers wait with an explicit s_waitcnt vmcnt before a barrier that publishes the tile.
-// M0 is saved and restored around the DMA (the compiler does not allow it on a clobber list).
+// M0 (the LDS base the DMA reads) is saved and restored around the DMA, since the compiler does
+// not allow it on a clobber list. An LDS DMA that reads M0 must not directly follow the write of
+// M0: the s_nop is the one wait state that gfx9-family parts require in between.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -140,11 +143,115 @@ __device__ __forceinline__ void dma16_sb(const void* base_ptr, uint32_t voff, ui
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(base), "s"(lb)
       : "memory");
+}
+
+__device__ __forceinline__ uint64_t uniform_u64(const void* p) {
+  // readfirstlane returns a signed int: go through uint32_t so each half is zero-extended
+  const uint64_t b = (uint64_t)(uintptr_t)p;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// This wave's share of two [64][128] bf16 tiles in one asm block: slices w, w+4, w+8, w+12 of
+// each (w = wave), i.e. eight 1-KiB DMAs. `off` holds the per-lane global byte offsets of the
+// four slices (tile_offsets<4>); slice i lands at LDS lds_a / lds_b + 4 KiB * i, where lds_a and
+// lds_b already include this wave's first slice. Tile bases and LDS addresses are uniform.
+// Every write of M0 is followed by one wait state before the DMA that reads it; M0 is restored.
+__device__ __forceinline__ void dma_tile_pair(const void* ga, const void* gb, const uint32_t* off,
+                                              uint32_t lds_a, uint32_t lds_b) {
+  const uint64_t a = uniform_u64(ga), b = uniform_u64(gb);
+  const uint32_t la = uniform_u32(lds_a), lb = uniform_u32(lds_b);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %6\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %6\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %6\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %6\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(a), "s"(b), "s"(la), "s"(lb)
+      : "memory", "scc");
+}
+
+// dma_tile_pair plus 128 bytes of a small record: lanes 0..7 copy rec + roff (per-lane byte
+// offsets) to LDS lds_r + 16 * lane. EXEC is narrowed to those lanes inside the asm block and
+// restored, so the caller needs no divergent branch. Nine vector memory operations per wave.
+__device__ __forceinline__ void dma_tile_pair_rec(const void* ga, const void* gb, const void* rec,
+                                                  const uint32_t* off, uint32_t roff,
+                                                  uint32_t lds_a, uint32_t lds_b,
+                                                  uint32_t lds_r) {
+  const uint64_t a = uniform_u64(ga), b = uniform_u64(gb), r = uniform_u64(rec);
+  const uint32_t la = uniform_u32(lds_a), lb = uniform_u32(lds_b), lr = uniform_u32(lds_r);
+  uint32_t saved;
+  uint64_t exec_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %7\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %7\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %7\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %7\n\t"
+      "s_mov_b32 m0, %11\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %8\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %8\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %8\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %8\n\t"
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, 0xff\n\t"
+      "s_mov_b32 m0, %12\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, %9\n\t"
+      "s_mov_b64 exec, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved), "=&s"(exec_saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(roff), "s"(a), "s"(b), "s"(r),
+        "s"(la), "s"(lb), "s"(lr)
+      : "memory", "scc");
 }
 
 // Per-lane byte offsets inside a [64][128] bf16 tile for the slices part, part + NPARTS, ... that

@@ -33,19 +33,25 @@ struct FwdParams {
 void launch_fwd(const FwdParams& p, hipStream_t stream);
 
 // ---- backward preprocess: Delta, zero dK/dV rows of empty kv blocks ----
+// The main kernels read a q block's row statistics as one record of LD_RECORD_FLOATS floats per
+// (bh, q block): -lse / scale_log2 of its 64 rows, then -Delta of its 64 rows. The kv-major kernel
+// loads them straight into its S and dP accumulators as the initial values, so the MFMAs produce
+// S - lse/scale_log2 and dP - Delta with no per-element subtraction.
+constexpr int LD_RECORD_FLOATS = 2 * BLOCK;
 struct BwdPreParams {
   const bf16* o;
   const bf16* dout;
+  const float* lse;        // [BH, S]
   const int32_t* k2q_num;  // [BH, nb]
-  float* delta;            // [BH, S]
+  float* lse_delta;        // [BH * nb, LD_RECORD_FLOATS]
   bf16* dk;
   bf16* dv;
   int BH, S, nb;
+  float scale_log2;
 };
 void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream);
 
 // ---- work order: per (b, h) a length-binned permutation of its items ----
-constexpr int ORDER_MIN_KV_BLOCKS = 1024;  // below: identity order
 constexpr int ORDER_MAX_KV_BLOCKS = 16384; // LDS holds one 32-bit key per block
 void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
                       hipStream_t stream);
@@ -56,8 +62,8 @@ struct BwdParams {
   const bf16* k;
   const bf16* v;
   const bf16* dout;
-  const float* lse;
-  const float* delta;
+  const float* lse;        // [BH, S] base-2 M-form lse (the dQ kernel's)
+  const float* lse_delta;  // [BH*nb, LD_RECORD_FLOATS]: the q blocks' records (see above)
   const int32_t* k2q_idx;  // [BH*nb, k2q_stride]
   const int32_t* k2q_num;  // [BH*nb]
   const int32_t* q2k_idx;  // [BH*nb, q2k_stride]

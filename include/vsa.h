@@ -111,7 +111,8 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *
  * Workspace (device, vsa_bwd_workspace_bytes() bytes, contents on entry irrelevant), regions in
  * this order, each at a 256-byte boundary (vsa_bwd_workspace_offset() gives the offsets):
- *   VSA_WS_DELTA     fp32 Delta [B, H, S]   (left holding Delta after the call)
+ *   VSA_WS_LSE_DELTA fp32 [B, H, nb, 2, 64]: per q block, its 64 lse values (a copy of `lse`)
+ *                    then its 64 Delta values (left holding them after the call)
  *   VSA_WS_KV_ORDER  int32 [B*H*nb] kv-major work order (when the library computes it)
  *   VSA_WS_Q_ORDER   int32 [B*H*nb] q-major work order (when the library computes it)
  * and only when the q2k lists are derived (derive_q2k != 0):
@@ -123,7 +124,7 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
 #define VSA_ORDER_MAX_KV_BLOCKS 16384
 
 typedef enum {
-  VSA_WS_DELTA = 0,
+  VSA_WS_LSE_DELTA = 0,
   VSA_WS_KV_ORDER = 1,
   VSA_WS_Q_ORDER = 2,
   VSA_WS_Q2K_NUM = 3,

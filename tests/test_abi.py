@@ -52,8 +52,8 @@ def test_workspace_sizes_and_layout():
     B, H, S = 1, 8, 32768
     nb = S // 64
     offs = [V.bwd_workspace_offset(B, H, S, r) for r in range(V.WS_END + 1)]
-    assert offs[V.WS_DELTA] == 0
-    assert offs[V.WS_KV_ORDER] == B * H * S * 4
+    assert offs[V.WS_LSE_DELTA] == 0
+    assert offs[V.WS_KV_ORDER] == B * H * S * 2 * 4
     assert offs[V.WS_Q_ORDER] == offs[V.WS_KV_ORDER] + B * H * nb * 4
     assert offs[V.WS_Q2K_NUM] == offs[V.WS_Q_ORDER] + B * H * nb * 4
     assert offs[V.WS_Q2K_IDX] == offs[V.WS_Q2K_NUM] + B * H * nb * 4

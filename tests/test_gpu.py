@@ -220,6 +220,11 @@ def _bwd_small(c, label):
     rdelta = O.delta(o.cpu(), c.do)
     gd = plan.delta().cpu().double().numpy()
     assert np.abs(gd - rdelta).max() <= 1e-5 * max(1.0, np.abs(rdelta).max())
+    # the records also carry -lse / scale_log2, divided in IEEE fp32 (torch's division rounds
+    # the same way)
+    glse = plan.lse_delta()[:, :, :, 0, :].reshape(c.B, c.H, c.S)
+    c2 = torch.tensor(plan.scale_log2(), dtype=torch.float32)
+    assert torch.equal(glse.cpu(), -(lse.cpu() / c2))
     return dq, dk, dv, rdq, rdk, rdv
 
 
