@@ -40,9 +40,17 @@ FLAGS = [
 ]
 
 
+# Per-source code generation options. The kv-major dK/dV kernel keeps its S and dP accumulators
+# in VGPRs, where the softmax arithmetic reads them, instead of accumulation registers that
+# would need a copy per element per step.
+SOURCE_FLAGS = {
+    "bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

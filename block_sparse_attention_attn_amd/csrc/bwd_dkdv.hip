@@ -106,10 +106,10 @@ bwd_dkdv_kernel(BwdParams p) {
   VSA_LDS char* const dr = (VSA_LDS char*)do_ring;
   VSA_LDS char* const lr = (VSA_LDS char*)ld_ring;
   uint32_t toff[4];
-  tile_offsets<4>(toff, lane, w);
+  tile_offsets_wave(toff, lane, w);
   const uint32_t roff = 16 * lane + 128 * w;  // this wave's quarter of a record (lanes 0..7)
-  const uint32_t q_lds = lds_addr(qr) + 1024 * w;
-  const uint32_t do_lds = lds_addr(dr) + 1024 * w;
+  const uint32_t q_lds = lds_addr(qr) + 4096 * w;  // this wave's slices 4w .. 4w+3
+  const uint32_t do_lds = lds_addr(dr) + 4096 * w;
   const uint32_t ld_lds = lds_addr(lr) + 128 * w;
   auto issue = [&](int qb, int st) __attribute__((always_inline)) {
     const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
@@ -165,11 +165,11 @@ bwd_dkdv_kernel(BwdParams p) {
   // A operands of S = Q K^T and dP = dO V^T for the q block in stage st: q rows 32*wq + l32,
   // d = 16*s + 8*g + 0..7
   bf16x8 qa[8], da[8];
-  auto load_rows = [&](int st) __attribute__((always_inline)) {
+  auto load_rows = [&](int st, int sb) __attribute__((always_inline)) {  // steps sb .. sb+3
     VSA_LDS char* qt = qr + st * STAGE_BYTES;
     VSA_LDS char* dt = dr + st * STAGE_BYTES;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = sb; s < sb + 4; ++s) {
       qa[s] = *(const VSA_LDS bf16x8*)(qt + tile_byte(qrow, 2 * s + g));
       da[s] = *(const VSA_LDS bf16x8*)(dt + tile_byte(qrow, 2 * s + g));
     }
@@ -192,7 +192,8 @@ bwd_dkdv_kernel(BwdParams p) {
   };
 
   f32x16 s0, p0, s1, p1;
-  load_rows(0);
+  load_rows(0, 0);
+  load_rows(0, 4);
   load_init(0, s0, p0);
   barrier_lds();  // everyone has read K/V out of stage 3
   issue(clampq(e3), 3);
@@ -201,17 +202,18 @@ bwd_dkdv_kernel(BwdParams p) {
     s0 = mfma32(qa[s], kf[s], s0);
     p0 = mfma32(da[s], vf[s], p0);
   }
-  load_rows(1);  // a repeat of q block 0 when n == 1
+  load_rows(1, 0);  // a repeat of q block 0 when n == 1
+  load_rows(1, 4);
   load_init(1, s1, p1);
 
   // Step t (q block t in stage st = t % 4): on entry (sc, pc) hold S - lse/scale_log2 and
   // dP - Delta of q block t, (sn, pn) the initial values of q block t+1 and (qa, da) its rows.
-  //   phase B: S/dP MFMAs of t+1, interleaved with P, dS of t and the transposed dO^T, Q^T reads
-  //            of t;
+  //   phase B: S/dP MFMAs of t+1, interleaved with the transposed dO^T, Q^T reads of t and
+  //            P, dS of t;
   //   mid:     q block t+2 has landed (own DMAs, then the barrier: everyone's) and everyone is
   //            done with stage st, which then receives q block t+4;
-  //   phase C: dV/dK MFMAs of t, interleaved with the row and record reads of t+2 into
-  //            (qa, da) and (sc, pc).
+  //   phase C: dV/dK MFMAs of t, interleaved with the record and row reads of t+2 into (sc, pc)
+  //            and (qa, da) and the DMA of q block t+4.
   // The last steps compute throwaway S/dP from repeated q blocks, which keeps the body free of
   // branches. The loop is unrolled by four so stage offsets are constants.
   auto step = [&](int t, int st, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn)
@@ -241,27 +243,30 @@ bwd_dkdv_kernel(BwdParams p) {
       sn = mfma32(qa[s], kf[s], sn);
       pn = mfma32(da[s], vf[s], pn);
     }
-    // P and dS of q block t. A padded kv column (zero K/V fragment) gets some finite or
-    // non-finite P; it only feeds that kv row of dV/dK, which the epilogue overwrites with 0.
-    float pv[16], dsv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sc[i] * scale_log2);
-      dsv[i] = pv[i] * pc[i];
-    }
+    // P and dS of q block t, half h (elements 8h .. 8h+7: q rows 32*wq + 16h + ..) in bf16. A
+    // padded kv column (zero K/V fragment) gets some finite or non-finite P; it only feeds that
+    // kv row of dV/dK, which the epilogue overwrites with 0.
     bf16x8 pa[2], sa[2];
+    auto softmax_half = [&](int h) __attribute__((always_inline)) {
+      float pv[8], dsv[8];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      pa[s2] = pack8(pv[8 * s2 + 0], pv[8 * s2 + 1], pv[8 * s2 + 2], pv[8 * s2 + 3],
-                     pv[8 * s2 + 4], pv[8 * s2 + 5], pv[8 * s2 + 6], pv[8 * s2 + 7]);
-      sa[s2] = pack8(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
-                     dsv[8 * s2 + 4], dsv[8 * s2 + 5], dsv[8 * s2 + 6], dsv[8 * s2 + 7]);
-    }
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(sc[8 * h + e] * scale_log2);
+        dsv[e] = pv[e] * pc[8 * h + e];
+      }
+      pa[h] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      sa[h] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    };
+    // Under the S/dP MFMAs; the empty asm keeps this arithmetic in this phase (it is otherwise
+    // free to sink next to its use after the barrier).
+    softmax_half(0);
+    softmax_half(1);
+    asm volatile("" : "+v"(pa[0]), "+v"(sa[0]), "+v"(pa[1]), "+v"(sa[1]));
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -272,23 +277,36 @@ bwd_dkdv_kernel(BwdParams p) {
     const int raw = entry(t + 4);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK));
     barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
-    issue(clampq(raw), st);
 
     // ---- phase C ----
-    load_rows(st2);
-    load_init(st2, sc, pc);
+    // dV/dK MFMAs of t. Record and row reads of q block t+2 (records first: they seed the first
+    // MFMAs of the next step), with q block t+4's DMA group into stage st split in three and
+    // placed between them: the asm blocks keep their order relative to the reads, so the nine
+    // DMAs spread over the phase instead of reaching the address unit together.
+    {
+      const int qb = clampq(raw);
+      const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
+      load_init(st2, sc, pc);
+      dma_rec128(recs + (size_t)qb * LD_RECORD_FLOATS, roff, ld_lds + st * LD_BYTES);
+      load_rows(st2, 0);
+      dma_tile(qh + tile, toff, q_lds + st * STAGE_BYTES);
+      load_rows(st2, 4);
+      dma_tile(doh + tile, toff, do_lds + st * STAGE_BYTES);
+    }
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int nt = 0; nt < 4; ++nt) {
+      dv_acc[nt] = mfma32(pa[0], db[0][nt], dv_acc[nt]);
+      dk_acc[nt] = mfma32(sa[0], qbt[0][nt], dk_acc[nt]);
+    }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        dv_acc[nt] = mfma32(pa[s2], db[s2][nt], dv_acc[nt]);
-        dk_acc[nt] = mfma32(sa[s2], qbt[s2][nt], dk_acc[nt]);
-      }
+    for (int nt = 0; nt < 4; ++nt) {
+      dv_acc[nt] = mfma32(pa[1], db[1][nt], dv_acc[nt]);
+      dk_acc[nt] = mfma32(sa[1], qbt[1][nt], dk_acc[nt]);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three row / record reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three record / row reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
     __builtin_amdgcn_sched_barrier(0);

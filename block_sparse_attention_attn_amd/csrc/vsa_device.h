@@ -162,11 +162,24 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
-// This wave's share of two [64][128] bf16 tiles in one asm block: slices w, w+4, w+8, w+12 of
-// each (w = wave), i.e. eight 1-KiB DMAs. `off` holds the per-lane global byte offsets of the
-// four slices (tile_offsets<4>); slice i lands at LDS lds_a / lds_b + 4 KiB * i, where lds_a and
-// lds_b already include this wave's first slice. Tile bases and LDS addresses are uniform.
-// Every write of M0 is followed by one wait state before the DMA that reads it; M0 is restored.
+// Tile DMA with one M0 write per tile. A [64][128] bf16 tile is 16 slices of 1 KiB (4 rows
+// each); wave w of four copies slices 4w .. 4w+3, whose LDS destinations are consecutive KiB.
+// global_load_lds adds its immediate offset to both the global and the LDS address, so M0 is set
+// once to the wave's first slice and the four DMAs carry offsets 0, 1024, 2048, 3072; the
+// per-lane global offsets (tile_offsets_wave) have the matching 1024 * i taken off.
+__device__ __forceinline__ void tile_offsets_wave(uint32_t* off, int lane, int w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = (4 * w + i) * 64 + lane;  // 16-byte chunk slot this lane fills
+    const int r = slot >> 4;
+    const int cc = (slot & 15) ^ swz128(r);
+    off[i] = (uint32_t)((r * HEAD_DIM + cc * 8) * 2 - 1024 * i);  // >= 0: row r >= 16w + 4i
+  }
+}
+
+// This wave's four slices of two tiles (ga -> lds_a, gb -> lds_b; the LDS addresses include the
+// wave's 4w KiB) in one asm block: eight vector memory operations. Every write of M0 is followed
+// by one wait state before the DMA that reads it; M0 is restored.
 __device__ __forceinline__ void dma_tile_pair(const void* ga, const void* gb, const uint32_t* off,
                                               uint32_t lds_a, uint32_t lds_b) {
   const uint64_t a = uniform_u64(ga), b = uniform_u64(gb);
@@ -177,31 +190,59 @@ __device__ __forceinline__ void dma_tile_pair(const void* ga, const void* gb, co
       "s_mov_b32 m0, %7\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %5\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %5\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %5\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %5\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %5 offset:3072\n\t"
       "s_mov_b32 m0, %8\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %6\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %6\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %6\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %6\n\t"
+      "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %6 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %6 offset:3072\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(a), "s"(b), "s"(la), "s"(lb)
-      : "memory", "scc");
+      : "memory");
+}
+
+// The same for one tile: four vector memory operations.
+__device__ __forceinline__ void dma_tile(const void* ga, const uint32_t* off, uint32_t lds_a) {
+  const uint64_t a = uniform_u64(ga);
+  const uint32_t la = uniform_u32(lds_a);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %5 offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(a), "s"(la)
+      : "memory");
+}
+
+// 128 bytes of a small record: lanes 0..7 copy rec + roff to LDS lds_r + 16 * lane, with EXEC
+// narrowed to them inside the asm block. One vector memory operation.
+__device__ __forceinline__ void dma_rec128(const void* rec, uint32_t roff, uint32_t lds_r) {
+  const uint64_t r = uniform_u64(rec);
+  const uint32_t lr = uniform_u32(lds_r);
+  uint32_t saved;
+  uint64_t exec_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, 0xff\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b64 exec, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved), "=&s"(exec_saved)
+      : "v"(roff), "s"(r), "s"(lr)
+      : "memory");
 }
 
 // dma_tile_pair plus 128 bytes of a small record: lanes 0..7 copy rec + roff (per-lane byte
@@ -220,27 +261,15 @@ __device__ __forceinline__ void dma_tile_pair_rec(const void* ga, const void* gb
       "s_mov_b32 m0, %10\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, %7\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %7\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %7\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %5, %7\n\t"
+      "global_load_lds_dwordx4 %3, %7 offset:1024\n\t"
+      "global_load_lds_dwordx4 %4, %7 offset:2048\n\t"
+      "global_load_lds_dwordx4 %5, %7 offset:3072\n\t"
       "s_mov_b32 m0, %11\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, %8\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %8\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %8\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %5, %8\n\t"
+      "global_load_lds_dwordx4 %3, %8 offset:1024\n\t"
+      "global_load_lds_dwordx4 %4, %8 offset:2048\n\t"
+      "global_load_lds_dwordx4 %5, %8 offset:3072\n\t"
       "s_mov_b64 %1, exec\n\t"
       "s_mov_b64 exec, 0xff\n\t"
       "s_mov_b32 m0, %12\n\t"
@@ -251,7 +280,7 @@ __device__ __forceinline__ void dma_tile_pair_rec(const void* ga, const void* gb
       : "=&s"(saved), "=&s"(exec_saved)
       : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(roff), "s"(a), "s"(b), "s"(r),
         "s"(la), "s"(lb), "s"(lr)
-      : "memory", "scc");
+      : "memory");
 }
 
 // Per-lane byte offsets inside a [64][128] bf16 tile for the slices part, part + NPARTS, ... that
