@@ -40,11 +40,12 @@ FLAGS = [
 ]
 
 
-# Per-source code generation options. The kv-major dK/dV kernel keeps its S and dP accumulators
-# in VGPRs, where the softmax arithmetic reads them, instead of accumulation registers that
-# would need a copy per element per step.
+# Per-source code generation options. The backward kernels keep their MFMA accumulators in
+# VGPRs, where the softmax arithmetic reads them, instead of accumulation registers that would
+# need a copy per element per step.
 SOURCE_FLAGS = {
     "bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
