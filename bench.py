@@ -82,7 +82,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_workload(n, steps, warmup):
+def run_workload(n, steps, warmup, dq_mode):
     import torch
 
     import block_sparse_attention_attn_amd as V
@@ -100,7 +100,8 @@ def run_workload(n, steps, warmup):
     k2q_num = torch.empty(c.B, c.H, c.nb, dtype=torch.int32, device=dev)
     inv_ws = torch.empty(V.invert_workspace_bytes(c.B, c.H, c.nb, c.nb), dtype=torch.uint8,
                          device=dev)
-    plan = V.BwdPlan(do, q, k, v, o, lse, k2q_idx, k2q_num, vbs, q2k_idx=idx, q2k_num=num)
+    plan = V.BwdPlan(do, q, k, v, o, lse, k2q_idx, k2q_num, vbs, q2k_idx=idx, q2k_num=num,
+                     dq_mode=dq_mode)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -148,9 +149,13 @@ def run_workload(n, steps, warmup):
         dkdv_ms=statistics.mean(dkdv), dkdv_ms_median=statistics.median(dkdv),
         dq_ms=statistics.mean(dq), dq_ms_median=statistics.median(dq))
     res["bwd_tflops"] = pairs * FLOP_PER_PAIR / (res["bwd_ms"] * 1e-3) / 1e12
-    # executed MFMA work: 4 GEMMs per pair in the dK/dV kernel, 3 in the dQ kernel
+    # executed MFMA work: 4 GEMMs per pair in the dK/dV kernel; 3 in the recomputing dQ kernel,
+    # 1 in the spill one, which reads 8 KiB of dS per pair from HBM
+    spill = dq_mode == V.DQ_SPILL
     res["dkdv_tflops"] = pairs * 4 * GEMM_FLOP / (res["dkdv_ms"] * 1e-3) / 1e12
-    res["dq_tflops"] = pairs * 3 * GEMM_FLOP / (res["dq_ms"] * 1e-3) / 1e12
+    res["dq_tflops"] = pairs * (1 if spill else 3) * GEMM_FLOP / (res["dq_ms"] * 1e-3) / 1e12
+    if spill:
+        res["dq_ds_read_GBps"] = pairs * 8192 / (res["dq_ms"] * 1e-3) / 1e9
     res["fwd_tflops"] = pairs * 2 * GEMM_FLOP / (res["fwd_ms"] * 1e-3) / 1e12
     del plan
     torch.cuda.empty_cache()
@@ -196,6 +201,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=(3, 4))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--dq-mode", choices=("spill", "recompute"), default="spill",
+                    help="dQ from dS tiles the dK/dV kernel spills to the workspace (8 KiB per "
+                         "pair), or recomputed from Q, K, V, dO")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (a known byte count for "
                          "scaling hardware traffic counters)")
@@ -218,13 +226,15 @@ def main():
         log("[bench] copy calibration: 268435456 bytes read, 268435456 bytes written")
         del src, dst
     log(f"[bench] workload {args.workload}: steps={args.steps} warmup={args.warmup}")
-    res, case = run_workload(args.workload, args.steps, args.warmup)
+    import block_sparse_attention_attn_amd as V
+    mode = V.DQ_SPILL if args.dq_mode == "spill" else V.DQ_RECOMPUTE
+    res, case = run_workload(args.workload, args.steps, args.warmup, mode)
     log(f"[bench] {json.dumps(res)}")
     secondary = None
     if not args.no_secondary:
         other = 4 if args.workload == 3 else 3
         log(f"[bench] secondary workload {other}")
-        r2, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2))
+        r2, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2), mode)
         log(f"[bench] {json.dumps(r2)}")
         secondary = dict(workload=WORKLOAD_TEXT[other], bwd_tflops=round(r2["bwd_tflops"], 2),
                          bwd_ms=round(r2["bwd_ms"], 4), dkdv_ms=round(r2["dkdv_ms"], 4),
@@ -257,6 +267,7 @@ def main():
             "heads": case.H,
             "head_dim": 128,
             "selected_pairs": res["pairs"],
+            "dq_mode": args.dq_mode,
             "parallelism": "none (1 GPU)",
         },
         "frac_of_peak": round(res["bwd_tflops"] / PEAK_BF16_TFLOPS, 4),

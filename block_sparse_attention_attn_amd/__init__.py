@@ -28,6 +28,7 @@ __all__ = [
     "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "ORDER_BIN_WIDTH", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
+    "DQ_RECOMPUTE", "DQ_SPILL",
 ]
 
 BLOCK = 64
@@ -59,11 +60,16 @@ class _BwdArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("batch", ctypes.c_int),
                 ("heads", ctypes.c_int), ("seqlen", ctypes.c_int), ("head_dim", ctypes.c_int),
                 ("num_kv_blocks", ctypes.c_int), ("max_q_blocks", ctypes.c_int),
-                ("q2k_stride", ctypes.c_int), ("sm_scale", ctypes.c_float)]
+                ("q2k_stride", ctypes.c_int), ("sm_scale", ctypes.c_float),
+                ("dq_mode", ctypes.c_int)]
 
 
 # workspace regions of the backward (vsa_bwd_ws_region)
-WS_LSE_DELTA, WS_KV_ORDER, WS_Q_ORDER, WS_Q2K_NUM, WS_Q2K_IDX, WS_BITMAP, WS_END = range(7)
+(WS_LSE_DELTA, WS_KV_ORDER, WS_Q_ORDER, WS_Q2K_NUM, WS_Q2K_IDX, WS_BITMAP, WS_KBASE, WS_QENT,
+ WS_DS, WS_END) = range(10)
+# how the q-major kernel gets dS (vsa_dq_mode): recomputed from Q, K, V, dO, or spilled by the
+# kv-major kernel into the workspace (8 KiB per possible pair)
+DQ_RECOMPUTE, DQ_SPILL = 0, 1
 
 
 # name -> (restype, argtypes); exactly the symbols include/vsa.h declares
@@ -76,8 +82,8 @@ _SIGNATURES = {
                                           ctypes.c_size_t, _p]),
     "vsa_fwd_check": (ctypes.c_int, [ctypes.POINTER(_FwdArgs)]),
     "vsa_fwd": (ctypes.c_int, [ctypes.POINTER(_FwdArgs), _p]),
-    "vsa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
-    "vsa_bwd_workspace_offset": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "vsa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "vsa_bwd_workspace_offset": (ctypes.c_size_t, [ctypes.c_int] * 6),
     "vsa_bwd_check": (ctypes.c_int, [ctypes.POINTER(_BwdArgs)]),
     "vsa_bwd": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), _p]),
     "vsa_bwd_stage": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), ctypes.c_int, _p]),
@@ -229,13 +235,17 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
     return o, lse
 
 
-def bwd_workspace_bytes(batch: int, heads: int, seqlen: int, derive_q2k: bool = True) -> int:
-    return int(lib().vsa_bwd_workspace_bytes(batch, heads, seqlen, int(bool(derive_q2k))))
+def bwd_workspace_bytes(batch: int, heads: int, seqlen: int, q2k_stride: int = 0,
+                        dq_mode: int = DQ_RECOMPUTE) -> int:
+    """Workspace bytes of a backward call; ``q2k_stride`` is the row width of the q2k lists the
+    call passes, 0 when the library derives them."""
+    return int(lib().vsa_bwd_workspace_bytes(batch, heads, seqlen, q2k_stride, dq_mode))
 
 
-def bwd_workspace_offset(batch: int, heads: int, seqlen: int, region: int) -> int:
+def bwd_workspace_offset(batch: int, heads: int, seqlen: int, region: int, q2k_stride: int = 0,
+                         dq_mode: int = DQ_RECOMPUTE) -> int:
     """Byte offset of a backward workspace region (WS_LSE_DELTA, WS_KV_ORDER, ...)."""
-    return int(lib().vsa_bwd_workspace_offset(batch, heads, seqlen, region))
+    return int(lib().vsa_bwd_workspace_offset(batch, heads, seqlen, q2k_stride, dq_mode, region))
 
 
 def bwd_order(k2q_num: torch.Tensor, bin_width: int = ORDER_BIN_WIDTH,
@@ -265,7 +275,7 @@ class BwdPlan:
 
     def __init__(self, grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                  sm_scale=None, order=None, workspace=None, out=None, q2k_idx=None,
-                 q2k_num=None):
+                 q2k_num=None, dq_mode=DQ_RECOMPUTE):
         _need_gpu(q, "q")
         if q.dim() != 4:
             raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
@@ -303,8 +313,9 @@ class BwdPlan:
             sm_scale = 1.0 / math.sqrt(D)
         if out is None:
             out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        kq = qidx.shape[-1] if qidx is not None else 0
         if workspace is None:
-            workspace = torch.empty(bwd_workspace_bytes(B, H, S, qidx is None), dtype=torch.uint8,
+            workspace = torch.empty(bwd_workspace_bytes(B, H, S, kq, dq_mode), dtype=torch.uint8,
                                     device=q.device)
         self.dq, self.dk, self.dv = out
         self.workspace = workspace
@@ -316,7 +327,7 @@ class BwdPlan:
                              self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                              B, H, S, D, nb, idx.shape[-1],
-                             qidx.shape[-1] if qidx is not None else 0, float(sm_scale))
+                             kq, float(sm_scale), int(dq_mode))
         self._ref = ctypes.byref(self.args)
         _check(lib().vsa_bwd_check(self._ref), "vsa_bwd")
 
@@ -330,7 +341,8 @@ class BwdPlan:
     def region(self, r: int, count: int, dtype=torch.int32) -> torch.Tensor:
         """``count`` elements of workspace region ``r`` (WS_LSE_DELTA, WS_KV_ORDER, ...)."""
         a = self.args
-        off = bwd_workspace_offset(a.batch, a.heads, a.seqlen, r)
+        off = bwd_workspace_offset(a.batch, a.heads, a.seqlen, r, a.q2k_stride if a.q2k_idx else 0,
+                                   a.dq_mode)
         nbytes = count * torch.empty(0, dtype=dtype).element_size()
         return self.workspace[off:off + nbytes].view(dtype)
 
@@ -361,16 +373,16 @@ def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
                       workspace: Optional[torch.Tensor] = None,
                       out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                       q2k_idx: Optional[torch.Tensor] = None,
-                      q2k_num: Optional[torch.Tensor] = None):
+                      q2k_num: Optional[torch.Tensor] = None, dq_mode: int = DQ_RECOMPUTE):
     """Backward from k2q metadata (``[B, H, nb, max_q_blocks]`` or ``[B*H*nb, max_q_blocks]``
     plus ``[B, H, nb]`` counts). Returns ``(dq, dk, dv)`` bf16."""
     return BwdPlan(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                    sm_scale=sm_scale, order=order, workspace=workspace, out=out,
-                   q2k_idx=q2k_idx, q2k_num=q2k_num).run()
+                   q2k_idx=q2k_idx, q2k_num=q2k_num, dq_mode=dq_mode).run()
 
 
 def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
-             sm_scale: Optional[float] = None):
+             sm_scale: Optional[float] = None, dq_mode: int = DQ_RECOMPUTE):
     """Backward from the forward's q2k metadata: inverts to k2q on the GPU, then runs the
     backward with both lists (the q-major dQ kernel walks q2k, the kv-major kernel k2q). The q2k
     rows must not repeat a kv block. Returns ``(dq, dk, dv)``."""
@@ -384,4 +396,4 @@ def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
     nb = variable_block_sizes.numel()
     k2q_idx, k2q_num = invert_indices(idx, num, nb)
     return backward_from_k2q(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
-                             sm_scale=sm_scale, q2k_idx=idx, q2k_num=num)
+                             sm_scale=sm_scale, q2k_idx=idx, q2k_num=num, dq_mode=dq_mode)

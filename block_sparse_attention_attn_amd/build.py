@@ -46,6 +46,7 @@ FLAGS = [
 SOURCE_FLAGS = {
     "bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd_dq_spill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

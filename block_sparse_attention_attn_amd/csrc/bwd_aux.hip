@@ -7,7 +7,9 @@
 //               kv-major kernel's S and dP MFMAs;
 //   order       the per-(b, h) length-binned permutation of work items that the launch header
 //               computes on device from 1024 kv blocks on (its order-kernel launch and the
-//               ORDER_MIN_KV_BLOCKS comment); used for the kv-major and the q-major kernel.
+//               ORDER_MIN_KV_BLOCKS comment); used for the kv-major and the q-major kernel;
+//   slot tables for the dS spill: where each (q block, kv block) pair's dS tile goes (kv-major
+//               order, contiguous per kv block) and, per q2k entry, where to find it.
 // The preprocess streams with 16-byte accesses, consecutive lanes on consecutive 16-byte chunks
 // of a row. (The pages' dQ postprocess -- scale by sm_scale, round to bf16 -- is fused into the
 // q-major dQ kernel's epilogue here.)
@@ -100,6 +102,93 @@ __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restri
 void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
                       hipStream_t stream) {
   hipLaunchKernelGGL(bwd_order_kernel, dim3(BH), dim3(1024), 0, stream, num, nb, bin_width, order);
+}
+
+// One workgroup per head: exclusive prefix sum of the clamped k2q counts. Thread t sums a
+// contiguous chunk of ceil(nb / 1024) counts, the 1024 chunk sums are scanned in LDS, and each
+// thread writes its chunk's prefixes.
+__global__ void __launch_bounds__(1024) spill_kbase_kernel(const int32_t* __restrict__ num, int nb,
+                                                           int stride, int32_t* __restrict__ kbase) {
+  __shared__ int32_t part[1024];
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int chunk = (nb + 1023) / 1024;
+  const int lo = tid * chunk;
+  const int hi = lo + chunk < nb ? lo + chunk : nb;
+  const int32_t* row = num + (size_t)bh * nb;
+  auto cnt = [&](int i) {
+    const int c = row[i];
+    return c < 0 ? 0 : (c > stride ? stride : c);
+  };
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += cnt(i);
+  part[tid] = sum;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the chunk sums
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;  // exclusive prefix of this chunk
+  for (int i = lo; i < hi; ++i) {
+    kbase[(size_t)bh * nb + i] = run;
+    run += cnt(i);
+  }
+}
+
+void launch_spill_kbase(const int32_t* k2q_num, int BH, int nb, int k2q_stride, int32_t* kbase,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(spill_kbase_kernel, dim3(BH), dim3(1024), 0, stream, k2q_num, nb, k2q_stride,
+                     kbase);
+}
+
+// One thread per q2k entry (bh, q, s): binary search of q in the ascending k2q row of its kv
+// block. A q missing from that row (a caller-contract violation: k2q is not the inverse of q2k,
+// or not ascending) gets the row's first slot, so every slot stays inside the head's range.
+__global__ void __launch_bounds__(256) spill_qent_kernel(
+    const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_num, int q2k_stride,
+    const int32_t* __restrict__ k2q_idx, const int32_t* __restrict__ k2q_num, int k2q_stride,
+    const int32_t* __restrict__ kbase, const int32_t* __restrict__ vbs, int nb, int cap,
+    int64_t* __restrict__ qent) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;  // entry within the head
+  const int bh = blockIdx.y;
+  if (e >= (size_t)nb * q2k_stride) return;
+  const int q = (int)(e / q2k_stride);
+  const int s = (int)(e - (size_t)q * q2k_stride);
+  const size_t qrow = (size_t)bh * nb + q;
+  int n = q2k_num[qrow];
+  n = n < 0 ? 0 : (n > q2k_stride ? q2k_stride : n);
+  if (s >= n) return;
+  int kv = q2k_idx[qrow * q2k_stride + s];
+  kv = kv < 0 ? 0 : (kv >= nb ? nb - 1 : kv);
+  const size_t krow = (size_t)bh * nb + kv;
+  int m = k2q_num[krow];
+  m = m < 0 ? 0 : (m > k2q_stride ? k2q_stride : m);
+  const int32_t* list = k2q_idx + krow * k2q_stride;
+  int lo = 0, hi = m;  // first position with list[pos] >= q
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] < q) lo = mid + 1; else hi = mid;
+  }
+  const int t = (lo < m && list[lo] == q) ? lo : 0;
+  int slot = kbase[krow] + t;
+  slot = slot < 0 ? 0 : (slot >= cap ? cap - 1 : slot);
+  int vb = vbs[kv];
+  vb = vb < 0 ? 0 : (vb > BLOCK ? BLOCK : vb);
+  qent[qrow * q2k_stride + s] =
+      (int64_t)(uint32_t)slot | ((int64_t)kv << 32) | ((int64_t)vb << 48);
+}
+
+void launch_spill_qent(const int32_t* q2k_idx, const int32_t* q2k_num, int q2k_stride,
+                       const int32_t* k2q_idx, const int32_t* k2q_num, int k2q_stride,
+                       const int32_t* kbase, const int32_t* vbs, int BH, int nb, int cap,
+                       int64_t* qent, hipStream_t stream) {
+  const size_t per_head = (size_t)nb * q2k_stride;
+  hipLaunchKernelGGL(spill_qent_kernel, dim3((unsigned)((per_head + 255) / 256), BH), dim3(256), 0,
+                     stream, q2k_idx, q2k_num, q2k_stride, k2q_idx, k2q_num, k2q_stride, kbase,
+                     vbs, nb, cap, qent);
 }
 
 }  // namespace vsa

@@ -51,6 +51,7 @@ constexpr int STAGES = 4;                        // ring depth: stage t%4 holds 
 constexpr int STAGE_BYTES = 16384;               // one [64][128] bf16 tile
 constexpr int LD_BYTES = LD_RECORD_FLOATS * 4;   // one q block's statistics record
 constexpr int DMA_PER_BLOCK = 9;                 // vector memory operations per wave per q block
+constexpr int STORES_PER_BLOCK = 2;              // dS stores per wave per q block (spill mode)
 
 __device__ __forceinline__ void barrier_lds() {
   // Wait for this wave's LDS traffic, then meet the other waves. Vector memory traffic (the next
@@ -66,6 +67,9 @@ __device__ __forceinline__ void barrier_lds_with(int v) {
 
 }  // namespace
 
+// SPILL: also write each pair's dS tile (bf16, the A operand of the dK GEMM) to the spill buffer
+// for the q-major dQ GEMM (bwd_dq_spill.hip).
+template <bool SPILL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char q_ring[STAGES * STAGE_BYTES];
@@ -130,9 +134,31 @@ bwd_dkdv_kernel(BwdParams p) {
     issue(clampq(e1), 1);  // (past the end of the list: repeats of the last q block)
     issue(clampq(e2), 2);
   }
+  // dS tiles (spill mode): q block t of this item goes to slot kbase[item] + t of its head. A
+  // lane stores its 16 dS values (two bf16x8) as one 32-byte record; the records of a wave's
+  // 32 kv rows are laid out so that the q-major kernel's transposed reads of two record groups
+  // fall on disjoint banks: record (w, g, l32) at ((8w + l32/4) * 256 + 128g + 32(l32%4)) bytes.
+  char* ds_item = nullptr;
+  int slot0 = 0;
+  const uint32_t ds_rec = ((8 * w + (l32 >> 2)) * 256 + 128 * g + 32 * (l32 & 3));
+  auto ds_tile = [&](int t) {
+    int slot = slot0 + t;
+    slot = slot < p.cap ? slot : p.cap - 1;  // inconsistent counts: stay inside the head
+    return ds_item + (size_t)slot * (BLOCK * BLOCK * 2);
+  };
+  if (SPILL) {
+    ds_item = (char*)p.ds + (size_t)bh * p.cap * (BLOCK * BLOCK * 2);
+    slot0 = ld_const(p.kbase, item);
+    // Two stores of zeros into q block 0's tile (rewritten at step 0: one wave's stores to one
+    // address land in order), so that every wait below counts the same two stores between the
+    // DMA groups of consecutive q blocks.
+    char* d = ds_tile(0) + ds_rec;
+    *(bf16x8*)d = bf16x8{};
+    *(bf16x8*)(d + 16) = bf16x8{};
+  }
   const int e3 = entry(3);
   // K/V and q blocks 0, 1 landed (own DMAs); q block 2's may still be in flight
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
   barrier_lds_with(e3);  // ... everyone's
 
   // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
@@ -274,8 +300,9 @@ bwd_dkdv_kernel(BwdParams p) {
     // Every step issues one q block's DMA group (past the end of the list: a repeat of the last
     // q block, into a stage nobody reads again), so the group of t+3 is always the newest and
     // nine outstanding operations mean q block t+2 has landed. No branch splits the step.
+    // (In spill mode the two dS stores of step t-1 sit between the groups of t+2 and t+3.)
     const int raw = entry(t + 4);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
     barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
 
     // ---- phase C ----
@@ -283,6 +310,11 @@ bwd_dkdv_kernel(BwdParams p) {
     // MFMAs of the next step), with q block t+4's DMA group into stage st split in three and
     // placed between them: the asm blocks keep their order relative to the reads, so the nine
     // DMAs spread over the phase instead of reaching the address unit together.
+    if (SPILL) {  // streamed past the caches: read once, by the q-major kernel
+      char* d = ds_tile(t) + ds_rec;
+      __builtin_nontemporal_store(sa[0], (bf16x8*)d);
+      __builtin_nontemporal_store(sa[1], (bf16x8*)(d + 16));
+    }
     {
       const int qb = clampq(raw);
       const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
@@ -358,7 +390,10 @@ bwd_dkdv_kernel(BwdParams p) {
 }
 
 void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.items_per_xcd * 8), dim3(256), 0, stream, p);
+  if (p.ds)
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(p.items_per_xcd * 8), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(p.items_per_xcd * 8), dim3(256), 0, stream, p);
 }
 
 }  // namespace vsa

@@ -1,0 +1,230 @@
+// bwd_dq_spill.hip -- dQ of the 64-token block-sparse attention backward from spilled dS tiles
+// (gfx950): the q-major half of the backward's main step when the kv-major kernel has written
+// every pair's dS to the workspace.
+//
+// What it computes (the gradient of the FastVideo backward test page's masked-dense reference;
+// launch header argument struct: dq carries sm_scale): for one q block i of (b, h),
+//     dQ_i = sum over kv blocks j in its q2k list of dS_ij K_j,    dq_i = bf16(sm_scale * dQ_i)
+// with dS_ij the bf16 tile the kv-major kernel used for dK_j (so dq and dk see the same dS), kv
+// rows at or past vbs[j] excluded. A q block with an empty list gets zero rows. This is the
+// pages' dQ accumulation and postprocess, reorganised as a per-q-block sum so that no atomics
+// and no fp32 accumulator are needed; it does one GEMM per pair instead of the three of the
+// recomputing kernel (bwd_dq.hip) and streams 8 KiB of dS per pair from HBM, which bounds it.
+//
+// gfx950 design: one 256-thread workgroup per q block, walking its slot-table row (VSA_WS_QENT:
+// dS slot, kv block and vbs per entry). Wave w computes dQ^T rows d = 32w .. 32w+31 for both q
+// halves: dQ^T += K^T dS^T with v_mfma_f32_32x32x16_bf16, four k-steps of 16 kv per pair. K_j
+// (16 KiB) and the dS tile (8 KiB) of each pair arrive by global_load_lds_dwordx4 into a
+// six-stage LDS ring, issued four pairs ahead of the step that reads them; both operands come
+// out of LDS through ds_read_b64_tr_b16, one pair ahead of their MFMAs. A pair of a ragged kv
+// block has its padded kv slots masked to zero in both operands (so neither stale K rows nor the
+// dS values of masked keys can reach dQ).
+#include "vsa_device.h"
+#include "vsa_kernels.h"
+
+namespace vsa {
+
+namespace {
+
+constexpr int STAGES = 6;
+constexpr int K_BYTES = 16384;  // one [64][128] bf16 K tile, swizzled
+constexpr int S_BYTES = 8192;   // one dS tile, as the kv-major kernel stored it
+constexpr int DMA_PER_PAIR = 6; // per wave: four 1-KiB slices of K, two of dS
+
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// The same barrier, with `v` (a scalar load's result) required in its registers first.
+__device__ __forceinline__ void barrier_lds_with(uint64_t v) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(v) : "memory");
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dq_spill_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char s_ring[STAGES * S_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_ring[STAGES * K_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int kh = lane >> 5;     // k half of the MFMA operands
+  const int grp = lane >> 4;    // 16-lane group
+  const int t16 = lane & 15;
+  const int gc = grp & 1;       // column half inside a 32-lane half
+
+  const int wid = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);
+  if (wid >= p.total_items) return;
+  const int item = p.q_order ? ld_const(p.q_order, wid) : wid;  // (b, h, q block)
+  if (item < 0 || item >= p.total_items) return;
+  int n = ld_const(p.q2k_num, item);
+  n = n < 0 ? 0 : (n > p.qent_stride ? p.qent_stride : n);
+  const int bh = item / p.nb;
+  const int i = item - bh * p.nb;
+  const size_t head = (size_t)bh * p.S * HEAD_DIM;
+  bf16* __restrict__ dq_blk = p.dq + head + (size_t)i * BLOCK * HEAD_DIM;
+  if (n == 0) {  // no selected kv block: zero rows
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *(i32x4*)((char*)dq_blk + (c * 256 + threadIdx.x) * 16) = i32x4{};
+    return;
+  }
+  const bf16* __restrict__ kh_ptr = p.k + head;
+  const char* __restrict__ ds_head = (const char*)p.ds + (size_t)bh * p.cap * S_BYTES;
+  const int64_t* __restrict__ ent = p.qent + (size_t)item * p.qent_stride;
+  auto entry = [&](int t) { return (uint64_t)ld_const(ent, t < n ? t : n - 1); };
+  auto kv_of = [&](uint64_t e) {
+    const int kv = (int)((e >> 32) & 0xFFFF);
+    return kv < p.nb ? kv : p.nb - 1;
+  };
+  auto slot_of = [&](uint64_t e) {
+    const int s = (int)(uint32_t)e;
+    return s < 0 ? 0 : (s >= p.cap ? p.cap - 1 : s);
+  };
+  auto vb_of = [&](uint64_t e) { return (int)((e >> 48) & 0xFF); };
+
+  uint32_t toff[4];
+  tile_offsets_wave(toff, lane, w);
+  const uint32_t k_lds = lds_addr((VSA_LDS char*)k_ring) + 4096 * w;
+  const uint32_t s_lds = lds_addr((VSA_LDS char*)s_ring) + 2048 * w;
+  const uint32_t s_off = 16 * lane;
+  auto issue = [&](uint64_t e, int st) __attribute__((always_inline)) {
+    dma_tile(kh_ptr + (size_t)kv_of(e) * BLOCK * HEAD_DIM, toff, k_lds + st * K_BYTES);
+    dma_lin2_nt(ds_head + (size_t)slot_of(e) * S_BYTES + 2048 * w, s_off, s_lds + st * S_BYTES);
+  };
+
+  // Operands of one pair. A = K^T: lane holds d = 32w + lane%32 and kv 16ks + 8kh + j. B = dS^T
+  // for q half qh: lane holds q column n = lane%32 (the record layout's order, see the epilogue)
+  // and the same kv. Each is two transposed reads of four kv rows.
+  struct Ops {
+    bf16x8 a[4];
+    bf16x8 b[2][4];
+  };
+  auto read_ops = [&](int st, Ops& o) __attribute__((always_inline)) {
+    VSA_LDS char* kt = (VSA_LDS char*)k_ring + st * K_BYTES;
+    VSA_LDS char* sb = (VSA_LDS char*)s_ring + st * S_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 16 * ks + 8 * kh;  // first kv of this lane's k slots
+      const int col = 32 * w + 16 * gc + 4 * (t16 & 3);
+      o.a[ks] = join(lds_read_tr(kt + tile_elem_byte(k0 + (t16 >> 2), col)),
+                     lds_read_tr(kt + tile_elem_byte(k0 + 4 + (t16 >> 2), col)));
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        s16x4 h2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kk = k0 + 4 * u;  // record rows kk .. kk+3: kv half kk/32, rows kk%32 ..
+          const int rec = ((qh + 2 * (kk >> 5)) * 8 + ((kk & 31) >> 2)) * 256 + 128 * gc +
+                          32 * (t16 >> 2) + 8 * (t16 & 3);
+          h2[u] = lds_read_tr(sb + rec);
+        }
+        o.b[qh][ks] = join(h2[0], h2[1]);
+      }
+    }
+  };
+  // Padded kv slots of a ragged block (kv >= vb) to zero, in both operands.
+  auto mask_ops = [&](int vb, Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 16 * ks + 8 * kh;
+      union {
+        i32x4 m;
+        bf16x8 v;
+      } mk;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        mk.m[d] = (k0 + 2 * d < vb ? 0xFFFF : 0) | (k0 + 2 * d + 1 < vb ? (int)0xFFFF0000u : 0);
+      auto andv = [&](bf16x8& x) {
+        union {
+          i32x4 m;
+          bf16x8 v;
+        } u;
+        u.v = x;
+        u.m &= mk.m;
+        x = u.v;
+      };
+      andv(o.a[ks]);
+      andv(o.b[0][ks]);
+      andv(o.b[1][ks]);
+    }
+  };
+
+  // ---- prologue: pairs 0..5 into stages 0..5 (past the end of the list: repeats) ----
+  uint64_t er[STAGES];
+#pragma unroll
+  for (int t = 0; t < STAGES; ++t) er[t] = entry(t);
+#pragma unroll
+  for (int t = 0; t < STAGES; ++t) issue(er[t], t);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * DMA_PER_PAIR));  // pairs 0, 1 landed
+  barrier_lds();  // ... everyone's
+
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  Ops x, y;
+  read_ops(0, x);
+  if (vb_of(er[0]) < BLOCK) mask_ops(vb_of(er[0]), x);
+
+  // Step t (pair t in stage t % 6): read pair t+1's operands, MFMAs of pair t; then pair t+2
+  // has landed (own DMAs, then the barrier: everyone's), everyone is done with stage t % 6, and
+  // pair t+6 goes there. The loop is unrolled by six so stage offsets are constants.
+  auto step = [&](int t, int st, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
+    const int st1 = st + 1 == STAGES ? 0 : st + 1;
+    read_ops(st1, nxt);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      acc[0] = mfma32(cur.a[ks], cur.b[0][ks], acc[0]);
+      acc[1] = mfma32(cur.a[ks], cur.b[1][ks], acc[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three transposed reads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint64_t e = entry(t + STAGES);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DMA_PER_PAIR));  // pair t+2 landed
+    barrier_lds_with(e);
+    issue(e, st);
+    const int vb1 = vb_of(er[st1]);
+    er[st] = e;
+    if (vb1 < BLOCK) mask_ops(vb1, nxt);  // rare: a ragged kv block
+  };
+  for (int t = 0; t < n; t += STAGES) {
+    step(t, 0, x, y);
+    if (t + 1 < n) step(t + 1, 1, y, x);
+    if (t + 2 < n) step(t + 2, 2, x, y);
+    if (t + 3 < n) step(t + 3, 3, y, x);
+    if (t + 4 < n) step(t + 4, 4, x, y);
+    if (t + 5 < n) step(t + 5, 5, y, x);
+  }
+  // no DMA may still be writing this workgroup's LDS when it ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // ---- epilogue: dq = bf16(sm_scale * dQ). acc[qh] element e of this lane is d = 32w +
+  // 8(e/4) + 4kh + e%4 and q = 32qh + q(n), n = lane%32, where the record layout puts column
+  // n = 16g + c at q = 16(c/8) + 8((c%8)/4) + 4g + c%4 ----
+  const int nn = lane & 31;
+  const int cq = nn & 15, gq = nn >> 4;
+  const int qoff = 16 * (cq >> 3) + 8 * ((cq & 7) >> 2) + 4 * gq + (cq & 3);
+  const float sc = p.sm_scale;
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    bf16* row = dq_blk + (size_t)(32 * qh + qoff) * HEAD_DIM + 32 * w + 4 * kh;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      union {
+        bf16 b[4];
+        s16x4 s;
+      } r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.b[e] = (bf16)(acc[qh][4 * c + e] * sc);
+      *(s16x4*)(row + 8 * c) = r.s;
+    }
+  }
+}
+
+void launch_bwd_dq_spill(const BwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_dq_spill_kernel, dim3(p.items_per_xcd * 8), dim3(256), 0, stream, p);
+}
+
+}  // namespace vsa

@@ -139,26 +139,35 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
 // backward
 // ------------------------------------------------------------------------------------------------
 
-size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int region) {
-  if (batch < 1 || heads < 1 || seqlen < vsa::BLOCK || region < VSA_WS_LSE_DELTA || region > VSA_WS_END)
+size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
+                                int region) {
+  if (batch < 1 || heads < 1 || seqlen < vsa::BLOCK || q2k_stride < 0 ||
+      (dq_mode != VSA_DQ_RECOMPUTE && dq_mode != VSA_DQ_SPILL) || region < VSA_WS_LSE_DELTA ||
+      region > VSA_WS_END)
     return 0;
   const size_t bh = (size_t)batch * (size_t)heads;
   const size_t nb = (size_t)seqlen / vsa::BLOCK;
+  const bool derive = q2k_stride == 0;
+  const bool spill = dq_mode == VSA_DQ_SPILL;
+  const size_t kq = derive ? nb : (size_t)q2k_stride;  // q2k row width
   const size_t sizes[VSA_WS_END] = {
       align256(bh * (size_t)seqlen * 2 * sizeof(float)),                      // lse, Delta
       align256(bh * nb * sizeof(int32_t)),                                    // kv order
       align256(bh * nb * sizeof(int32_t)),                                    // q order
-      align256(bh * nb * sizeof(int32_t)),                                    // q2k_num
-      align256(bh * nb * nb * sizeof(int32_t)),                               // q2k_idx
-      align256(vsa::invert_bitmap_bytes((int)bh, (int)nb, (int)nb)),          // bitmap
+      derive ? align256(bh * nb * sizeof(int32_t)) : 0,                       // q2k_num
+      derive ? align256(bh * nb * nb * sizeof(int32_t)) : 0,                  // q2k_idx
+      derive ? align256(vsa::invert_bitmap_bytes((int)bh, (int)nb, (int)nb)) : 0,  // bitmap
+      spill ? align256(bh * nb * sizeof(int32_t)) : 0,                        // kbase
+      spill ? align256(bh * nb * kq * sizeof(int64_t)) : 0,                   // qent
+      spill ? align256(bh * nb * kq * (size_t)(vsa::BLOCK * vsa::BLOCK) * 2) : 0,  // dS tiles
   };
   size_t off = 0;
   for (int r = 0; r < region; ++r) off += sizes[r];
   return off;
 }
 
-size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int derive_q2k) {
-  return vsa_bwd_workspace_offset(batch, heads, seqlen, derive_q2k ? VSA_WS_END : VSA_WS_Q2K_NUM);
+size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int q2k_stride, int dq_mode) {
+  return vsa_bwd_workspace_offset(batch, heads, seqlen, q2k_stride, dq_mode, VSA_WS_END);
 }
 
 int vsa_bwd_check(const vsa_bwd_args* a) {
@@ -184,7 +193,19 @@ int vsa_bwd_check(const vsa_bwd_args* a) {
     return fail(VSA_EINVAL, "vsa_bwd: q2k_stride must be >= 1 when q2k lists are given");
   if (!a->dq || !a->dk || !a->dv) return fail(VSA_EINVAL, "vsa_bwd: null output pointer");
   if (!a->workspace) return fail(VSA_EINVAL, "vsa_bwd: null workspace");
-  const size_t need = vsa_bwd_workspace_bytes(a->batch, a->heads, a->seqlen, a->q2k_idx == nullptr);
+  if (a->dq_mode != VSA_DQ_RECOMPUTE && a->dq_mode != VSA_DQ_SPILL)
+    return fail(VSA_EINVAL, "vsa_bwd: dq_mode must be VSA_DQ_RECOMPUTE or VSA_DQ_SPILL, got " +
+                                std::to_string(a->dq_mode));
+  if (a->dq_mode == VSA_DQ_SPILL) {
+    const long long kq = a->q2k_idx ? a->q2k_stride : a->num_kv_blocks;
+    if (a->num_kv_blocks > 65535)
+      return fail(VSA_EUNSUPPORTED, "vsa_bwd: VSA_DQ_SPILL supports at most 65535 kv blocks");
+    if ((long long)a->num_kv_blocks * kq >= (1LL << 31))
+      return fail(VSA_EUNSUPPORTED, "vsa_bwd: VSA_DQ_SPILL needs num_kv_blocks * q2k row width "
+                                    "below 2^31");
+  }
+  const size_t need = vsa_bwd_workspace_bytes(a->batch, a->heads, a->seqlen,
+                                              a->q2k_idx ? a->q2k_stride : 0, a->dq_mode);
   if (a->workspace_bytes < need)
     return fail(VSA_EINVAL, "vsa_bwd: workspace of " + std::to_string(a->workspace_bytes) +
                                 " bytes, need " + std::to_string(need));
@@ -219,14 +240,22 @@ struct WsView {
   int32_t* q2k_num;
   int32_t* q2k_idx;
   uint32_t* bitmap;
+  int32_t* kbase;
+  int64_t* qent;
+  vsa::bf16* ds;
 };
 
 WsView ws_view(const vsa_bwd_args* a) {
   char* ws = (char*)a->workspace;
-  auto at = [&](int r) { return ws + vsa_bwd_workspace_offset(a->batch, a->heads, a->seqlen, r); };
-  return WsView{(float*)at(VSA_WS_LSE_DELTA), (int32_t*)at(VSA_WS_KV_ORDER), (int32_t*)at(VSA_WS_Q_ORDER),
-                (int32_t*)at(VSA_WS_Q2K_NUM), (int32_t*)at(VSA_WS_Q2K_IDX),
-                (uint32_t*)at(VSA_WS_BITMAP)};
+  const int kq = a->q2k_idx ? a->q2k_stride : 0;
+  auto at = [&](int r) {
+    return ws + vsa_bwd_workspace_offset(a->batch, a->heads, a->seqlen, kq, a->dq_mode, r);
+  };
+  return WsView{(float*)at(VSA_WS_LSE_DELTA), (int32_t*)at(VSA_WS_KV_ORDER),
+                (int32_t*)at(VSA_WS_Q_ORDER),  (int32_t*)at(VSA_WS_Q2K_NUM),
+                (int32_t*)at(VSA_WS_Q2K_IDX),  (uint32_t*)at(VSA_WS_BITMAP),
+                (int32_t*)at(VSA_WS_KBASE),    (int64_t*)at(VSA_WS_QENT),
+                (vsa::bf16*)at(VSA_WS_DS)};
 }
 
 vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
@@ -252,6 +281,12 @@ vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
   m.nb = a->num_kv_blocks;
   m.k2q_stride = a->max_q_blocks;
   m.q2k_stride = derive ? a->num_kv_blocks : a->q2k_stride;
+  const bool spill = a->dq_mode == VSA_DQ_SPILL;
+  m.kbase = spill ? ws.kbase : nullptr;
+  m.qent = spill ? ws.qent : nullptr;
+  m.ds = spill ? ws.ds : nullptr;
+  m.qent_stride = m.q2k_stride;
+  m.cap = spill ? a->num_kv_blocks * m.q2k_stride : 0;
   m.total_items = a->batch * a->heads * a->num_kv_blocks;
   m.items_per_xcd = (m.total_items + 7) / 8;
   m.sm_scale = a->sm_scale;
@@ -297,7 +332,18 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
         }
         vsa::launch_bwd_order(derive ? ws.q2k_num : a->q2k_num, BH, nb, VSA_ORDER_BIN_WIDTH,
                               ws.q_order, s);
-        return launch_status("vsa_bwd q order");
+        const int r = launch_status("vsa_bwd q order");
+        if (r != VSA_OK) return r;
+      }
+      if (a->dq_mode == VSA_DQ_SPILL) {
+        const vsa::BwdParams m = main_params(a, ws);
+        vsa::launch_spill_kbase(a->k2q_num, BH, nb, a->max_q_blocks, ws.kbase, s);
+        int r = launch_status("vsa_bwd dS slot bases");
+        if (r != VSA_OK) return r;
+        vsa::launch_spill_qent(m.q2k_idx, m.q2k_num, m.q2k_stride, a->k2q_idx, a->k2q_num,
+                               a->max_q_blocks, ws.kbase, a->vbs, BH, nb, m.cap, ws.qent, s);
+        r = launch_status("vsa_bwd dS slot table");
+        if (r != VSA_OK) return r;
       }
       return VSA_OK;
     }
@@ -305,7 +351,10 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       vsa::launch_bwd_dkdv(main_params(a, ws), s);
       return launch_status("vsa_bwd dk/dv kernel");
     case VSA_BWD_DQ:
-      vsa::launch_bwd_dq(main_params(a, ws), s);
+      if (a->dq_mode == VSA_DQ_SPILL)
+        vsa::launch_bwd_dq_spill(main_params(a, ws), s);
+      else
+        vsa::launch_bwd_dq(main_params(a, ws), s);
       return launch_status("vsa_bwd dq kernel");
     default:
       return fail(VSA_EINVAL, "vsa_bwd_stage: unknown stage " + std::to_string(stage));

@@ -224,6 +224,25 @@ __device__ __forceinline__ void dma_tile(const void* ga, const uint32_t* off, ui
       : "memory");
 }
 
+// Two consecutive 1-KiB DMAs of contiguous bytes: lane l copies g + voff (+1024) to LDS
+// lds + 16 * l (+1024); voff is normally 16 * lane. Two vector memory operations, non-temporal
+// (for data read exactly once).
+__device__ __forceinline__ void dma_lin2_nt(const void* g, uint32_t voff, uint32_t lds) {
+  const uint64_t a = uniform_u64(g);
+  const uint32_t la = uniform_u32(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:1024 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(a), "s"(la)
+      : "memory");
+}
+
 // 128 bytes of a small record: lanes 0..7 copy rec + roff to LDS lds_r + 16 * lane, with EXEC
 // narrowed to them inside the asm block. One vector memory operation.
 __device__ __forceinline__ void dma_rec128(const void* rec, uint32_t roff, uint32_t lds_r) {

@@ -74,10 +74,27 @@ struct BwdParams {
   bf16* dq;
   bf16* dk;
   bf16* dv;
+  // dS spill (nullptr ds: recompute mode): slot tables from the index stage and the tiles
+  const int32_t* kbase;  // [BH*nb]: first slot of each kv block's pairs inside its head
+  const int64_t* qent;   // [BH*nb, qent_stride]: slot | kv << 32 | vbs[kv] << 48
+  bf16* ds;              // [BH, cap, 64*64]
+  int cap, qent_stride;  // slots per head (nb * K'), q2k row width K'
   int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
   float scale_log2, sm_scale;
 };
 void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 void launch_bwd_dq(const BwdParams& p, hipStream_t stream);
+void launch_bwd_dq_spill(const BwdParams& p, hipStream_t stream);
+
+// ---- dS slot tables (spill mode) ----
+// kbase[bh, kv] = sum of min(max(k2q_num, 0), k2q_stride) over the kv blocks before kv in head bh.
+void launch_spill_kbase(const int32_t* k2q_num, int BH, int nb, int k2q_stride, int32_t* kbase,
+                        hipStream_t stream);
+// qent[bh, q, s] for s < q2k_num[bh, q]: the slot of pair (q, kv = q2k_idx[bh, q, s]), i.e.
+// kbase[bh, kv] + (position of q in the ascending k2q row of kv), packed with kv and vbs[kv].
+void launch_spill_qent(const int32_t* q2k_idx, const int32_t* q2k_num, int q2k_stride,
+                       const int32_t* k2q_idx, const int32_t* k2q_num, int k2q_stride,
+                       const int32_t* kbase, const int32_t* vbs, int BH, int nb, int cap,
+                       int64_t* qent, hipStream_t stream);
 
 }  // namespace vsa

@@ -91,8 +91,16 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *
  * The main step runs as two kernels without atomics: a kv-major one (one work item per
  * (b, h, kv block), walking the k2q list) for dk and dv, and a q-major one (one item per
- * (b, h, q block), walking the q2k list) for dq, which recomputes the scores. All three outputs
- * are bitwise reproducible run to run, whatever the work order.
+ * (b, h, q block), walking the q2k list) for dq. All three outputs are bitwise reproducible run
+ * to run, whatever the work order. The q-major kernel gets dS in one of two ways (dq_mode):
+ *   VSA_DQ_RECOMPUTE  it recomputes S and dP for each pair from Q, K, V, dO, lse and Delta
+ *                     (three GEMMs per pair, no extra memory);
+ *   VSA_DQ_SPILL      the kv-major kernel writes every pair's dS (bf16, the same values its dK
+ *                     GEMM uses) into the workspace and dq is one block-sparse GEMM dS K per
+ *                     pair, reading 8 KiB of dS per pair from HBM. This needs 8 KiB of workspace
+ *                     per possible pair (B*H*nb*q2k_stride of them, nb*nb when q2k is derived)
+ *                     and k2q rows in ascending order (as vsa_invert_indices writes them); it
+ *                     supports num_kv_blocks <= 65535.
  *
  * q2k lists (optional): the forward's q2k_idx [B, H, num_kv_blocks, q2k_stride] / q2k_num, which
  * must describe the same selection as k2q (each pair once). NULL: the library derives them from
@@ -110,15 +118,23 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  * any order.
  *
  * Workspace (device, vsa_bwd_workspace_bytes() bytes, contents on entry irrelevant), regions in
- * this order, each at a 256-byte boundary (vsa_bwd_workspace_offset() gives the offsets):
- *   VSA_WS_LSE_DELTA fp32 [B, H, nb, 2, 64]: per q block, its 64 lse values (a copy of `lse`)
- *                    then its 64 Delta values (left holding them after the call)
+ * this order, each at a 256-byte boundary (vsa_bwd_workspace_offset() gives the offsets); a
+ * region the call does not use has size 0. K' below is q2k_stride, or nb when q2k is derived.
+ *   VSA_WS_LSE_DELTA fp32 [B, H, nb, 2, 64]: per q block, -lse / scale_log2 of its 64 rows
+ *                    (scale_log2 = fp32(sm_scale * log2 e)), then -Delta of its 64 rows; left
+ *                    holding them after the call
  *   VSA_WS_KV_ORDER  int32 [B*H*nb] kv-major work order (when the library computes it)
  *   VSA_WS_Q_ORDER   int32 [B*H*nb] q-major work order (when the library computes it)
- * and only when the q2k lists are derived (derive_q2k != 0):
+ * only when the q2k lists are derived (q2k_stride argument 0):
  *   VSA_WS_Q2K_NUM   int32 [B, H, nb]
  *   VSA_WS_Q2K_IDX   int32 [B, H, nb, nb]
- *   VSA_WS_BITMAP    the inversion's bitmap */
+ *   VSA_WS_BITMAP    the inversion's bitmap
+ * only in VSA_DQ_SPILL mode:
+ *   VSA_WS_KBASE     int32 [B, H, nb]: per kv block, the first dS slot of its head's pairs
+ *                    (exclusive prefix sum of k2q_num inside the head)
+ *   VSA_WS_QENT      int64 [B, H, nb, K']: per q2k entry, its dS slot | kv block << 32 |
+ *                    vbs[kv block] << 48
+ *   VSA_WS_DS        bf16 [B, H, nb*K', 64, 64]: the dS tiles, slot-major */
 #define VSA_ORDER_MIN_KV_BLOCKS 64
 #define VSA_ORDER_BIN_WIDTH 4
 #define VSA_ORDER_MAX_KV_BLOCKS 16384
@@ -130,8 +146,13 @@ typedef enum {
   VSA_WS_Q2K_NUM = 3,
   VSA_WS_Q2K_IDX = 4,
   VSA_WS_BITMAP = 5,
-  VSA_WS_END = 6
+  VSA_WS_KBASE = 6,
+  VSA_WS_QENT = 7,
+  VSA_WS_DS = 8,
+  VSA_WS_END = 9
 } vsa_bwd_ws_region;
+
+typedef enum { VSA_DQ_RECOMPUTE = 0, VSA_DQ_SPILL = 1 } vsa_dq_mode;
 
 typedef struct {
   const void* q;          /* bf16 [B, H, S, 128] */
@@ -153,12 +174,17 @@ typedef struct {
   size_t workspace_bytes;
   int batch, heads, seqlen, head_dim, num_kv_blocks, max_q_blocks, q2k_stride;
   float sm_scale;
+  int dq_mode;            /* vsa_dq_mode */
 } vsa_bwd_args;
 
-/* Bytes of workspace for a backward call; derive_q2k != 0 when q2k_idx/q2k_num are NULL. */
-size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int derive_q2k);
-/* Byte offset of a workspace region (vsa_bwd_ws_region); VSA_WS_END is the derive_q2k size. */
-size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int region);
+/* Bytes of workspace for a backward call. q2k_stride: the row width of the q2k lists the call
+ * passes, or 0 when q2k_idx/q2k_num are NULL (derived); dq_mode: a vsa_dq_mode. 0 for an invalid
+ * shape. */
+size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int q2k_stride, int dq_mode);
+/* Byte offset of a workspace region (vsa_bwd_ws_region) for the same arguments; VSA_WS_END gives
+ * the total. */
+size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
+                                int region);
 /* Host-only validation of a backward call; reads no device memory. */
 int vsa_bwd_check(const vsa_bwd_args* a);
 int vsa_bwd(const vsa_bwd_args* a, void* stream);
@@ -166,13 +192,16 @@ int vsa_bwd(const vsa_bwd_args* a, void* stream);
 /* The backward's stages one at a time, for callers that time or interleave them. Each call
  * validates like vsa_bwd. Run on one stream in the order PREPROCESS, INDEX, DKDV, DQ, they
  * enqueue exactly the kernels vsa_bwd enqueues and produce the same results. INDEX derives the
- * q2k lists when they are not given and computes the work orders when num_kv_blocks is in
- * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS]; otherwise it enqueues nothing. DKDV and DQ
- * only read what PREPROCESS and INDEX wrote, so they may run in either order. */
+ * q2k lists when they are not given, computes the work orders when num_kv_blocks is in
+ * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS] and builds the dS slot tables in
+ * VSA_DQ_SPILL mode; otherwise it enqueues nothing. In VSA_DQ_RECOMPUTE mode DKDV and DQ only read
+ * what PREPROCESS and INDEX wrote and may run in either order; in VSA_DQ_SPILL mode DQ reads the
+ * dS tiles DKDV writes and must follow it. */
 typedef enum {
   VSA_BWD_PREPROCESS = 0,  /* Delta; zero dk/dv rows of kv blocks with an empty k2q list */
-  VSA_BWD_INDEX = 1,       /* q2k derivation (if needed) and the length-binned work orders */
-  VSA_BWD_DKDV = 2,        /* kv-major kernel: dk, dv */
+  VSA_BWD_INDEX = 1,       /* q2k derivation (if needed), the length-binned work orders and,
+                              in VSA_DQ_SPILL mode, the dS slot tables */
+  VSA_BWD_DKDV = 2,        /* kv-major kernel: dk, dv (and the dS tiles in VSA_DQ_SPILL mode) */
   VSA_BWD_DQ = 3           /* q-major kernel: dq = bf16(sm_scale * dS K) */
 } vsa_bwd_stage_id;
 int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream);

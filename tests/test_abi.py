@@ -51,6 +51,7 @@ def test_status_strings():
 def test_workspace_sizes_and_layout():
     B, H, S = 1, 8, 32768
     nb = S // 64
+    # derived q2k, recompute mode
     offs = [V.bwd_workspace_offset(B, H, S, r) for r in range(V.WS_END + 1)]
     assert offs[V.WS_LSE_DELTA] == 0
     assert offs[V.WS_KV_ORDER] == B * H * S * 2 * 4
@@ -58,12 +59,29 @@ def test_workspace_sizes_and_layout():
     assert offs[V.WS_Q2K_NUM] == offs[V.WS_Q_ORDER] + B * H * nb * 4
     assert offs[V.WS_Q2K_IDX] == offs[V.WS_Q2K_NUM] + B * H * nb * 4
     assert offs[V.WS_BITMAP] == offs[V.WS_Q2K_IDX] + B * H * nb * nb * 4
-    assert offs[V.WS_END] == offs[V.WS_BITMAP] + B * H * nb * ((nb + 31) // 32) * 4
-    assert V.bwd_workspace_bytes(B, H, S, False) == offs[V.WS_Q2K_NUM]
-    assert V.bwd_workspace_bytes(B, H, S, True) == offs[V.WS_END]
+    assert offs[V.WS_KBASE] == offs[V.WS_BITMAP] + B * H * nb * ((nb + 31) // 32) * 4
+    assert offs[V.WS_KBASE] == offs[V.WS_QENT] == offs[V.WS_DS] == offs[V.WS_END]
+    assert V.bwd_workspace_bytes(B, H, S) == offs[V.WS_END]
+    # given q2k lists (row width 128): no derivation regions
+    given = [V.bwd_workspace_offset(B, H, S, r, 128) for r in range(V.WS_END + 1)]
+    assert given[V.WS_Q2K_NUM] == given[V.WS_END] == offs[V.WS_Q2K_NUM]
+    assert V.bwd_workspace_bytes(B, H, S, 128) == offs[V.WS_Q2K_NUM]
+    # spill mode: slot bases, the slot table and one 8 KiB dS tile per possible pair
+    sp = [V.bwd_workspace_offset(B, H, S, r, 128, V.DQ_SPILL) for r in range(V.WS_END + 1)]
+    assert sp[V.WS_KBASE] == offs[V.WS_Q2K_NUM]
+    assert sp[V.WS_QENT] == sp[V.WS_KBASE] + B * H * nb * 4
+    assert sp[V.WS_DS] == sp[V.WS_QENT] + B * H * nb * 128 * 8
+    assert sp[V.WS_END] == sp[V.WS_DS] + B * H * nb * 128 * 64 * 64 * 2
+    # derived q2k in spill mode: row width nb for the slot table and tiles
+    spd = [V.bwd_workspace_offset(1, 2, 64 * 5, r, 0, V.DQ_SPILL) for r in range(V.WS_END + 1)]
+    assert spd[V.WS_END] - spd[V.WS_DS] == 2 * 5 * 5 * 8192
     # every region starts on a 256-byte boundary, also for odd sizes
-    assert all(V.bwd_workspace_offset(1, 3, 64 * 5, r) % 256 == 0 for r in range(V.WS_END + 1))
+    for kq in (0, 3):
+        for mode in (V.DQ_RECOMPUTE, V.DQ_SPILL):
+            assert all(V.bwd_workspace_offset(1, 3, 64 * 5, r, kq, mode) % 256 == 0
+                       for r in range(V.WS_END + 1))
     assert V.bwd_workspace_bytes(0, 1, 64) == 0
+    assert V.bwd_workspace_bytes(1, 1, 64, 0, 7) == 0  # unknown mode
     assert V.invert_workspace_bytes(2, 3, 100, 50) == ((2 * 3 * 50 * 4 * 4 + 255) // 256) * 256
     assert V.invert_workspace_bytes(1, 1, 0, 1) == 0
 
@@ -72,9 +90,9 @@ def _bwd_args(**over):
     fake = 0x10000  # never dereferenced: validation fails or we do not launch
     a = dict(q=fake, k=fake, v=fake, o=fake, dout=fake, lse=fake, k2q_idx=fake, k2q_num=fake,
              q2k_idx=None, q2k_num=None, vbs=fake, order=None, dq=fake, dk=fake, dv=fake,
-             workspace=fake, workspace_bytes=V.bwd_workspace_bytes(1, 2, 256, True), batch=1,
+             workspace=fake, workspace_bytes=V.bwd_workspace_bytes(1, 2, 256), batch=1,
              heads=2, seqlen=256, head_dim=128, num_kv_blocks=4, max_q_blocks=4, q2k_stride=0,
-             sm_scale=0.088)
+             sm_scale=0.088, dq_mode=V.DQ_RECOMPUTE)
     a.update(over)
     return V._BwdArgs(**a)
 
@@ -87,12 +105,19 @@ def test_bwd_check_accepts_a_valid_call():
     assert _check(_bwd_args()) == VSA_OK
     # odd block counts are fine
     assert _check(_bwd_args(num_kv_blocks=3, seqlen=192,
-                            workspace_bytes=V.bwd_workspace_bytes(1, 2, 192, True))) == VSA_OK
+                            workspace_bytes=V.bwd_workspace_bytes(1, 2, 192))) == VSA_OK
     # given q2k lists need less workspace
-    small = V.bwd_workspace_bytes(1, 2, 256, False)
+    small = V.bwd_workspace_bytes(1, 2, 256, 2)
     assert _check(_bwd_args(q2k_idx=0x10000, q2k_num=0x10000, q2k_stride=2,
                             workspace_bytes=small)) == VSA_OK
     assert _check(_bwd_args(workspace_bytes=small)) == VSA_EINVAL
+    # the dS spill needs its tiles' room
+    spill = V.bwd_workspace_bytes(1, 2, 256, 2, V.DQ_SPILL)
+    assert _check(_bwd_args(q2k_idx=0x10000, q2k_num=0x10000, q2k_stride=2, workspace_bytes=spill,
+                            dq_mode=V.DQ_SPILL)) == VSA_OK
+    assert _check(_bwd_args(q2k_idx=0x10000, q2k_num=0x10000, q2k_stride=2, workspace_bytes=small,
+                            dq_mode=V.DQ_SPILL)) == VSA_EINVAL
+    assert _check(_bwd_args(dq_mode=2)) == VSA_EINVAL
 
 
 @pytest.mark.parametrize("over,status", [

@@ -189,7 +189,10 @@ def test_forward_parity(n):
 # backward on small workloads, o and lse from the oracle (as the FastVideo test does)
 # -----------------------------------------------------------------------------------------------
 
-def _bwd_small(c, label):
+MODES = {"recompute": V.DQ_RECOMPUTE, "spill": V.DQ_SPILL}
+
+
+def _bwd_small(c, label, mode=V.DQ_RECOMPUTE):
     d = to_dev(c)
     ro, rl = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
     o = torch.from_numpy(O.bf16_rne(ro)).to(torch.bfloat16).to(DEV)
@@ -197,21 +200,28 @@ def _bwd_small(c, label):
     ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
     k2q_idx = torch.from_numpy(ridx).to(DEV)
     k2q_num = torch.from_numpy(rnum).to(DEV)
-    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S, True),), 0xFF, dtype=torch.uint8,
+    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S, 0, mode),), 0xFF, dtype=torch.uint8,
                     device=DEV)
     out = (nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"]))
-    say(f"[backward] {label} (q2k derived from k2q)")
+    say(f"[backward] {label} (q2k derived from k2q, dq mode {mode})")
     plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
-                     workspace=ws, out=out)
+                     workspace=ws, out=out, dq_mode=mode)
     dq, dk, dv = plan.run()
     torch.cuda.synchronize()
     # the same call with the forward's q2k lists given: bit-identical results
     say(f"[backward] {label} (q2k given)")
     given = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num,
-                                d["vbs"], q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"])
+                                d["vbs"], q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"],
+                                dq_mode=mode)
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv), given):
         assert torch.equal(a, b)
+    if mode == V.DQ_SPILL:
+        # dk, dv come from the same kernel arithmetic in both modes: identical bits
+        other = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num,
+                                    d["vbs"], dq_mode=V.DQ_RECOMPUTE)
+        torch.cuda.synchronize()
+        assert torch.equal(dk, other[1]) and torch.equal(dv, other[2])
     rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
     for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
         assert got.dtype == torch.bfloat16
@@ -228,10 +238,11 @@ def _bwd_small(c, label):
     return dq, dk, dv, rdq, rdk, rdv
 
 
+@pytest.mark.parametrize("mode", sorted(MODES))
 @pytest.mark.parametrize("n", [1, 2])
-def test_backward_parity(n):
+def test_backward_parity(n, mode):
     c = workloads.config(n)
-    dq, dk, dv, *_ = _bwd_small(c, f"config {n}")
+    dq, dk, dv, *_ = _bwd_small(c, f"config {n}", MODES[mode])
     if n == 2:
         dk, dv = dk.float().cpu(), dv.float().cpu()
         for kb in (4, 11):  # selected by no q block
@@ -254,8 +265,9 @@ EDGE_CASES = {
 }
 
 
+@pytest.mark.parametrize("mode", sorted(MODES))
 @pytest.mark.parametrize("name", sorted(EDGE_CASES))
-def test_backward_edge_cases(name):
+def test_backward_edge_cases(name, mode):
     B, H, nb, topk, vbs, pool, empty = EDGE_CASES[name]
     c = workloads.make_case(B, H, nb, topk, seed=17, vbs=vbs, kv_pool=pool, name=name)
     for b, h, qb in empty:
@@ -266,24 +278,26 @@ def test_backward_edge_cases(name):
     o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
     torch.cuda.synchronize()
     _fwd_compare(c, d, o, lse)
-    dq, dk, dv, rdq, rdk, rdv = _bwd_small(c, f"edge case {name}")
+    dq, dk, dv, rdq, rdk, rdv = _bwd_small(c, f"edge case {name}", MODES[mode])
     # exact zeros wherever the oracle is exactly zero (unselected, padded, empty rows)
     for got, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
         zero = ref == 0
         assert np.all(got.float().cpu().numpy()[zero] == 0)
 
 
-def test_backward_any_order_gives_identical_bits():
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_backward_any_order_gives_identical_bits(mode):
     """Any kv work order: the same dq, dk, dv bits (fixed per-item summation order, no atomics)."""
     c = workloads.config(2)
     d = to_dev(c)
     o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
     k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
-    say("[backward] identity vs reversed order")
-    a = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"])
+    say(f"[backward] identity vs reversed order ({mode})")
+    a = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                            dq_mode=MODES[mode])
     rev = torch.arange(c.B * c.H * c.nb - 1, -1, -1, dtype=torch.int32, device=DEV)
     b = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
-                            order=rev)
+                            order=rev, dq_mode=MODES[mode])
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
@@ -297,7 +311,7 @@ def test_nondefault_stream():
     with torch.cuda.stream(s):
         o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
         dq, dk, dv = V.backward(d["do"], d["q"], d["k"], d["v"], o, lse, d["q2k_idx"],
-                                d["q2k_num"], d["vbs"])
+                                d["q2k_num"], d["vbs"], dq_mode=V.DQ_SPILL)
     s.synchronize()
     rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
     check_close("dq", dq, rdq)
@@ -309,18 +323,20 @@ def test_nondefault_stream():
 # full-size workloads: sampled blocks + invariants
 # -----------------------------------------------------------------------------------------------
 
-def _end_to_end(c):
+def _end_to_end(c, mode=V.DQ_RECOMPUTE, give_q2k=False):
     """GPU forward -> GPU invert -> GPU backward, outputs and workspace NaN-prefilled."""
     d = to_dev(c)
     o = nan_like(d["q"])
     lse = nan_like(torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=DEV))
     V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"], out=(o, lse))
     k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
-    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S, True),), 0xFF, dtype=torch.uint8,
+    kq = d["q2k_idx"].shape[-1] if give_q2k else 0
+    ws = torch.full((V.bwd_workspace_bytes(c.B, c.H, c.S, kq, mode),), 0xFF, dtype=torch.uint8,
                     device=DEV)
     out = (nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"]))
+    extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"]) if give_q2k else {}
     plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
-                     workspace=ws, out=out)
+                     workspace=ws, out=out, dq_mode=mode, **extra)
     dq, dk, dv = plan.run()
     torch.cuda.synchronize()
     return d, o, lse, (k2q_idx, k2q_num), plan, (dq, dk, dv)
@@ -356,8 +372,8 @@ def _invariants(c, grads):
 
 def test_config3_32k_end_to_end_sampled():
     c = workloads.config(3)
-    say("[end-to-end] config 3 (B=1 H=8 S=32768, 25%)")
-    d, o, lse, (k2q_idx, k2q_num), plan, grads = _end_to_end(c)
+    say("[end-to-end] config 3 (B=1 H=8 S=32768, 25%, dS spill, q2k given)")
+    d, o, lse, (k2q_idx, k2q_num), plan, grads = _end_to_end(c, V.DQ_SPILL, give_q2k=True)
     # 512 kv blocks: the library computed the length-binned kv-major order into the workspace
     n = c.B * c.H * c.nb
     assert np.array_equal(plan.region(V.WS_KV_ORDER, n).cpu().numpy(),
@@ -390,6 +406,20 @@ def test_config4_65k_order_stability_sampled():
     dq, dk, dv = grads
     _sampled_checks(c, o, lse, grads, qblocks=[(0, 1, 7), (0, 6, 1023)],
                     kvblocks=[(0, 2, 0), (0, 7, 777)])
+    del plan, again
+    # the dS spill with the forward's q2k lists: the same dk, dv bits, dq on samples, and
+    # run-to-run identical
+    say("[end-to-end] config 4, dS spill")
+    sp = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                   q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"], dq_mode=V.DQ_SPILL)
+    g2 = tuple(t.clone() for t in sp.run())
+    torch.cuda.synchronize()
+    assert torch.equal(g2[1], dk) and torch.equal(g2[2], dv)
+    g3 = sp.run()
+    torch.cuda.synchronize()
+    for x, y in zip(g2, g3):
+        assert torch.equal(x, y)
+    _sampled_checks(c, o, lse, g2, qblocks=[(0, 1, 7), (0, 6, 1023)], kvblocks=[])
 
 
 def _head(c, h):
