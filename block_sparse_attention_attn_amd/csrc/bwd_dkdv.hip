@@ -160,6 +160,7 @@ bwd_dkdv_kernel(BwdParams p) {
   // K/V and q blocks 0, 1 landed (own DMAs); q block 2's may still be in flight
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
   barrier_lds_with(e3);  // ... everyone's
+  int raw = entry(4);    // the list entry step 0 fetches; in by step 0's barrier
 
   // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
   const int kv_l = 32 * wk + l32;
@@ -301,9 +302,14 @@ bwd_dkdv_kernel(BwdParams p) {
     // q block, into a stage nobody reads again), so the group of t+3 is always the newest and
     // nine outstanding operations mean q block t+2 has landed. No branch splits the step.
     // (In spill mode the two dS stores of step t-1 sit between the groups of t+2 and t+3.)
-    const int raw = entry(t + 4);
+    // The list entry of q block t+4 was loaded after the previous barrier; the compiler-visible
+    // lgkmcnt(0) tells the compiler that every LDS read issued so far is complete, so the scalar
+    // load issued below for the next step adds no wait for them.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
+    const int qb = clampq(raw);
+    raw = entry(t + 5);     // in by the next step's barrier
 
     // ---- phase C ----
     // dV/dK MFMAs of t. Record and row reads of q block t+2 (records first: they seed the first
@@ -316,7 +322,6 @@ bwd_dkdv_kernel(BwdParams p) {
       __builtin_nontemporal_store(sa[1], (bf16x8*)(d + 16));
     }
     {
-      const int qb = clampq(raw);
       const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
       load_init(st2, sc, pc);
       dma_rec128(recs + (size_t)qb * LD_RECORD_FLOATS, roff, ld_lds + st * LD_BYTES);

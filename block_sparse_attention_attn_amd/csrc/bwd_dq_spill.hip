@@ -14,9 +14,10 @@
 // gfx950 design: one 256-thread workgroup per q block, walking its slot-table row (VSA_WS_QENT:
 // dS slot, kv block and vbs per entry). Wave w computes dQ^T rows d = 32w .. 32w+31 for both q
 // halves: dQ^T += K^T dS^T with v_mfma_f32_32x32x16_bf16, four k-steps of 16 kv per pair. K_j
-// (16 KiB) and the dS tile (8 KiB) of each pair arrive by global_load_lds_dwordx4 into a
-// six-stage LDS ring, issued four pairs ahead of the step that reads them; both operands come
-// out of LDS through ds_read_b64_tr_b16, one pair ahead of their MFMAs. A pair of a ragged kv
+// (16 KiB) and the dS tile (8 KiB) of each pair arrive by global_load_lds_dwordx4 into two LDS
+// rings: dS, streamed from HBM, is fetched six steps before it is read; K, mostly L2 hits, two
+// steps before. Both operands come out of LDS through ds_read_b64_tr_b16, one pair ahead of
+// their MFMAs. A pair of a ragged kv
 // block has its padded kv slots masked to zero in both operands (so neither stale K rows nor the
 // dS values of masked keys can reach dQ).
 #include "vsa_device.h"
@@ -26,10 +27,14 @@ namespace vsa {
 
 namespace {
 
-constexpr int STAGES = 6;
+// Two rings: dS tiles come from HBM and are fetched eight pairs ahead (SD stages), K tiles are
+// mostly L2 hits and are fetched four pairs ahead (SK stages). 8 x 8 KiB + 4 x 16 KiB = 128 KiB.
+constexpr int SD = 8;
+constexpr int SK = 4;
 constexpr int K_BYTES = 16384;  // one [64][128] bf16 K tile, swizzled
 constexpr int S_BYTES = 8192;   // one dS tile, as the kv-major kernel stored it
-constexpr int DMA_PER_PAIR = 6; // per wave: four 1-KiB slices of K, two of dS
+constexpr int DMA_K = 4;        // per wave per pair: four 1-KiB slices of K
+constexpr int DMA_S = 2;        // ... and two of dS
 
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -43,8 +48,8 @@ __device__ __forceinline__ void barrier_lds_with(uint64_t v) {
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dq_spill_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char s_ring[STAGES * S_BYTES];
-  __shared__ __attribute__((aligned(1024))) char k_ring[STAGES * K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char s_ring[SD * S_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_ring[SK * K_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -88,9 +93,11 @@ bwd_dq_spill_kernel(BwdParams p) {
   const uint32_t k_lds = lds_addr((VSA_LDS char*)k_ring) + 4096 * w;
   const uint32_t s_lds = lds_addr((VSA_LDS char*)s_ring) + 2048 * w;
   const uint32_t s_off = 16 * lane;
-  auto issue = [&](uint64_t e, int st) __attribute__((always_inline)) {
-    dma_tile(kh_ptr + (size_t)kv_of(e) * BLOCK * HEAD_DIM, toff, k_lds + st * K_BYTES);
-    dma_lin2_nt(ds_head + (size_t)slot_of(e) * S_BYTES + 2048 * w, s_off, s_lds + st * S_BYTES);
+  auto issue_k = [&](uint64_t e, int sk) __attribute__((always_inline)) {
+    dma_tile(kh_ptr + (size_t)kv_of(e) * BLOCK * HEAD_DIM, toff, k_lds + sk * K_BYTES);
+  };
+  auto issue_s = [&](uint64_t e, int sd) __attribute__((always_inline)) {
+    dma_lin2_nt(ds_head + (size_t)slot_of(e) * S_BYTES + 2048 * w, s_off, s_lds + sd * S_BYTES);
   };
 
   // Operands of one pair. A = K^T: lane holds d = 32w + lane%32 and kv 16ks + 8kh + j. B = dS^T
@@ -100,9 +107,9 @@ bwd_dq_spill_kernel(BwdParams p) {
     bf16x8 a[4];
     bf16x8 b[2][4];
   };
-  auto read_ops = [&](int st, Ops& o) __attribute__((always_inline)) {
-    VSA_LDS char* kt = (VSA_LDS char*)k_ring + st * K_BYTES;
-    VSA_LDS char* sb = (VSA_LDS char*)s_ring + st * S_BYTES;
+  auto read_ops = [&](int sk, int sd, Ops& o) __attribute__((always_inline)) {
+    VSA_LDS char* kt = (VSA_LDS char*)k_ring + sk * K_BYTES;
+    VSA_LDS char* sb = (VSA_LDS char*)s_ring + sd * S_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int k0 = 16 * ks + 8 * kh;  // first kv of this lane's k slots
@@ -150,26 +157,44 @@ bwd_dq_spill_kernel(BwdParams p) {
     }
   };
 
-  // ---- prologue: pairs 0..5 into stages 0..5 (past the end of the list: repeats) ----
-  uint64_t er[STAGES];
+  // ---- prologue ----
+  // Pair u's K goes to k stage u % SK, its dS to s stage u % SD (past the end of the list:
+  // repeats of the last pair). In the steady state the barrier of step u frees both stages of
+  // pair u and step u then issues K of pair u+4 and dS of pair u+8, in that order. The prologue
+  // issues dS 0..3, then (K u, dS u+4) for u = 0..3: the same order the steady state would have
+  // produced, so one wait count holds from the first step on.
+  uint64_t ek[SK];  // entries of the pairs whose K tiles are in the k ring
+  uint64_t es[SD - SK];
 #pragma unroll
-  for (int t = 0; t < STAGES; ++t) er[t] = entry(t);
+  for (int u = 0; u < SK; ++u) ek[u] = entry(u);
 #pragma unroll
-  for (int t = 0; t < STAGES; ++t) issue(er[t], t);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * DMA_PER_PAIR));  // pairs 0, 1 landed
+  for (int u = 0; u < SD - SK; ++u) es[u] = entry(SK + u);
+#pragma unroll
+  for (int u = 0; u < SK; ++u) issue_s(ek[u], u);
+#pragma unroll
+  for (int u = 0; u < SK; ++u) {
+    issue_k(ek[u], u);
+    issue_s(es[u], SK + u);
+  }
+  // pairs 0, 1 landed: after K of pair 1 come dS 5, K 2, dS 6, K 3, dS 7
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DMA_S + 2 * DMA_K));
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
   barrier_lds();  // ... everyone's
+  uint64_t nk = entry(SK), ns = entry(SD);  // the next step's K and dS entries
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   Ops x, y;
-  read_ops(0, x);
-  if (vb_of(er[0]) < BLOCK) mask_ops(vb_of(er[0]), x);
+  read_ops(0, 0, x);
+  if (vb_of(ek[0]) < BLOCK) mask_ops(vb_of(ek[0]), x);
 
-  // Step t (pair t in stage t % 6): read pair t+1's operands, MFMAs of pair t; then pair t+2
-  // has landed (own DMAs, then the barrier: everyone's), everyone is done with stage t % 6, and
-  // pair t+6 goes there. The loop is unrolled by six so stage offsets are constants.
-  auto step = [&](int t, int st, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
-    const int st1 = st + 1 == STAGES ? 0 : st + 1;
-    read_ops(st1, nxt);
+  // Step t (pair t: k stage t % SK, s stage t % SD): read pair t+1's operands, MFMAs of pair t;
+  // then, once K of pair t+2 (and with it everything issued earlier, dS of t+2 included) has
+  // landed -- own DMAs, then the barrier: everyone's -- everyone is done with pair t's stages:
+  // K of pair t+4 and dS of pair t+8 go there. Unrolled by eight so stage offsets are constants.
+  auto step = [&](int t, int u, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
+    const int sk = u % SK, sd = u;            // stages of pair t
+    const int sk1 = (u + 1) % SK, sd1 = (u + 1) % SD;  // stages of pair t+1
+    read_ops(sk1, sd1, nxt);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       acc[0] = mfma32(cur.a[ks], cur.b[0][ks], acc[0]);
@@ -181,21 +206,27 @@ bwd_dq_spill_kernel(BwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three transposed reads
     }
     __builtin_amdgcn_sched_barrier(0);
-    const uint64_t e = entry(t + STAGES);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DMA_PER_PAIR));  // pair t+2 landed
-    barrier_lds_with(e);
-    issue(e, st);
-    const int vb1 = vb_of(er[st1]);
-    er[st] = e;
+    // after K of pair t+2: dS t+6, K t+3, dS t+7
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DMA_S + DMA_K));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
+    barrier_lds_with(nk ^ ns);           // (the entries loaded last step are in)
+    issue_k(nk, sk);
+    issue_s(ns, sd);
+    const int vb1 = vb_of(ek[sk1]);
+    ek[sk] = nk;
+    nk = entry(t + SK + 1);  // the next step's; waited for at its barrier
+    ns = entry(t + SD + 1);
     if (vb1 < BLOCK) mask_ops(vb1, nxt);  // rare: a ragged kv block
   };
-  for (int t = 0; t < n; t += STAGES) {
+  for (int t = 0; t < n; t += SD) {
     step(t, 0, x, y);
     if (t + 1 < n) step(t + 1, 1, y, x);
     if (t + 2 < n) step(t + 2, 2, x, y);
     if (t + 3 < n) step(t + 3, 3, y, x);
     if (t + 4 < n) step(t + 4, 4, x, y);
     if (t + 5 < n) step(t + 5, 5, y, x);
+    if (t + 6 < n) step(t + 6, 6, x, y);
+    if (t + 7 < n) step(t + 7, 7, y, x);
   }
   // no DMA may still be writing this workgroup's LDS when it ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
