@@ -285,6 +285,55 @@ def test_backward_edge_cases(name, mode):
         assert np.all(got.float().cpu().numpy()[zero] == 0)
 
 
+@pytest.mark.parametrize("give_q2k", [False, True])
+@pytest.mark.parametrize("n", [2, "odd_blocks_ragged"])
+def test_spill_slot_tables_bit_exact(n, give_q2k):
+    """The dS slot tables of the spill mode (index work: bit-exact). Expected values from their
+    definition in include/vsa.h, on the oracle's k2q: kbase = exclusive prefix sum of the k2q
+    counts inside each head; qent = (kbase[kv] + position of q in kv's ascending k2q row) |
+    kv << 32 | vbs[kv] << 48 for every q2k entry."""
+    if n == 2:
+        c = workloads.config(2)
+    else:
+        B, H, nb, topk, vbs, pool, _ = EDGE_CASES[n]
+        c = workloads.make_case(B, H, nb, topk, seed=17, vbs=vbs, kv_pool=pool, name=n)
+    d = to_dev(c)
+    ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
+    k2q_idx, k2q_num = torch.from_numpy(ridx).to(DEV), torch.from_numpy(rnum).to(DEV)
+    o = torch.zeros_like(d["q"])
+    lse = torch.zeros(c.B, c.H, c.S, dtype=torch.float32, device=DEV)
+    extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"]) if give_q2k else {}
+    plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                     dq_mode=V.DQ_SPILL, **extra)
+    say(f"[slot tables] {n}, q2k {'given' if give_q2k else 'derived'}")
+    plan.stage(plan.PREPROCESS)
+    plan.stage(plan.INDEX)
+    torch.cuda.synchronize()
+    BH, nb = c.B * c.H, c.nb
+    kq = c.q2k_idx.shape[-1] if give_q2k else nb
+    num = rnum.reshape(BH, nb).astype(np.int64)
+    kbase = np.zeros((BH, nb), np.int64)
+    kbase[:, 1:] = np.cumsum(num, axis=1)[:, :-1]
+    assert np.array_equal(plan.region(V.WS_KBASE, BH * nb).cpu().numpy().reshape(BH, nb), kbase)
+    got = plan.region(V.WS_QENT, BH * nb * kq, torch.int64).cpu().numpy().reshape(BH, nb, kq)
+    # the q2k lists the library walks: the given ones, or the inverse of k2q (ascending)
+    if give_q2k:
+        qidx = c.q2k_idx.numpy().reshape(BH, nb, -1)
+        qnum = c.q2k_num.numpy().reshape(BH, nb)
+    else:
+        di, dn = O.invert_indices(ridx, rnum, nb)
+        qidx, qnum = di.reshape(BH, nb, -1), dn.reshape(BH, nb)
+    vbs = c.vbs.numpy()
+    kidx = ridx.reshape(BH, nb, -1)
+    for bh in range(BH):
+        for q in range(nb):
+            for s_ in range(int(qnum[bh, q])):
+                kv = int(qidx[bh, q, s_])
+                row = list(kidx[bh, kv, :num[bh, kv]])
+                want = (int(kbase[bh, kv]) + row.index(q)) | (kv << 32) | (int(vbs[kv]) << 48)
+                assert int(got[bh, q, s_]) == want, (bh, q, s_)
+
+
 @pytest.mark.parametrize("mode", sorted(MODES))
 def test_backward_any_order_gives_identical_bits(mode):
     """Any kv work order: the same dq, dk, dv bits (fixed per-item summation order, no atomics)."""
