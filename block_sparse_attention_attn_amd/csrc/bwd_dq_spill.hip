@@ -15,11 +15,11 @@
 // dS slot, kv block and vbs per entry). Wave w computes dQ^T rows d = 32w .. 32w+31 for both q
 // halves: dQ^T += K^T dS^T with v_mfma_f32_32x32x16_bf16, four k-steps of 16 kv per pair. K_j
 // (16 KiB) and the dS tile (8 KiB) of each pair arrive by global_load_lds_dwordx4 into two LDS
-// rings: dS, streamed from HBM, is fetched six steps before it is read; K, mostly L2 hits, two
-// steps before. Both operands come out of LDS through ds_read_b64_tr_b16, one pair ahead of
-// their MFMAs. A pair of a ragged kv
-// block has its padded kv slots masked to zero in both operands (so neither stale K rows nor the
-// dS values of masked keys can reach dQ).
+// rings of 80 KiB together, so two workgroups share a CU: dS, streamed from HBM, is fetched three
+// steps before it is read; K, mostly L2 hits, two steps before. Both operands come out of LDS
+// through ds_read_b64_tr_b16, one pair ahead of their MFMAs. A pair of a ragged kv block has its
+// padded kv slots masked to zero in both operands (so neither stale K rows nor the dS values of
+// masked keys can reach dQ).
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -27,26 +27,25 @@ namespace vsa {
 
 namespace {
 
-// Two rings: dS tiles come from HBM and are fetched eight pairs ahead (SD stages), K tiles are
-// mostly L2 hits and are fetched four pairs ahead (SK stages). 8 x 8 KiB + 4 x 16 KiB = 128 KiB.
-constexpr int SD = 8;
-constexpr int SK = 4;
+// Two rings per workgroup: dS tiles (from HBM) in SD stages, K tiles (mostly L2 hits) in SK
+// stages; the tile of pair t goes to stage t % SD (t % SK). 4 x 8 KiB + 3 x 16 KiB = 80 KiB, so two
+// workgroups share a CU and each covers the other's barrier and issue gaps.
+constexpr int SD = 4;
+constexpr int SK = 3;
+constexpr int UNROLL = 12;      // a multiple of SD and SK: stage offsets are constants
+static_assert(SD >= SK && SK >= 3 && UNROLL % SD == 0 && UNROLL % SK == 0 && UNROLL % 2 == 0, "");
 constexpr int K_BYTES = 16384;  // one [64][128] bf16 K tile, swizzled
 constexpr int S_BYTES = 8192;   // one dS tile, as the kv-major kernel stored it
 constexpr int DMA_K = 4;        // per wave per pair: four 1-KiB slices of K
 constexpr int DMA_S = 2;        // ... and two of dS
 
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// The same barrier, with `v` (a scalar load's result) required in its registers first.
-__device__ __forceinline__ void barrier_lds_with(uint64_t v) {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(v) : "memory");
-}
+// A workgroup barrier that does not wait for this wave's LDS reads: the reads in flight at each
+// barrier are of stages no DMA issued after it writes.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 }  // namespace
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_spill_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char s_ring[SD * S_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_ring[SK * K_BYTES];
@@ -93,11 +92,15 @@ bwd_dq_spill_kernel(BwdParams p) {
   const uint32_t k_lds = lds_addr((VSA_LDS char*)k_ring) + 4096 * w;
   const uint32_t s_lds = lds_addr((VSA_LDS char*)s_ring) + 2048 * w;
   const uint32_t s_off = 16 * lane;
-  auto issue_k = [&](uint64_t e, int sk) __attribute__((always_inline)) {
-    dma_tile(kh_ptr + (size_t)kv_of(e) * BLOCK * HEAD_DIM, toff, k_lds + sk * K_BYTES);
+  auto k_src = [&](uint64_t e) { return (const void*)(kh_ptr + (size_t)kv_of(e) * BLOCK * HEAD_DIM); };
+  auto s_src = [&](uint64_t e) {
+    return (const void*)(ds_head + (size_t)slot_of(e) * S_BYTES + 2048 * w);
   };
-  auto issue_s = [&](uint64_t e, int sd) __attribute__((always_inline)) {
-    dma_lin2_nt(ds_head + (size_t)slot_of(e) * S_BYTES + 2048 * w, s_off, s_lds + sd * S_BYTES);
+  auto issue_k = [&](const void* src, int sk) __attribute__((always_inline)) {
+    dma_tile(src, toff, k_lds + sk * K_BYTES);
+  };
+  auto issue_s = [&](const void* src, int sd) __attribute__((always_inline)) {
+    dma_lin2_nt(src, s_off, s_lds + sd * S_BYTES);
   };
 
   // Operands of one pair. A = K^T: lane holds d = 32w + lane%32 and kv 16ks + 8kh + j. B = dS^T
@@ -158,28 +161,24 @@ bwd_dq_spill_kernel(BwdParams p) {
   };
 
   // ---- prologue ----
-  // Pair u's K goes to k stage u % SK, its dS to s stage u % SD (past the end of the list:
-  // repeats of the last pair). In the steady state the barrier of step u frees both stages of
-  // pair u and step u then issues K of pair u+4 and dS of pair u+8, in that order. The prologue
-  // issues dS 0..3, then (K u, dS u+4) for u = 0..3: the same order the steady state would have
-  // produced, so one wait count holds from the first step on.
-  uint64_t ek[SK];  // entries of the pairs whose K tiles are in the k ring
-  uint64_t es[SD - SK];
+  // In the steady state step u issues K of pair u+SK and then dS of pair u+SD. The prologue runs
+  // the virtual steps u = -SD .. -1 of that sequence (skipping K of negative pairs), so the DMA
+  // order, and with it every wait count below, is the same from the first step on.
+  uint64_t e0[SD];
 #pragma unroll
-  for (int u = 0; u < SK; ++u) ek[u] = entry(u);
+  for (int u = 0; u < SD; ++u) e0[u] = entry(u);
+  uint64_t ek[SK];  // entries of the pairs whose K tiles are in the k ring (pair p: ek[p % SK])
 #pragma unroll
-  for (int u = 0; u < SD - SK; ++u) es[u] = entry(SK + u);
+  for (int u = 0; u < SK; ++u) ek[u] = e0[u];
 #pragma unroll
-  for (int u = 0; u < SK; ++u) issue_s(ek[u], u);
-#pragma unroll
-  for (int u = 0; u < SK; ++u) {
-    issue_k(ek[u], u);
-    issue_s(es[u], SK + u);
+  for (int u = -SD; u < 0; ++u) {
+    if (u + SK >= 0) issue_k(k_src(e0[u + SK]), u + SK);
+    issue_s(s_src(e0[u + SD]), u + SD);
   }
-  // pairs 0, 1 landed: after K of pair 1 come dS 5, K 2, dS 6, K 3, dS 7
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DMA_S + 2 * DMA_K));
+  // pairs 0 and 1 landed: after K of pair 1 come its step's dS and SK - 2 whole steps
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_S + (SK - 2) * (DMA_K + DMA_S)));
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
-  barrier_lds();  // ... everyone's
+  barrier_only();                      // ... everyone's
   uint64_t nk = entry(SK), ns = entry(SD);  // the next step's K and dS entries
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
@@ -187,13 +186,18 @@ bwd_dq_spill_kernel(BwdParams p) {
   read_ops(0, 0, x);
   if (vb_of(ek[0]) < BLOCK) mask_ops(vb_of(ek[0]), x);
 
-  // Step t (pair t: k stage t % SK, s stage t % SD): read pair t+1's operands, MFMAs of pair t;
-  // then, once K of pair t+2 (and with it everything issued earlier, dS of t+2 included) has
-  // landed -- own DMAs, then the barrier: everyone's -- everyone is done with pair t's stages:
-  // K of pair t+4 and dS of pair t+8 go there. Unrolled by eight so stage offsets are constants.
+  // Step t (pair t: k stage t % SK, s stage t % SD). First everything this wave asked of LDS and
+  // of the scalar cache is in: pair t's operands and the entries loaded last step. Then pair t+1's
+  // operands are read while pair t's MFMAs run. Once K and dS of pair t+2 have landed (own DMAs,
+  // then the barrier: everyone's), everyone is done with pair t's stages: K of pair t+SK and dS
+  // of pair t+SD go there.
   auto step = [&](int t, int u, Ops& cur, Ops& nxt) __attribute__((always_inline)) {
-    const int sk = u % SK, sd = u;            // stages of pair t
+    const int sk = u % SK, sd = u % SD;                // stages of pair t
     const int sk1 = (u + 1) % SK, sd1 = (u + 1) % SD;  // stages of pair t+1
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
+    const void* kn = k_src(nk);
+    const void* sn = s_src(ns);
+    asm volatile("" ::"s"(kn), "s"(sn));  // source addresses ready before the MFMAs
     read_ops(sk1, sd1, nxt);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -206,27 +210,23 @@ bwd_dq_spill_kernel(BwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three transposed reads
     }
     __builtin_amdgcn_sched_barrier(0);
-    // after K of pair t+2: dS t+6, K t+3, dS t+7
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DMA_S + DMA_K));
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
-    barrier_lds_with(nk ^ ns);           // (the entries loaded last step are in)
-    issue_k(nk, sk);
-    issue_s(ns, sd);
+    // K of pair t+2 was issued SK-2 steps ago; after it come its step's dS and SK-3 whole steps
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_S + (SK - 3) * (DMA_K + DMA_S)));
+    barrier_only();
+    issue_k(kn, sk);
+    issue_s(sn, sd);
     const int vb1 = vb_of(ek[sk1]);
     ek[sk] = nk;
-    nk = entry(t + SK + 1);  // the next step's; waited for at its barrier
+    nk = entry(t + SK + 1);  // the next step's; waited for at its top
     ns = entry(t + SD + 1);
     if (vb1 < BLOCK) mask_ops(vb1, nxt);  // rare: a ragged kv block
   };
-  for (int t = 0; t < n; t += SD) {
-    step(t, 0, x, y);
-    if (t + 1 < n) step(t + 1, 1, y, x);
-    if (t + 2 < n) step(t + 2, 2, x, y);
-    if (t + 3 < n) step(t + 3, 3, y, x);
-    if (t + 4 < n) step(t + 4, 4, x, y);
-    if (t + 5 < n) step(t + 5, 5, y, x);
-    if (t + 6 < n) step(t + 6, 6, x, y);
-    if (t + 7 < n) step(t + 7, 7, y, x);
+  for (int t = 0; t < n; t += UNROLL) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; u += 2) {
+      if (t + u < n) step(t + u, u, x, y);
+      if (t + u + 1 < n) step(t + u + 1, u + 1, y, x);
+    }
   }
   // no DMA may still be writing this workgroup's LDS when it ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
