@@ -218,6 +218,25 @@ bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
+  // LDS byte addresses of the transposed reads below, one per (column group nt, row half h) and
+  // ring: the q half (16 rows), the stage and the ring base differ only by constants, which the
+  // reads carry as immediate offsets (the empty asm keeps the compiler from re-deriving the dO
+  // addresses from the Q ones, which would cost an add per read: the dO ring starts at 64 KiB,
+  // past the reach of an immediate).
+  uint32_t trq[4][2], trd[4][2];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int off = tile_elem_byte(32 * wq + 4 * (grp >> 1) + (t16 >> 2) + 8 * h,
+                                     32 * nt + 16 * (grp & 1) + 4 * (t16 & 3));
+      trq[nt][h] = lds_addr(qr) + off;
+      trd[nt][h] = lds_addr(dr) + off;
+      asm volatile("" : "+v"(trq[nt][h]), "+v"(trd[nt][h]));
+    }
+  }
+  auto rd_tr = [](uint32_t a) { return lds_read_tr((const VSA_LDS void*)(uintptr_t)a); };
+
   f32x16 s0, p0, s1, p1;
   load_rows(0, 0);
   load_rows(0, 4);
@@ -246,8 +265,6 @@ bwd_dkdv_kernel(BwdParams p) {
   auto step = [&](int t, int st, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn)
                   __attribute__((always_inline)) {
     const int st2 = (st + 2) & 3;
-    VSA_LDS char* qt = qr + st * STAGE_BYTES;
-    VSA_LDS char* dt = dr + st * STAGE_BYTES;
 
     // ---- phase B ----
     // transposed B operands of dV/dK for q block t: k slot jj of step s2 is q row
@@ -255,14 +272,11 @@ bwd_dkdv_kernel(BwdParams p) {
     bf16x8 db[2][4], qbt[2][4];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const int q0 = 32 * wq + 16 * s2 + 4 * (grp >> 1) + (t16 >> 2);
+      const uint32_t o = st * STAGE_BYTES + s2 * 16 * 256;  // stage, then 16 rows further down
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int col = 32 * nt + 16 * (grp & 1) + 4 * (t16 & 3);
-        db[s2][nt] = join(lds_read_tr(dt + tile_elem_byte(q0, col)),
-                          lds_read_tr(dt + tile_elem_byte(q0 + 8, col)));
-        qbt[s2][nt] = join(lds_read_tr(qt + tile_elem_byte(q0, col)),
-                           lds_read_tr(qt + tile_elem_byte(q0 + 8, col)));
+        db[s2][nt] = join(rd_tr(trd[nt][0] + o), rd_tr(trd[nt][1] + o));
+        qbt[s2][nt] = join(rd_tr(trq[nt][0] + o), rd_tr(trq[nt][1] + o));
       }
     }
 #pragma unroll
