@@ -8,170 +8,229 @@
 //     x = (q k^T) * sm_scale * log2(e)   for kv rows < vbs[j], -inf otherwise
 //     o = sum_j softmax_2(x) v,  lse = max(x) + log2(sum 2^(x - max))
 // with a base-2 online softmax (v_exp_f32 is 2^x natively). A row with no valid key gets o = 0
-// and lse = -inf.
+// and lse = -inf; kv ids outside [0, nb) in a list contribute nothing.
 //
-// gfx950 layout: one 256-thread workgroup per (b, h, q block); wave w owns q rows 16*w..16*w+15
-// and keeps them in registers as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16). K_j and
-// V_j tiles stream through swizzled LDS (global_load_lds_dwordx4, double-buffered). The column
-// statistics of S^T are lane-local plus a 4-group exchange; P^T (bf16) feeds O^T += V^T P^T
-// directly as the B operand, with V^T from ds_read_b64_tr_b16 transposed reads.
+// gfx950 design: one 256-thread workgroup per (b, h, q block), two per CU. The four waves form a
+// 2 x 2 grid, q half x kv half: wave (wq, wk) takes q rows 32wq .. 32wq+31 and, of every kv
+// block, kv rows 32wk .. 32wk+31. Each wave runs its own online softmax over its kv halves (its
+// own running max, sum and O^T), and the two kv halves of a q half are merged once at the end
+// (max of the two maxima, each side rescaled to it). So no statistic crosses waves inside the
+// loop, and each wave reads only its half of every K and V tile from LDS.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from the swizzled LDS tile
+//     (ds_read_b128), B = Q^T fragments held in registers for the whole item.
+//   * A q column's 32 scores sit in one lane pair (l, l ^ 32): the max and the sum are lane-local
+//     plus one exchange.
+//   * The running max is only raised when a block's max exceeds it by more than 8 (in log2
+//     units): the exponentials then stay below 2^8, O^T and the sum are rescaled rarely, and the
+//     final o = O / l and lse = max + log2(l) are unchanged in exact arithmetic.
+//   * P^T (bf16) is the B operand of O^T += V^T P^T straight from the D layout of S^T (the kv
+//     contraction index is permuted to match); V^T comes from ds_read_b64_tr_b16.
+//   * K and V tiles arrive by global_load_lds_dwordx4 into a two-stage LDS ring, one block ahead.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
 namespace vsa {
 
-__global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char k_s0[16384];
-  __shared__ __attribute__((aligned(1024))) char k_s1[16384];
-  __shared__ __attribute__((aligned(1024))) char v_s0[16384];
-  __shared__ __attribute__((aligned(1024))) char v_s1[16384];
+namespace {
+
+constexpr int TILE = 16384;         // one [64][128] bf16 tile
+constexpr float RESCALE_GAP = 8.f;  // raise the running max only when exceeded by this much
+
+}  // namespace
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_kernel(FwdParams p) {
+  // stage s: K tile at 2s * TILE, V tile at (2s + 1) * TILE
+  __shared__ __attribute__((aligned(1024))) char kv_s[4 * TILE];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
-  const int g = lane >> 4;    // 16-lane group = k group of the 16x16x32 layout
-  const int l16 = lane & 15;
+  const int wq = w & 1;   // q half
+  const int wk = w >> 1;  // kv half
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int grp = lane >> 4;
+  const int t16 = lane & 15;
 
-  const int item = blockIdx.x;  // (bh, q block)
+  const int item = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);  // (bh, q block)
+  if (item >= p.BH * p.nb) return;
   const int bh = item / p.nb;
   const int qb = item - bh * p.nb;
   int n = ld_const(p.q2k_num, item);
   n = n < 0 ? 0 : (n > p.q2k_stride ? p.q2k_stride : n);
   const int32_t* list = p.q2k_idx + (size_t)item * p.q2k_stride;
   const size_t head = (size_t)bh * p.S * HEAD_DIM;
+  const int qrow = qb * BLOCK + 32 * wq + l32;  // this lane's q row (a column of S^T)
 
-
-  // Q^T fragment: lane holds q row 16*w + l16, d = 32*s + 8*g + 0..7.
-  const int qrow = qb * BLOCK + 16 * w + l16;
-  bf16x8 qf[4];
+  // B operand of S^T = K Q^T: lane holds Q[qrow][16s + 8g + 0..7], s = 0..7
+  bf16x8 qf[8];
   {
     const bf16x8* qr = (const bf16x8*)(p.q + head + (size_t)qrow * HEAD_DIM);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = qr[4 * s + g];
+    for (int s = 0; s < 8; ++s) qf[s] = qr[2 * s + g];
   }
 
-  f32x4 oacc[8];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) oacc[mt] = f32x4{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
-  const float scale_log2 = p.scale_log2;
-
-  // skip out-of-range kv ids (a caller contract violation) instead of reading out of bounds
-  auto kv_of = [&](int t) {
-    const int kb = ld_const(list, t);
-    return (kb >= 0 && kb < p.nb) ? kb : -1;
+  // list entry t: its kv block (an out-of-range id is read as block 0 and masked entirely)
+  auto kv_raw = [&](int t) { return ld_const(list, t); };
+  auto kv_ok = [&](int kb) { return kb >= 0 && kb < p.nb; };
+  uint32_t toff[4];
+  tile_offsets_wave(toff, lane, w);
+  const uint32_t lds0 = lds_addr((VSA_LDS char*)kv_s) + 4096 * w;
+  auto issue = [&](int kb, int st) __attribute__((always_inline)) {
+    const size_t tile = (size_t)(kv_ok(kb) ? kb : 0) * BLOCK * HEAD_DIM;
+    dma_tile_pair(p.k + head + tile, p.v + head + tile, toff, lds0 + 2 * st * TILE,
+                  lds0 + (2 * st + 1) * TILE);
   };
 
-  if (n > 0) {
-    const int kb0 = kv_of(0);
-    if (kb0 >= 0) {
-      tile_load_async<4>(p.k + head + (size_t)kb0 * BLOCK * HEAD_DIM, (VSA_LDS char*)k_s0, lane, w);
-      tile_load_async<4>(p.v + head + (size_t)kb0 * BLOCK * HEAD_DIM, (VSA_LDS char*)v_s0, lane, w);
-    }
-  }
-  auto step = [&](int t, VSA_LDS char* kt, VSA_LDS char* vt, VSA_LDS char* kn_s,
-                  VSA_LDS char* vn_s) __attribute__((always_inline)) {
-    const int kb = kv_of(t);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this block's K/V tiles have landed
-    __syncthreads();
-    if (t + 1 < n) {
-      const int kn = kv_of(t + 1);
-      if (kn >= 0) {
-        tile_load_async<4>(p.k + head + (size_t)kn * BLOCK * HEAD_DIM, kn_s, lane, w);
-        tile_load_async<4>(p.v + head + (size_t)kn * BLOCK * HEAD_DIM, vn_s, lane, w);
-      }
-    }
-    if (kb < 0) return;
-    const int vb = ld_const(p.vbs, kb);
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+  float m_run = -__builtin_inff();  // of this lane's q column over this wave's kv halves
+  float l_run = 0.f;
+  const float scale_log2 = p.scale_log2;
+  const int kv_l = 32 * wk + l32;  // this lane's kv row of the A operand of S^T
 
-    // S^T tiles: element i of tile mt is kv 16*mt + 4*g + i, q 16*w + l16
-    f32x4 sacc[4];
+  if (n > 0) issue(kv_raw(0), 0);
+  int kb = n > 0 ? kv_raw(0) : 0;
+  for (int t = 0; t < n; ++t) {
+    const int st = t & 1;
+    // block t landed (own DMAs, then the barrier: everyone's); everyone is done with block t-1,
+    // whose stage receives block t+1
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
+    asm volatile("s_barrier" ::: "memory");
+    const int kb_next = t + 1 < n ? kv_raw(t + 1) : 0;
+    if (t + 1 < n) issue(kb_next, st ^ 1);
+    const VSA_LDS char* kt = (const VSA_LDS char*)kv_s + 2 * st * TILE;
+    const VSA_LDS char* vt = kt + TILE;
+    const int vb = kv_ok(kb) ? ld_const(p.vbs, kb) : 0;
+
+    // S^T tile: element i is kv 32wk + 8(i/4) + 4g + i%4, q = this lane's column
+    bf16x8 ka[8];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = f32x4{};
+    for (int s = 0; s < 8; ++s) ka[s] = *(const VSA_LDS bf16x8*)(kt + tile_byte(kv_l, 2 * s + g));
+    // V^T operands of O^T += V^T P^T: k-step c, slot j is kv 32wk + 16c + 8(j/4) + 4g + j%4 (the
+    // D-layout order of S^T); d tile dt, lane's d = 32dt + l32
+    bf16x8 va[4][2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 ka = *(const VSA_LDS bf16x8*)(kt + tile_byte(16 * mt + l16, 4 * s + g));
-        sacc[mt] = mfma16(ka, qf[s], sacc[mt]);
+    for (int c = 0; c < 2; ++c) {
+      const int r0 = 32 * wk + 16 * c + 4 * g + (t16 >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int col = 32 * dt + 16 * (grp & 1) + 4 * (t16 & 3);
+        va[dt][c] = join(lds_read_tr(vt + tile_elem_byte(r0, col)),
+                         lds_read_tr(vt + tile_elem_byte(r0 + 8, col)));
       }
     }
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sacc = mfma32(ka[s], qf[s], sacc);
+
     float x[16];
-    float mx = -__builtin_inff();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int i = 0; i < 16; ++i) x[i] = sacc[i] * scale_log2;
+    if (vb < BLOCK) {  // ragged or invalid block: mask kv rows >= vb
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kv = 16 * mt + 4 * g + i;
-        const float xi = kv < vb ? sacc[mt][i] * scale_log2 : -__builtin_inff();
-        x[4 * mt + i] = xi;
-        mx = fmaxf(mx, xi);
+      for (int i = 0; i < 16; ++i) {
+        const int kv = 32 * wk + 8 * (i / 4) + 4 * g + (i & 3);
+        x[i] = kv < vb ? x[i] : -__builtin_inff();
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float ps[16];
-    float rs = 0.0f;
+    // raise the running max (and rescale) only when this block's max exceeds it by the gap;
+    // both lanes of a q column decide alike, and the branch is taken by the whole wave
+    const bool raise = mx > m_run + RESCALE_GAP;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mx : m_run;
+      const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
+    float pv[16];
+    float rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      ps[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
-      rs += ps[i];
+      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      rs += pv[i];
     }
-    rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+    l_run += rs;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      oacc[mt][0] *= alpha;
-      oacc[mt][1] *= alpha;
-      oacc[mt][2] *= alpha;
-      oacc[mt][3] *= alpha;
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 pb = pack8(pv[8 * c + 0], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
+                              pv[8 * c + 4], pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma32(va[dt][c], pb, oacc[dt]);
     }
-    // O^T[d][q] += V^T[d][kv] P^T[kv][q]; k slot jj of step s2 is kv 32*s2 + 16*(jj/4) + 4*g + jj%4
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 pb = pack8(ps[8 * s2 + 0], ps[8 * s2 + 1], ps[8 * s2 + 2], ps[8 * s2 + 3],
-                              ps[8 * s2 + 4], ps[8 * s2 + 5], ps[8 * s2 + 6], ps[8 * s2 + 7]);
-      const int kv0 = 32 * s2 + 4 * g + (l16 >> 2);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int col = 16 * mt + 4 * (l16 & 3);
-        const bf16x8 va = join(lds_read_tr(vt + tile_elem_byte(kv0, col)),
-                               lds_read_tr(vt + tile_elem_byte(kv0 + 16, col)));
-        oacc[mt] = mfma16(va, pb, oacc[mt]);
-      }
-    }
-  };
-  for (int t = 0; t < n; t += 2) {
-    step(t, (VSA_LDS char*)k_s0, (VSA_LDS char*)v_s0, (VSA_LDS char*)k_s1, (VSA_LDS char*)v_s1);
-    if (t + 1 < n)
-      step(t + 1, (VSA_LDS char*)k_s1, (VSA_LDS char*)v_s1, (VSA_LDS char*)k_s0, (VSA_LDS char*)v_s0);
+    kb = kb_next;
   }
 
-  // o row q = 16*w + l16; tile mt holds d = 16*mt + 4*g + 0..3
-  const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  // ---- merge the two kv halves of each q half through LDS, normalise, store ----
+  // The wave with kv half wk finalises d tiles 2wk, 2wk+1 and hands the other two over.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("s_barrier" ::: "memory");  // every wave is done with the rings
+  VSA_LDS f32x4* xo = (VSA_LDS f32x4*)(kv_s + (2 * wq + wk) * 9216);      // my hand-over
+  VSA_LDS f32x4* po = (VSA_LDS f32x4*)(kv_s + (2 * wq + (wk ^ 1)) * 9216);  // the partner's
+  VSA_LDS float* xs = (VSA_LDS float*)(xo + 8 * 64);
+  VSA_LDS float* ps = (VSA_LDS float*)(po + 8 * 64);
+  auto hand_over = [&](const f32x16& a, const f32x16& b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      xo[c * 64 + lane] = f32x4{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+      xo[(4 + c) * 64 + lane] = f32x4{b[4 * c], b[4 * c + 1], b[4 * c + 2], b[4 * c + 3]};
+    }
+  };
+  if (wk == 0)  // uniform: constant register indices in each branch
+    hand_over(oacc[2], oacc[3]);
+  else
+    hand_over(oacc[0], oacc[1]);
+  xs[lane] = m_run;
+  xs[64 + lane] = l_run;
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("s_barrier" ::: "memory");
+  const float m_o = ps[lane], l_o = ps[64 + lane];
+  const float m = fmaxf(m_run, m_o);
+  const float a_me = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+  const float a_o = m_o == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_o - m);
+  const float l = a_me * l_run + a_o * l_o;
+  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
   bf16* orow = p.o + head + (size_t)qrow * HEAD_DIM;
+  auto finish = [&](const f32x16& mine, int u, int dt) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    union {
-      bf16 b[4];
-      s16x4 s;
-    } u;
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 o2 = po[(u * 4 + c) * 64 + lane];
+      union {
+        bf16 b[4];
+        s16x4 s;
+      } r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u.b[i] = (bf16)(oacc[mt][i] * inv_l);
-    *(s16x4*)(orow + 16 * mt + 4 * g) = u.s;
+      for (int e = 0; e < 4; ++e) r.b[e] = (bf16)((a_me * mine[4 * c + e] + a_o * o2[e]) * inv_l);
+      // element 4c + e of tile dt is d = 32dt + 8c + 4g + e
+      *(s16x4*)(orow + 32 * dt + 8 * c + 4 * g) = r.s;
+    }
+  };
+  if (wk == 0) {
+    finish(oacc[0], 0, 0);
+    finish(oacc[1], 1, 1);
+  } else {
+    finish(oacc[2], 0, 2);
+    finish(oacc[3], 1, 3);
   }
-  if (g == 0) {
-    const float lse = l_run > 0.0f ? m_run + __builtin_log2f(l_run) : -__builtin_inff();
-    p.lse[(size_t)bh * p.S + qrow] = lse;
-  }
+  if (wk == 0 && g == 0)
+    p.lse[(size_t)bh * p.S + qrow] = l > 0.f ? m + __builtin_log2f(l) : -__builtin_inff();
 }
 
 void launch_fwd(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)(p.BH * p.nb)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)(p.items_per_xcd * 8)), dim3(256), 0, stream, p);
 }
 
 }  // namespace vsa

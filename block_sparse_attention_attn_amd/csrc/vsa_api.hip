@@ -130,6 +130,7 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
   p.S = a->seqlen;
   p.nb = a->num_kv_blocks;
   p.q2k_stride = a->q2k_stride;
+  p.items_per_xcd = (p.BH * p.nb + 7) / 8;
   p.scale_log2 = scale_log2(a->sm_scale);
   vsa::launch_fwd(p, (hipStream_t)stream);
   return launch_status("vsa_fwd");

@@ -28,6 +28,7 @@ struct FwdParams {
   bf16* o;
   float* lse;
   int BH, S, nb, q2k_stride;
+  int items_per_xcd;  // ceil(BH * nb / 8): workgroup ids map XCD-first onto (bh, q block) items
   float scale_log2;
 };
 void launch_fwd(const FwdParams& p, hipStream_t stream);
