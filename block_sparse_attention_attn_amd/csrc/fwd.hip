@@ -19,13 +19,14 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from the swizzled LDS tile
 //     (ds_read_b128), B = Q^T fragments held in registers for the whole item.
 //   * A q column's 32 scores sit in one lane pair (l, l ^ 32): the max and the sum are lane-local
-//     plus one exchange.
+//     plus one v_permlane32_swap.
 //   * The running max is only raised when a block's max exceeds it by more than 8 (in log2
 //     units): the exponentials then stay below 2^8, O^T and the sum are rescaled rarely, and the
 //     final o = O / l and lse = max + log2(l) are unchanged in exact arithmetic.
 //   * P^T (bf16) is the B operand of O^T += V^T P^T straight from the D layout of S^T (the kv
 //     contraction index is permuted to match); V^T comes from ds_read_b64_tr_b16.
-//   * K and V tiles arrive by global_load_lds_dwordx4 into a two-stage LDS ring, one block ahead.
+//   * K and V tiles arrive by global_load_lds_dwordx4 into two-stage LDS rings, K two blocks and
+//     V one block ahead: the S^T MFMAs of block t+1 run under the softmax of block t.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -40,7 +41,7 @@ constexpr float RESCALE_GAP = 8.f;  // raise the running max only when exceeded 
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(FwdParams p) {
-  // stage s: K tile at 2s * TILE, V tile at (2s + 1) * TILE
+  // K stage s at s * TILE, V stage s at (2 + s) * TILE (s = 0, 1)
   __shared__ __attribute__((aligned(1024))) char kv_s[4 * TILE];
 
   const int lane = threadIdx.x & 63;
@@ -70,16 +71,26 @@ fwd_kernel(FwdParams p) {
     for (int s = 0; s < 8; ++s) qf[s] = qr[2 * s + g];
   }
 
-  // list entry t: its kv block (an out-of-range id is read as block 0 and masked entirely)
-  auto kv_raw = [&](int t) { return ld_const(list, t); };
+  // list entry t (clamped to the list; an out-of-range kv id is read as block 0, masked entirely)
+  auto kv_raw = [&](int t) { return ld_const(list, t < n ? t : n - 1); };
   auto kv_ok = [&](int kb) { return kb >= 0 && kb < p.nb; };
+  auto vb_of = [&](int kb) { return kv_ok(kb) ? ld_const(p.vbs, kb) : 0; };
   uint32_t toff[4];
   tile_offsets_wave(toff, lane, w);
   const uint32_t lds0 = lds_addr((VSA_LDS char*)kv_s) + 4096 * w;
-  auto issue = [&](int kb, int st) __attribute__((always_inline)) {
-    const size_t tile = (size_t)(kv_ok(kb) ? kb : 0) * BLOCK * HEAD_DIM;
-    dma_tile_pair(p.k + head + tile, p.v + head + tile, toff, lds0 + 2 * st * TILE,
-                  lds0 + (2 * st + 1) * TILE);
+  auto tile_of = [&](int kb) { return (size_t)(kv_ok(kb) ? kb : 0) * BLOCK * HEAD_DIM; };
+  auto issue_k = [&](int kb, int st) __attribute__((always_inline)) {
+    dma_tile(p.k + head + tile_of(kb), toff, lds0 + st * TILE);
+  };
+  auto issue_v = [&](int kb, int st) __attribute__((always_inline)) {
+    dma_tile(p.v + head + tile_of(kb), toff, lds0 + (2 + st) * TILE);
+  };
+  const int kv_l = 32 * wk + l32;  // this lane's kv row of the A operand of S^T
+  // A operand of S^T (K rows) from K stage st
+  auto read_k = [&](int st, bf16x8 (&ka)[8]) __attribute__((always_inline)) {
+    const VSA_LDS char* kt = (const VSA_LDS char*)kv_s + st * TILE;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) ka[s] = *(const VSA_LDS bf16x8*)(kt + tile_byte(kv_l, 2 * s + g));
   };
 
   f32x16 oacc[4];
@@ -88,29 +99,48 @@ fwd_kernel(FwdParams p) {
   float m_run = -__builtin_inff();  // of this lane's q column over this wave's kv halves
   float l_run = 0.f;
   const float scale_log2 = p.scale_log2;
-  const int kv_l = 32 * wk + l32;  // this lane's kv row of the A operand of S^T
 
-  if (n > 0) issue(kv_raw(0), 0);
-  int kb = n > 0 ? kv_raw(0) : 0;
-  for (int t = 0; t < n; ++t) {
-    const int st = t & 1;
-    // block t landed (own DMAs, then the barrier: everyone's); everyone is done with block t-1,
-    // whose stage receives block t+1
+  // Block t: K in K stage t % 2, V in V stage t % 2. The S^T tile of block t is computed during
+  // step t-1 (the prologue for t = 0), so step t overlaps the softmax of t with the S^T MFMAs of
+  // t+1. Step t issues K of block t+2 (into the K stage block t used) and V of block t+1 (into
+  // the V stage block t-1 used); past the end of the list the last block is repeated, so no
+  // branch splits the step (the extra S^T tile is never used).
+  // The list entries of blocks t, t+1, t+2 (e0, e1, e2) and block t's valid rows (vb0) are loaded
+  // at the end of the step before, so no scalar-load wait sits inside a step.
+  f32x16 sacc = f32x16{};
+  int e0 = 0, e1 = 0, e2 = 0, vb0 = 0;
+  if (n > 0) {
+    e0 = kv_raw(0);
+    e1 = kv_raw(1);
+    e2 = kv_raw(2);
+    vb0 = vb_of(e0);
+    issue_k(e0, 0);
+    issue_v(e0, 0);
+    issue_k(e1, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
     asm volatile("s_barrier" ::: "memory");
-    const int kb_next = t + 1 < n ? kv_raw(t + 1) : 0;
-    if (t + 1 < n) issue(kb_next, st ^ 1);
-    const VSA_LDS char* kt = (const VSA_LDS char*)kv_s + 2 * st * TILE;
-    const VSA_LDS char* vt = kt + TILE;
-    const int vb = kv_ok(kb) ? ld_const(p.vbs, kb) : 0;
-
-    // S^T tile: element i is kv 32wk + 8(i/4) + 4g + i%4, q = this lane's column
     bf16x8 ka[8];
+    read_k(0, ka);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) ka[s] = *(const VSA_LDS bf16x8*)(kt + tile_byte(kv_l, 2 * s + g));
+    for (int s = 0; s < 8; ++s) sacc = mfma32(ka[s], qf[s], sacc);
+  }
+  for (int t = 0; t < n; ++t) {
+    const int st = t & 1;
+    // K of t+1 and V of t landed (own DMAs, then the barrier: everyone's); everyone is done with
+    // K of t and V of t-1
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
+    asm volatile("s_barrier" ::: "memory");
+    issue_k(e2, st);
+    issue_v(e1, st ^ 1);
+    const int vb = vb0;
+
+    bf16x8 ka[8];
+    read_k(st ^ 1, ka);
     // V^T operands of O^T += V^T P^T: k-step c, slot j is kv 32wk + 16c + 8(j/4) + 4g + j%4 (the
     // D-layout order of S^T); d tile dt, lane's d = 32dt + l32
+    const VSA_LDS char* vt = (const VSA_LDS char*)kv_s + (2 + st) * TILE;
     bf16x8 va[4][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -122,10 +152,8 @@ fwd_kernel(FwdParams p) {
                          lds_read_tr(vt + tile_elem_byte(r0 + 8, col)));
       }
     }
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sacc = mfma32(ka[s], qf[s], sacc);
 
+    // softmax of block t. S^T element i is kv 32wk + 8(i/4) + 4g + i%4, q = this lane's column.
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = sacc[i] * scale_log2;
@@ -139,7 +167,7 @@ fwd_kernel(FwdParams p) {
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = pair_max32(mx);
     // raise the running max (and rescale) only when this block's max exceeds it by the gap;
     // both lanes of a q column decide alike, and the branch is taken by the whole wave
     const bool raise = mx > m_run + RESCALE_GAP;
@@ -154,6 +182,10 @@ fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
     }
     const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
+    // exponentials of t under the S^T MFMAs of t+1, then the O^T MFMAs of t
+    f32x16 snext = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) snext = mfma32(ka[s], qf[s], snext);
     float pv[16];
     float rs = 0.f;
 #pragma unroll
@@ -161,8 +193,7 @@ fwd_kernel(FwdParams p) {
       pv[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
       rs += pv[i];
     }
-    rs += __shfl_xor(rs, 32, 64);
-    l_run += rs;
+    l_run += pair_sum32(rs);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const bf16x8 pb = pack8(pv[8 * c + 0], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
@@ -170,7 +201,15 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma32(va[dt][c], pb, oacc[dt]);
     }
-    kb = kb_next;
+    // the next step's entry and row count: issued after every LDS read of this step is consumed
+    // (a scalar load in flight would make the compiler wait for all LDS reads at once)
+    __builtin_amdgcn_sched_barrier(0);
+    const int e3 = kv_raw(t + 3), vb1 = vb_of(e1);
+    sacc = snext;
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
+    vb0 = vb1;
   }
 
   // ---- merge the two kv halves of each q half through LDS, normalise, store ----

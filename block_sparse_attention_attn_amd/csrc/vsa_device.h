@@ -59,6 +59,19 @@ __device__ __forceinline__ s16x4 lds_read_tr(const VSA_LDS void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((VSA_LDS s16x4*)p);
 }
 
+// Max and sum of a lane's value with the value of lane l ^ 32, through v_permlane32_swap (a VALU
+// lane swap, no LDS traffic): swapping a register with itself leaves the values of lanes l % 32
+// and 32 + l % 32 in the two halves of the result, in that order for both lanes of the pair, so
+// the two lanes get bitwise equal results.
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Eight fp32 values to one bf16x8 operand, round-to-nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
                                         float a5, float a6, float a7) {
