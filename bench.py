@@ -23,6 +23,8 @@ bracketed by HIP events on the stream it runs on (torch's current stream, which 
 
 The headline workload is B=1 H=8 S=32768 D=128, 25 % density (default); --workload 4 selects
 S=65536 at 12.5 % density. The line also carries the other headline workload's backward TFLOPS.
+--workload 5 times the 524288-token case (recompute dQ mode; use few steps, e.g. --steps 3
+--warmup 1: a step is a few seconds).
 Only one GPU is used: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -47,6 +49,9 @@ WORKLOAD_TEXT = {
        "(top-k 128 of 512 kv blocks per q block), all blocks full, o/lse from the GPU forward",
     4: "VSA 64-token block-sparse attention backward, B=1 H=8 S=65536 D=128 bf16, 12.5% density "
        "(top-k 128 of 1024 kv blocks per q block), all blocks full, device work order",
+    5: "VSA 64-token block-sparse attention backward, B=1 H=8 S=524288 D=128 bf16, 25% density "
+       "(top-k 2048 of 8192 kv blocks per q block), last kv block 40 valid tokens, inputs "
+       "0.5*N(0,1), dq recomputed (the dS tiles would need 1 TiB)",
 }
 
 
@@ -198,7 +203,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, choices=(3, 4))
+    ap.add_argument("--workload", type=int, default=3, choices=(3, 4, 5))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--dq-mode", choices=("spill", "recompute"), default="spill",
@@ -227,11 +232,14 @@ def main():
         del src, dst
     log(f"[bench] workload {args.workload}: steps={args.steps} warmup={args.warmup}")
     import block_sparse_attention_attn_amd as V
+    if args.workload == 5 and args.dq_mode == "spill":
+        log("[bench] workload 5: the dS tiles would need 1 TiB of workspace; dq is recomputed")
+        args.dq_mode = "recompute"
     mode = V.DQ_SPILL if args.dq_mode == "spill" else V.DQ_RECOMPUTE
     res, case = run_workload(args.workload, args.steps, args.warmup, mode)
     log(f"[bench] {json.dumps(res)}")
     secondary = None
-    if not args.no_secondary:
+    if not args.no_secondary and args.workload != 5:
         other = 4 if args.workload == 3 else 3
         log(f"[bench] secondary workload {other}")
         r2, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2), mode)
