@@ -185,6 +185,28 @@ def test_forward_parity(n):
     _fwd_compare(c, d, o, lse)
 
 
+def test_forward_ignores_out_of_range_kv_ids():
+    """kv ids outside [0, nb) in a q2k list (a caller-contract violation) contribute nothing and
+    fault nothing: the forward with such ids inserted in the middle of the lists gives the same
+    bits as without them."""
+    c = workloads.make_case(1, 2, 8, 3, seed=23, vbs=[64, 64, 64, 64, 64, 64, 64, 29])
+    d = to_dev(c)
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    # lists of width 5: the three valid ids with -1 and nb spliced in after the first one
+    bad = torch.empty(1, 2, 8, 5, dtype=torch.int32)
+    bad[..., 0] = c.q2k_idx[..., 0]
+    bad[..., 1] = -1
+    bad[..., 2] = c.q2k_idx[..., 1]
+    bad[..., 3] = c.nb
+    bad[..., 4] = c.q2k_idx[..., 2]
+    num = torch.full((1, 2, 8), 5, dtype=torch.int32)
+    say("[forward] lists with out-of-range kv ids")
+    o2, lse2 = V.forward(d["q"], d["k"], d["v"], bad.to(DEV), num.to(DEV), d["vbs"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    assert torch.equal(lse, lse2)
+
+
 # -----------------------------------------------------------------------------------------------
 # backward on small workloads, o and lse from the oracle (as the FastVideo test does)
 # -----------------------------------------------------------------------------------------------
