@@ -57,13 +57,12 @@ void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_pre_kernel, dim3(p.nb, p.BH), dim3(256), 0, stream, p);
 }
 
-// One workgroup per (b, h): bitonic sort of 32-bit keys (inverted bin << 14 | kv) in LDS, so the
-// result is larger bins first and ascending kv inside a bin -- a deterministic permutation.
-// bin = k2q_num / bin_width, clamped to 18 bits.
-__global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ num_in, int nb,
-                                                         int bin_width, int32_t* __restrict__ order) {
+// Work order of one (b, h) (one 1024-thread workgroup): bitonic sort of 32-bit keys (inverted
+// bin << 14 | kv) in LDS, so the result is larger bins first and ascending kv inside a bin -- a
+// deterministic permutation. bin = count / bin_width, clamped to 18 bits.
+__device__ void order_block(const int32_t* __restrict__ num_in, int nb, int bin_width,
+                            int32_t* __restrict__ order, int bh) {
   __shared__ uint32_t keys[ORDER_MAX_KV_BLOCKS];
-  const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   int P = 1;
   while (P < nb) P <<= 1;
@@ -99,18 +98,12 @@ __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restri
     order[(size_t)bh * nb + r] = bh * nb + (int)(keys[r] & 0x3FFFu);
 }
 
-void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
-                      hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_order_kernel, dim3(BH), dim3(1024), 0, stream, num, nb, bin_width, order);
-}
-
-// One workgroup per head: exclusive prefix sum of the clamped k2q counts. Thread t sums a
-// contiguous chunk of ceil(nb / 1024) counts, the 1024 chunk sums are scanned in LDS, and each
-// thread writes its chunk's prefixes.
-__global__ void __launch_bounds__(1024) spill_kbase_kernel(const int32_t* __restrict__ num, int nb,
-                                                           int stride, int32_t* __restrict__ kbase) {
+// dS slot bases of one head (one 1024-thread workgroup): exclusive prefix sum of the clamped k2q
+// counts. Thread t sums a contiguous chunk of ceil(nb / 1024) counts, the 1024 chunk sums are
+// scanned in LDS, and each thread writes its chunk's prefixes.
+__device__ void kbase_block(const int32_t* __restrict__ num, int nb, int stride,
+                            int32_t* __restrict__ kbase, int bh) {
   __shared__ int32_t part[1024];
-  const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int chunk = (nb + 1023) / 1024;
   const int lo = tid * chunk;
@@ -138,11 +131,34 @@ __global__ void __launch_bounds__(1024) spill_kbase_kernel(const int32_t* __rest
   }
 }
 
-void launch_spill_kbase(const int32_t* k2q_num, int BH, int nb, int k2q_stride, int32_t* kbase,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL(spill_kbase_kernel, dim3(BH), dim3(1024), 0, stream, k2q_num, nb, k2q_stride,
-                     kbase);
+__global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ num_in, int nb,
+                                                         int bin_width, int32_t* __restrict__ order) {
+  order_block(num_in, nb, bin_width, order, blockIdx.x);
 }
+
+void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
+                      hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_order_kernel, dim3(BH), dim3(1024), 0, stream, num, nb, bin_width, order);
+}
+
+// The index stage's per-head tasks in one launch: workgroup (bh, task) runs task blockIdx.y of the
+// list for head bh (a work order or the dS slot bases); the tasks are independent.
+__global__ void __launch_bounds__(1024) index_tasks_kernel(IndexTasks t, int nb, int bin_width,
+                                                           int k2q_stride) {
+  const IndexTask& task = t.task[blockIdx.y];
+  if (task.kind == IndexTask::ORDER)
+    order_block(task.num, nb, bin_width, task.out, blockIdx.x);
+  else
+    kbase_block(task.num, nb, k2q_stride, task.out, blockIdx.x);
+}
+
+void launch_index_tasks(const IndexTasks& t, int BH, int nb, int bin_width, int k2q_stride,
+                        hipStream_t stream) {
+  if (t.count <= 0) return;
+  hipLaunchKernelGGL(index_tasks_kernel, dim3(BH, t.count), dim3(1024), 0, stream, t, nb,
+                     bin_width, k2q_stride);
+}
+
 
 // One thread per q2k entry (bh, q, s): binary search of q in the ascending k2q row of its kv
 // block. A q missing from that row (a caller-contract violation: k2q is not the inverse of q2k,

@@ -325,25 +325,26 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
         const int r = launch_status("vsa_bwd q2k derivation");
         if (r != VSA_OK) return r;
       }
+      // the work orders and the dS slot bases: independent per-head tasks, one launch
+      vsa::IndexTasks tasks{};
       if (uses_device_order(a)) {
-        if (!a->order) {
-          vsa::launch_bwd_order(a->k2q_num, BH, nb, VSA_ORDER_BIN_WIDTH, ws.kv_order, s);
-          const int r = launch_status("vsa_bwd kv order");
-          if (r != VSA_OK) return r;
-        }
-        vsa::launch_bwd_order(derive ? ws.q2k_num : a->q2k_num, BH, nb, VSA_ORDER_BIN_WIDTH,
-                              ws.q_order, s);
-        const int r = launch_status("vsa_bwd q order");
+        if (!a->order)
+          tasks.task[tasks.count++] = {vsa::IndexTask::ORDER, a->k2q_num, ws.kv_order};
+        tasks.task[tasks.count++] = {vsa::IndexTask::ORDER, derive ? ws.q2k_num : a->q2k_num,
+                                     ws.q_order};
+      }
+      if (a->dq_mode == VSA_DQ_SPILL)
+        tasks.task[tasks.count++] = {vsa::IndexTask::KBASE, a->k2q_num, ws.kbase};
+      if (tasks.count > 0) {
+        vsa::launch_index_tasks(tasks, BH, nb, VSA_ORDER_BIN_WIDTH, a->max_q_blocks, s);
+        const int r = launch_status("vsa_bwd work orders / dS slot bases");
         if (r != VSA_OK) return r;
       }
       if (a->dq_mode == VSA_DQ_SPILL) {
         const vsa::BwdParams m = main_params(a, ws);
-        vsa::launch_spill_kbase(a->k2q_num, BH, nb, a->max_q_blocks, ws.kbase, s);
-        int r = launch_status("vsa_bwd dS slot bases");
-        if (r != VSA_OK) return r;
         vsa::launch_spill_qent(m.q2k_idx, m.q2k_num, m.q2k_stride, a->k2q_idx, a->k2q_num,
                                a->max_q_blocks, ws.kbase, a->vbs, BH, nb, m.cap, ws.qent, s);
-        r = launch_status("vsa_bwd dS slot table");
+        const int r = launch_status("vsa_bwd dS slot table");
         if (r != VSA_OK) return r;
       }
       return VSA_OK;

@@ -56,6 +56,21 @@ void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream);
 constexpr int ORDER_MAX_KV_BLOCKS = 16384; // LDS holds one 32-bit key per block
 void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
                       hipStream_t stream);
+// Up to three per-head tasks of the index stage in one launch (one 1024-thread workgroup per
+// head and task): ORDER writes the work order of `num` (counts per item) to `out`; KBASE writes
+// the dS slot bases (exclusive prefix sum of the clamped k2q counts `num`) to `out`.
+struct IndexTask {
+  enum Kind { ORDER = 0, KBASE = 1 };
+  int kind;
+  const int32_t* num;
+  int32_t* out;
+};
+struct IndexTasks {
+  IndexTask task[3];
+  int count;
+};
+void launch_index_tasks(const IndexTasks& t, int BH, int nb, int bin_width, int k2q_stride,
+                        hipStream_t stream);
 
 // ---- the two main backward kernels (kv-major dK/dV, q-major dQ) ----
 struct BwdParams {
@@ -88,9 +103,8 @@ void launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 void launch_bwd_dq_spill(const BwdParams& p, hipStream_t stream);
 
 // ---- dS slot tables (spill mode) ----
-// kbase[bh, kv] = sum of min(max(k2q_num, 0), k2q_stride) over the kv blocks before kv in head bh.
-void launch_spill_kbase(const int32_t* k2q_num, int BH, int nb, int k2q_stride, int32_t* kbase,
-                        hipStream_t stream);
+// kbase[bh, kv] = sum of min(max(k2q_num, 0), k2q_stride) over the kv blocks before kv in head bh:
+// an IndexTask::KBASE task.
 // qent[bh, q, s] for s < q2k_num[bh, q]: the slot of pair (q, kv = q2k_idx[bh, q, s]), i.e.
 // kbase[bh, kv] + (position of q in the ascending k2q row of kv), packed with kv and vbs[kv].
 void launch_spill_qent(const int32_t* q2k_idx, const int32_t* q2k_num, int q2k_stride,
