@@ -321,6 +321,14 @@ bwd_dkdv_kernel(BwdParams p) {
     // load issued below for the next step adds no wait for them.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    // The dS tile of q block t (spill mode) goes out here, between this wave's wait and the
+    // barrier, where the wave would otherwise idle until the others arrive; stores issued inside
+    // phase C delay its MFMAs and DMAs.
+    if (SPILL) {  // streamed past the caches: read once, by the q-major kernel
+      char* d = ds_tile(t) + ds_rec;
+      __builtin_nontemporal_store(sa[0], (bf16x8*)d);
+      __builtin_nontemporal_store(sa[1], (bf16x8*)(d + 16));
+    }
     barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
     const int qb = clampq(raw);
     raw = entry(t + 5);     // in by the next step's barrier
@@ -330,11 +338,6 @@ bwd_dkdv_kernel(BwdParams p) {
     // MFMAs of the next step), with q block t+4's DMA group into stage st split in three and
     // placed between them: the asm blocks keep their order relative to the reads, so the nine
     // DMAs spread over the phase instead of reaching the address unit together.
-    if (SPILL) {  // streamed past the caches: read once, by the q-major kernel
-      char* d = ds_tile(t) + ds_rec;
-      __builtin_nontemporal_store(sa[0], (bf16x8*)d);
-      __builtin_nontemporal_store(sa[1], (bf16x8*)(d + 16));
-    }
     {
       const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
       load_init(st2, sc, pc);
