@@ -242,7 +242,12 @@ bwd_dkdv_kernel(BwdParams p) {
   load_rows(0, 4);
   load_init(0, s0, p0);
   barrier_lds();  // everyone has read K/V out of stage 3
-  issue(clampq(e3), 3);
+  // q block 3's record and Q tile; step 0's phase B issues its dO tile (see the step below)
+  {
+    const int qb3 = clampq(e3);
+    dma_rec128(recs + (size_t)qb3 * LD_RECORD_FLOATS, roff, ld_lds + 3 * LD_BYTES);
+    dma_tile(qh + (size_t)qb3 * BLOCK * HEAD_DIM, toff, q_lds + 3 * STAGE_BYTES);
+  }
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     s0 = mfma32(qa[s], kf[s], s0);
@@ -254,17 +259,23 @@ bwd_dkdv_kernel(BwdParams p) {
 
   // Step t (q block t in stage st = t % 4): on entry (sc, pc) hold S - lse/scale_log2 and
   // dP - Delta of q block t, (sn, pn) the initial values of q block t+1 and (qa, da) its rows.
-  //   phase B: S/dP MFMAs of t+1, interleaved with the transposed dO^T, Q^T reads of t and
-  //            P, dS of t;
+  //   phase B: the dO DMA of q block t+3, then the S/dP MFMAs of t+1, interleaved with the
+  //            transposed dO^T, Q^T reads of t and P, dS of t;
   //   mid:     q block t+2 has landed (own DMAs, then the barrier: everyone's) and everyone is
   //            done with stage st, which then receives q block t+4;
   //   phase C: dV/dK MFMAs of t, interleaved with the record and row reads of t+2 into (sc, pc)
-  //            and (qa, da) and the DMA of q block t+4.
+  //            and (qa, da) and the record and Q DMAs of q block t+4.
   // The last steps compute throwaway S/dP from repeated q blocks, which keeps the body free of
   // branches. The loop is unrolled by four so stage offsets are constants.
+  int qb_carry = clampq(e3);  // the q block whose dO tile the next phase B fetches
   auto step = [&](int t, int st, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn)
                   __attribute__((always_inline)) {
     const int st2 = (st + 2) & 3;
+    // dO tile of q block t+3 into stage (t+3)%4, the second half of the DMA group whose record
+    // and Q tile phase C of the previous step issued (both after the barrier that freed the
+    // stage). Issued here, ahead of the transposed reads, it spreads the group's nine operations
+    // over two phases; all of phase C it costs about 1 % more.
+    dma_tile(doh + (size_t)qb_carry * BLOCK * HEAD_DIM, toff, do_lds + ((st + 3) & 3) * STAGE_BYTES);
 
     // ---- phase B ----
     // transposed B operands of dV/dK for q block t: k slot jj of step s2 is q row
@@ -314,8 +325,10 @@ bwd_dkdv_kernel(BwdParams p) {
     // ---- mid ----
     // Every step issues one q block's DMA group (past the end of the list: a repeat of the last
     // q block, into a stage nobody reads again), so the group of t+3 is always the newest and
-    // nine outstanding operations mean q block t+2 has landed. No branch splits the step.
-    // (In spill mode the two dS stores of step t-1 sit between the groups of t+2 and t+3.)
+    // nine outstanding operations mean q block t+2 has landed: the group of t+2 ends with its dO
+    // tile (phase B of step t-1), and after it come the record, Q and dO of t+3. No branch splits
+    // the step. (In spill mode the two dS stores of step t-1 sit between the groups of t+2 and
+    // t+3.)
     // The list entry of q block t+4 was loaded after the previous barrier; the compiler-visible
     // lgkmcnt(0) tells the compiler that every LDS read issued so far is complete, so the scalar
     // load issued below for the next step adds no wait for them.
@@ -331,13 +344,14 @@ bwd_dkdv_kernel(BwdParams p) {
     }
     barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
     const int qb = clampq(raw);
+    qb_carry = qb;
     raw = entry(t + 5);     // in by the next step's barrier
 
     // ---- phase C ----
     // dV/dK MFMAs of t. Record and row reads of q block t+2 (records first: they seed the first
-    // MFMAs of the next step), with q block t+4's DMA group into stage st split in three and
-    // placed between them: the asm blocks keep their order relative to the reads, so the nine
-    // DMAs spread over the phase instead of reaching the address unit together.
+    // MFMAs of the next step), with q block t+4's record and Q tile DMAs into stage st placed
+    // between them: the asm blocks keep their order relative to the reads, so the DMAs spread
+    // over the phase instead of reaching the address unit together.
     {
       const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
       load_init(st2, sc, pc);
@@ -345,7 +359,6 @@ bwd_dkdv_kernel(BwdParams p) {
       load_rows(st2, 0);
       dma_tile(qh + tile, toff, q_lds + st * STAGE_BYTES);
       load_rows(st2, 4);
-      dma_tile(doh + tile, toff, do_lds + st * STAGE_BYTES);
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
