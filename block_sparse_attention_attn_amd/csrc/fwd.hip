@@ -132,12 +132,14 @@ fwd_kernel(FwdParams p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
     asm volatile("s_barrier" ::: "memory");
-    issue_k(e2, st);
-    issue_v(e1, st ^ 1);
     const int vb = vb0;
 
+    // Each DMA follows the LDS reads of its kind (the asm keeps its place among them), so the
+    // reads of this step are requested first and the two DMA groups reach the address unit
+    // apart: about 1.5 % faster than both groups right after the barrier.
     bf16x8 ka[8];
     read_k(st ^ 1, ka);
+    issue_k(e2, st);
     // V^T operands of O^T += V^T P^T: k-step c, slot j is kv 32wk + 16c + 8(j/4) + 4g + j%4 (the
     // D-layout order of S^T); d tile dt, lane's d = 32dt + l32
     const VSA_LDS char* vt = (const VSA_LDS char*)kv_s + (2 + st) * TILE;
@@ -152,6 +154,7 @@ fwd_kernel(FwdParams p) {
                          lds_read_tr(vt + tile_elem_byte(r0 + 8, col)));
       }
     }
+    issue_v(e1, st ^ 1);
 
     // softmax of block t. S^T element i is kv 32wk + 8(i/4) + 4g + i%4, q = this lane's column.
     float x[16];
