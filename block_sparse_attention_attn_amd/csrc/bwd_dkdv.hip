@@ -93,6 +93,21 @@ bwd_dkdv_kernel(BwdParams p) {
   int n = ld_const(p.k2q_num, item);
   n = n > p.k2q_stride ? p.k2q_stride : n;
   if (n <= 0) return;
+  // q-range chunk: this launch takes list positions [start, start + n) and adds to (first: starts)
+  // the fp32 partial sums of the chunks before, which the last chunk turns into dk, dv
+  int start = 0;
+  bool first = true, last = true;
+  if (p.nchunks > 0) {
+    const int32_t* cb = p.chunk_bounds + (size_t)item * (p.nchunks + 1) + p.chunk;
+    int b0 = ld_const(cb, 0), b1 = ld_const(cb, 1);
+    b0 = b0 < 0 ? 0 : (b0 > n ? n : b0);
+    b1 = b1 < b0 ? b0 : (b1 > n ? n : b1);
+    start = b0;
+    n = b1 - b0;
+    first = p.chunk == 0;
+    last = p.chunk == p.nchunks - 1;
+    if (n == 0 && !first && !last) return;  // nothing to add, nothing to finish
+  }
   const int bh = item / p.nb;
   const int j = item - bh * p.nb;
   const int vb = ld_const(p.vbs, j);
@@ -100,7 +115,7 @@ bwd_dkdv_kernel(BwdParams p) {
   const bf16* __restrict__ qh = p.q + head;
   const bf16* __restrict__ doh = p.dout + head;
   const float* __restrict__ recs = p.lse_delta + (size_t)bh * p.nb * LD_RECORD_FLOATS;
-  const int* __restrict__ list = p.k2q_idx + (size_t)item * p.k2q_stride;
+  const int* __restrict__ list = p.k2q_idx + (size_t)item * p.k2q_stride + start;
   // q block ids outside [0, nb) violate the caller contract; clamp them so no access leaves the
   // tensors (the result is then unspecified, but nothing faults)
   auto clampq = [&](int qb) { return qb < 0 ? 0 : (qb >= p.nb ? p.nb - 1 : qb); };
@@ -121,269 +136,273 @@ bwd_dkdv_kernel(BwdParams p) {
                       q_lds + st * STAGE_BYTES, do_lds + st * STAGE_BYTES, ld_lds + st * LD_BYTES);
   };
 
-  // ---- prologue ----
-  // K_j, V_j into stage 3 of the rings; q blocks 0, 1, 2 into stages 0, 1, 2.
-  {
-    const size_t tile = (size_t)j * BLOCK * HEAD_DIM;
-    dma_tile_pair(p.k + head + tile, p.v + head + tile, toff, q_lds + 3 * STAGE_BYTES,
-                  do_lds + 3 * STAGE_BYTES);
-  }
-  {
-    const int e0 = entry(0), e1 = entry(1), e2 = entry(2);
-    issue(clampq(e0), 0);
-    issue(clampq(e1), 1);  // (past the end of the list: repeats of the last q block)
-    issue(clampq(e2), 2);
-  }
-  // dS tiles (spill mode): q block t of this item goes to slot kbase[item] + t of its head. A
-  // lane stores its 16 dS values (two bf16x8) as one 32-byte record; the records of a wave's
-  // 32 kv rows are laid out so that the q-major kernel's transposed reads of two record groups
-  // fall on disjoint banks: record (w, g, l32) at ((8w + l32/4) * 256 + 128g + 32(l32%4)) bytes.
-  char* ds_item = nullptr;
-  int slot0 = 0;
-  const uint32_t ds_rec = ((8 * w + (l32 >> 2)) * 256 + 128 * g + 32 * (l32 & 3));
-  auto ds_tile = [&](int t) {
-    int slot = slot0 + t;
-    slot = slot < p.cap ? slot : p.cap - 1;  // inconsistent counts: stay inside the head
-    return ds_item + (size_t)slot * (BLOCK * BLOCK * 2);
-  };
-  if (SPILL) {
-    ds_item = (char*)p.ds + (size_t)bh * p.cap * (BLOCK * BLOCK * 2);
-    slot0 = ld_const(p.kbase, item);
-    // Two stores of zeros into q block 0's tile (rewritten at step 0: one wave's stores to one
-    // address land in order), so that every wait below counts the same two stores between the
-    // DMA groups of consecutive q blocks.
-    char* d = ds_tile(0) + ds_rec;
-    *(bf16x8*)d = bf16x8{};
-    *(bf16x8*)(d + 16) = bf16x8{};
-  }
-  const int e3 = entry(3);
-  // K/V and q blocks 0, 1 landed (own DMAs); q block 2's may still be in flight
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
-  barrier_lds_with(e3);  // ... everyone's
-  int raw = entry(4);    // the list entry step 0 fetches; in by step 0's barrier
-
-  // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
-  const int kv_l = 32 * wk + l32;
-  const bool kv_valid = kv_l < vb;
-  bf16x8 kf[8], vf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int b = 3 * STAGE_BYTES + tile_byte(kv_l, 2 * s + g);
-    kf[s] = *(const VSA_LDS bf16x8*)(qr + b);
-    vf[s] = *(const VSA_LDS bf16x8*)(dr + b);
-  }
-  if (!kv_valid) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kf[s] = bf16x8{};
-      vf[s] = bf16x8{};
-    }
-  }
-
   f32x16 dv_acc[4], dk_acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     dv_acc[nt] = f32x16{};
     dk_acc[nt] = f32x16{};
   }
-  const float scale_log2 = p.scale_log2;
-  const int qrow = 32 * wq + l32;
-
-  // A operands of S = Q K^T and dP = dO V^T for the q block in stage st: q rows 32*wq + l32,
-  // d = 16*s + 8*g + 0..7
-  bf16x8 qa[8], da[8];
-  auto load_rows = [&](int st, int sb) __attribute__((always_inline)) {  // steps sb .. sb+3
-    VSA_LDS char* qt = qr + st * STAGE_BYTES;
-    VSA_LDS char* dt = dr + st * STAGE_BYTES;
-#pragma unroll
-    for (int s = sb; s < sb + 4; ++s) {
-      qa[s] = *(const VSA_LDS bf16x8*)(qt + tile_byte(qrow, 2 * s + g));
-      da[s] = *(const VSA_LDS bf16x8*)(dt + tile_byte(qrow, 2 * s + g));
+  // An empty chunk (first or last of several) only starts or finishes the partial sums.
+  if (n > 0) {
+    // ---- prologue ----
+    // K_j, V_j into stage 3 of the rings; q blocks 0, 1, 2 into stages 0, 1, 2.
+    {
+      const size_t tile = (size_t)j * BLOCK * HEAD_DIM;
+      dma_tile_pair(p.k + head + tile, p.v + head + tile, toff, q_lds + 3 * STAGE_BYTES,
+                    do_lds + 3 * STAGE_BYTES);
     }
-  };
-  // Initial accumulators of the q block in stage st from its record: element i of S / dP is
-  // q row 32*wq + 8*(i/4) + 4*g + i%4.
-  auto load_init = [&](int st, f32x16& sa_, f32x16& pa_) __attribute__((always_inline)) {
-    const VSA_LDS float* ld = (const VSA_LDS float*)(lr + st * LD_BYTES);
+    {
+      const int e0 = entry(0), e1 = entry(1), e2 = entry(2);
+      issue(clampq(e0), 0);
+      issue(clampq(e1), 1);  // (past the end of the list: repeats of the last q block)
+      issue(clampq(e2), 2);
+    }
+    // dS tiles (spill mode): q block t of this item goes to slot kbase[item] + t of its head. A
+    // lane stores its 16 dS values (two bf16x8) as one 32-byte record; the records of a wave's
+    // 32 kv rows are laid out so that the q-major kernel's transposed reads of two record groups
+    // fall on disjoint banks: record (w, g, l32) at ((8w + l32/4) * 256 + 128g + 32(l32%4)) bytes.
+    char* ds_item = nullptr;
+    int slot0 = 0;
+    const uint32_t ds_rec = ((8 * w + (l32 >> 2)) * 256 + 128 * g + 32 * (l32 & 3));
+    auto ds_tile = [&](int t) {
+      int slot = slot0 + t;
+      slot = slot < p.cap ? slot : p.cap - 1;  // inconsistent counts: stay inside the head
+      return ds_item + (size_t)slot * (BLOCK * BLOCK * 2);
+    };
+    if (SPILL) {
+      ds_item = (char*)p.ds + (size_t)bh * p.cap * (BLOCK * BLOCK * 2);
+      slot0 = ld_const(p.kbase, item) + start;
+      // Two stores of zeros into q block 0's tile (rewritten at step 0: one wave's stores to one
+      // address land in order), so that every wait below counts the same two stores between the
+      // DMA groups of consecutive q blocks.
+      char* d = ds_tile(0) + ds_rec;
+      *(bf16x8*)d = bf16x8{};
+      *(bf16x8*)(d + 16) = bf16x8{};
+    }
+    const int e3 = entry(3);
+    // K/V and q blocks 0, 1 landed (own DMAs); q block 2's may still be in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
+    barrier_lds_with(e3);  // ... everyone's
+    int raw = entry(4);    // the list entry step 0 fetches; in by step 0's barrier
+
+    // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
+    const int kv_l = 32 * wk + l32;
+    const bool kv_valid = kv_l < vb;
+    bf16x8 kf[8], vf[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int q = 32 * wq + 8 * c + 4 * g;
-      const f32x4 a = *(const VSA_LDS f32x4*)(ld + q);
-      const f32x4 b = *(const VSA_LDS f32x4*)(ld + BLOCK + q);
+    for (int s = 0; s < 8; ++s) {
+      const int b = 3 * STAGE_BYTES + tile_byte(kv_l, 2 * s + g);
+      kf[s] = *(const VSA_LDS bf16x8*)(qr + b);
+      vf[s] = *(const VSA_LDS bf16x8*)(dr + b);
+    }
+    if (!kv_valid) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sa_[4 * c + e] = a[e];
-        pa_[4 * c + e] = b[e];
+      for (int s = 0; s < 8; ++s) {
+        kf[s] = bf16x8{};
+        vf[s] = bf16x8{};
       }
     }
-  };
 
-  // LDS byte addresses of the transposed reads below, one per (column group nt, row half h) and
-  // ring: the q half (16 rows), the stage and the ring base differ only by constants, which the
-  // reads carry as immediate offsets (the empty asm keeps the compiler from re-deriving the dO
-  // addresses from the Q ones, which would cost an add per read: the dO ring starts at 64 KiB,
-  // past the reach of an immediate).
-  uint32_t trq[4][2], trd[4][2];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int off = tile_elem_byte(32 * wq + 4 * (grp >> 1) + (t16 >> 2) + 8 * h,
-                                     32 * nt + 16 * (grp & 1) + 4 * (t16 & 3));
-      trq[nt][h] = lds_addr(qr) + off;
-      trd[nt][h] = lds_addr(dr) + off;
-      asm volatile("" : "+v"(trq[nt][h]), "+v"(trd[nt][h]));
-    }
-  }
-  auto rd_tr = [](uint32_t a) { return lds_read_tr((const VSA_LDS void*)(uintptr_t)a); };
+    const float scale_log2 = p.scale_log2;
+    const int qrow = 32 * wq + l32;
 
-  f32x16 s0, p0, s1, p1;
-  load_rows(0, 0);
-  load_rows(0, 4);
-  load_init(0, s0, p0);
-  barrier_lds();  // everyone has read K/V out of stage 3
-  // q block 3's record and Q tile; step 0's phase B issues its dO tile (see the step below)
-  {
-    const int qb3 = clampq(e3);
-    dma_rec128(recs + (size_t)qb3 * LD_RECORD_FLOATS, roff, ld_lds + 3 * LD_BYTES);
-    dma_tile(qh + (size_t)qb3 * BLOCK * HEAD_DIM, toff, q_lds + 3 * STAGE_BYTES);
-  }
+    // A operands of S = Q K^T and dP = dO V^T for the q block in stage st: q rows 32*wq + l32,
+    // d = 16*s + 8*g + 0..7
+    bf16x8 qa[8], da[8];
+    auto load_rows = [&](int st, int sb) __attribute__((always_inline)) {  // steps sb .. sb+3
+      VSA_LDS char* qt = qr + st * STAGE_BYTES;
+      VSA_LDS char* dt = dr + st * STAGE_BYTES;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    s0 = mfma32(qa[s], kf[s], s0);
-    p0 = mfma32(da[s], vf[s], p0);
-  }
-  load_rows(1, 0);  // a repeat of q block 0 when n == 1
-  load_rows(1, 4);
-  load_init(1, s1, p1);
-
-  // Step t (q block t in stage st = t % 4): on entry (sc, pc) hold S - lse/scale_log2 and
-  // dP - Delta of q block t, (sn, pn) the initial values of q block t+1 and (qa, da) its rows.
-  //   phase B: the dO DMA of q block t+3, then the S/dP MFMAs of t+1, interleaved with the
-  //            transposed dO^T, Q^T reads of t and P, dS of t;
-  //   mid:     q block t+2 has landed (own DMAs, then the barrier: everyone's) and everyone is
-  //            done with stage st, which then receives q block t+4;
-  //   phase C: dV/dK MFMAs of t, interleaved with the record and row reads of t+2 into (sc, pc)
-  //            and (qa, da) and the record and Q DMAs of q block t+4.
-  // The last steps compute throwaway S/dP from repeated q blocks, which keeps the body free of
-  // branches. The loop is unrolled by four so stage offsets are constants.
-  int qb_carry = clampq(e3);  // the q block whose dO tile the next phase B fetches
-  auto step = [&](int t, int st, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn)
-                  __attribute__((always_inline)) {
-    const int st2 = (st + 2) & 3;
-    // dO tile of q block t+3 into stage (t+3)%4, the second half of the DMA group whose record
-    // and Q tile phase C of the previous step issued (both after the barrier that freed the
-    // stage). Issued here, ahead of the transposed reads, it spreads the group's nine operations
-    // over two phases; all of phase C it costs about 1 % more.
-    dma_tile(doh + (size_t)qb_carry * BLOCK * HEAD_DIM, toff, do_lds + ((st + 3) & 3) * STAGE_BYTES);
-
-    // ---- phase B ----
-    // transposed B operands of dV/dK for q block t: k slot jj of step s2 is q row
-    // 32*wq + 16*s2 + 8*(jj/4) + 4*g + jj%4, matching the D layout of S
-    bf16x8 db[2][4], qbt[2][4];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const uint32_t o = st * STAGE_BYTES + s2 * 16 * 256;  // stage, then 16 rows further down
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        db[s2][nt] = join(rd_tr(trd[nt][0] + o), rd_tr(trd[nt][1] + o));
-        qbt[s2][nt] = join(rd_tr(trq[nt][0] + o), rd_tr(trq[nt][1] + o));
+      for (int s = sb; s < sb + 4; ++s) {
+        qa[s] = *(const VSA_LDS bf16x8*)(qt + tile_byte(qrow, 2 * s + g));
+        da[s] = *(const VSA_LDS bf16x8*)(dt + tile_byte(qrow, 2 * s + g));
       }
+    };
+    // Initial accumulators of the q block in stage st from its record: element i of S / dP is
+    // q row 32*wq + 8*(i/4) + 4*g + i%4.
+    auto load_init = [&](int st, f32x16& sa_, f32x16& pa_) __attribute__((always_inline)) {
+      const VSA_LDS float* ld = (const VSA_LDS float*)(lr + st * LD_BYTES);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int q = 32 * wq + 8 * c + 4 * g;
+        const f32x4 a = *(const VSA_LDS f32x4*)(ld + q);
+        const f32x4 b = *(const VSA_LDS f32x4*)(ld + BLOCK + q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sa_[4 * c + e] = a[e];
+          pa_[4 * c + e] = b[e];
+        }
+      }
+    };
+
+    // LDS byte addresses of the transposed reads below, one per (column group nt, row half h) and
+    // ring: the q half (16 rows), the stage and the ring base differ only by constants, which the
+    // reads carry as immediate offsets (the empty asm keeps the compiler from re-deriving the dO
+    // addresses from the Q ones, which would cost an add per read: the dO ring starts at 64 KiB,
+    // past the reach of an immediate).
+    uint32_t trq[4][2], trd[4][2];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int off = tile_elem_byte(32 * wq + 4 * (grp >> 1) + (t16 >> 2) + 8 * h,
+                                       32 * nt + 16 * (grp & 1) + 4 * (t16 & 3));
+        trq[nt][h] = lds_addr(qr) + off;
+        trd[nt][h] = lds_addr(dr) + off;
+        asm volatile("" : "+v"(trq[nt][h]), "+v"(trd[nt][h]));
+      }
+    }
+    auto rd_tr = [](uint32_t a) { return lds_read_tr((const VSA_LDS void*)(uintptr_t)a); };
+
+    f32x16 s0, p0, s1, p1;
+    load_rows(0, 0);
+    load_rows(0, 4);
+    load_init(0, s0, p0);
+    barrier_lds();  // everyone has read K/V out of stage 3
+    // q block 3's record and Q tile; step 0's phase B issues its dO tile (see the step below)
+    {
+      const int qb3 = clampq(e3);
+      dma_rec128(recs + (size_t)qb3 * LD_RECORD_FLOATS, roff, ld_lds + 3 * LD_BYTES);
+      dma_tile(qh + (size_t)qb3 * BLOCK * HEAD_DIM, toff, q_lds + 3 * STAGE_BYTES);
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      sn = mfma32(qa[s], kf[s], sn);
-      pn = mfma32(da[s], vf[s], pn);
+      s0 = mfma32(qa[s], kf[s], s0);
+      p0 = mfma32(da[s], vf[s], p0);
     }
-    // P and dS of q block t, half h (elements 8h .. 8h+7: q rows 32*wq + 16h + ..) in bf16. A
-    // padded kv column (zero K/V fragment) gets some finite or non-finite P; it only feeds that
-    // kv row of dV/dK, which the epilogue overwrites with 0.
-    bf16x8 pa[2], sa[2];
-    auto softmax_half = [&](int h) __attribute__((always_inline)) {
-      float pv[8], dsv[8];
+    load_rows(1, 0);  // a repeat of q block 0 when n == 1
+    load_rows(1, 4);
+    load_init(1, s1, p1);
+
+    // Step t (q block t in stage st = t % 4): on entry (sc, pc) hold S - lse/scale_log2 and
+    // dP - Delta of q block t, (sn, pn) the initial values of q block t+1 and (qa, da) its rows.
+    //   phase B: the dO DMA of q block t+3, then the S/dP MFMAs of t+1, interleaved with the
+    //            transposed dO^T, Q^T reads of t and P, dS of t;
+    //   mid:     q block t+2 has landed (own DMAs, then the barrier: everyone's) and everyone is
+    //            done with stage st, which then receives q block t+4;
+    //   phase C: dV/dK MFMAs of t, interleaved with the record and row reads of t+2 into (sc, pc)
+    //            and (qa, da) and the record and Q DMAs of q block t+4.
+    // The last steps compute throwaway S/dP from repeated q blocks, which keeps the body free of
+    // branches. The loop is unrolled by four so stage offsets are constants.
+    int qb_carry = clampq(e3);  // the q block whose dO tile the next phase B fetches
+    auto step = [&](int t, int st, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn)
+                    __attribute__((always_inline)) {
+      const int st2 = (st + 2) & 3;
+      // dO tile of q block t+3 into stage (t+3)%4, the second half of the DMA group whose record
+      // and Q tile phase C of the previous step issued (both after the barrier that freed the
+      // stage). Issued here, ahead of the transposed reads, it spreads the group's nine operations
+      // over two phases; all of phase C it costs about 1 % more.
+      dma_tile(doh + (size_t)qb_carry * BLOCK * HEAD_DIM, toff,
+               do_lds + ((st + 3) & 3) * STAGE_BYTES);
+
+      // ---- phase B ----
+      // transposed B operands of dV/dK for q block t: k slot jj of step s2 is q row
+      // 32*wq + 16*s2 + 8*(jj/4) + 4*g + jj%4, matching the D layout of S
+      bf16x8 db[2][4], qbt[2][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(sc[8 * h + e] * scale_log2);
-        dsv[e] = pv[e] * pc[8 * h + e];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint32_t o = st * STAGE_BYTES + s2 * 16 * 256;  // stage, then 16 rows further down
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          db[s2][nt] = join(rd_tr(trd[nt][0] + o), rd_tr(trd[nt][1] + o));
+          qbt[s2][nt] = join(rd_tr(trq[nt][0] + o), rd_tr(trq[nt][1] + o));
+        }
       }
-      pa[h] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      sa[h] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sn = mfma32(qa[s], kf[s], sn);
+        pn = mfma32(da[s], vf[s], pn);
+      }
+      // P and dS of q block t, half h (elements 8h .. 8h+7: q rows 32*wq + 16h + ..) in bf16. A
+      // padded kv column (zero K/V fragment) gets some finite or non-finite P; it only feeds that
+      // kv row of dV/dK, which the epilogue overwrites with 0.
+      bf16x8 pa[2], sa[2];
+      auto softmax_half = [&](int h) __attribute__((always_inline)) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(sc[8 * h + e] * scale_log2);
+          dsv[e] = pv[e] * pc[8 * h + e];
+        }
+        pa[h] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        sa[h] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      };
+      // Under the S/dP MFMAs; the empty asm keeps this arithmetic in this phase (it is otherwise
+      // free to sink next to its use after the barrier).
+      softmax_half(0);
+      softmax_half(1);
+      asm volatile("" : "+v"(pa[0]), "+v"(sa[0]), "+v"(pa[1]), "+v"(sa[1]));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- mid ----
+      // Every step issues one q block's DMA group (past the end of the list: a repeat of the last
+      // q block, into a stage nobody reads again), so the group of t+3 is always the newest and
+      // nine outstanding operations mean q block t+2 has landed: the group of t+2 ends with its dO
+      // tile (phase B of step t-1), and after it come the record, Q and dO of t+3. No branch splits
+      // the step. (In spill mode the two dS stores of step t-1 sit between the groups of t+2 and
+      // t+3.)
+      // The list entry of q block t+4 was loaded after the previous barrier; the compiler-visible
+      // lgkmcnt(0) tells the compiler that every LDS read issued so far is complete, so the scalar
+      // load issued below for the next step adds no wait for them.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      // The dS tile of q block t (spill mode) goes out here, between this wave's wait and the
+      // barrier, where the wave would otherwise idle until the others arrive; stores issued inside
+      // phase C delay its MFMAs and DMAs.
+      if (SPILL) {  // streamed past the caches: read once, by the q-major kernel
+        char* d = ds_tile(t) + ds_rec;
+        __builtin_nontemporal_store(sa[0], (bf16x8*)d);
+        __builtin_nontemporal_store(sa[1], (bf16x8*)(d + 16));
+      }
+      barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
+      const int qb = clampq(raw);
+      qb_carry = qb;
+      raw = entry(t + 5);     // in by the next step's barrier
+
+      // ---- phase C ----
+      // dV/dK MFMAs of t. Record and row reads of q block t+2 (records first: they seed the first
+      // MFMAs of the next step), with q block t+4's record and Q tile DMAs into stage st placed
+      // between them: the asm blocks keep their order relative to the reads, so the DMAs spread
+      // over the phase instead of reaching the address unit together.
+      {
+        const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
+        load_init(st2, sc, pc);
+        dma_rec128(recs + (size_t)qb * LD_RECORD_FLOATS, roff, ld_lds + st * LD_BYTES);
+        load_rows(st2, 0);
+        dma_tile(qh + tile, toff, q_lds + st * STAGE_BYTES);
+        load_rows(st2, 4);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        dv_acc[nt] = mfma32(pa[0], db[0][nt], dv_acc[nt]);
+        dk_acc[nt] = mfma32(sa[0], qbt[0][nt], dk_acc[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        dv_acc[nt] = mfma32(pa[1], db[1][nt], dv_acc[nt]);
+        dk_acc[nt] = mfma32(sa[1], qbt[1][nt], dk_acc[nt]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three record / row reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
-    // Under the S/dP MFMAs; the empty asm keeps this arithmetic in this phase (it is otherwise
-    // free to sink next to its use after the barrier).
-    softmax_half(0);
-    softmax_half(1);
-    asm volatile("" : "+v"(pa[0]), "+v"(sa[0]), "+v"(pa[1]), "+v"(sa[1]));
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
+    for (int t = 0; t < n; t += 4) {
+      step(t, 0, s0, p0, s1, p1);
+      if (t + 1 < n) step(t + 1, 1, s1, p1, s0, p0);
+      if (t + 2 < n) step(t + 2, 2, s0, p0, s1, p1);
+      if (t + 3 < n) step(t + 3, 3, s1, p1, s0, p0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- mid ----
-    // Every step issues one q block's DMA group (past the end of the list: a repeat of the last
-    // q block, into a stage nobody reads again), so the group of t+3 is always the newest and
-    // nine outstanding operations mean q block t+2 has landed: the group of t+2 ends with its dO
-    // tile (phase B of step t-1), and after it come the record, Q and dO of t+3. No branch splits
-    // the step. (In spill mode the two dS stores of step t-1 sit between the groups of t+2 and
-    // t+3.)
-    // The list entry of q block t+4 was loaded after the previous barrier; the compiler-visible
-    // lgkmcnt(0) tells the compiler that every LDS read issued so far is complete, so the scalar
-    // load issued below for the next step adds no wait for them.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    // The dS tile of q block t (spill mode) goes out here, between this wave's wait and the
-    // barrier, where the wave would otherwise idle until the others arrive; stores issued inside
-    // phase C delay its MFMAs and DMAs.
-    if (SPILL) {  // streamed past the caches: read once, by the q-major kernel
-      char* d = ds_tile(t) + ds_rec;
-      __builtin_nontemporal_store(sa[0], (bf16x8*)d);
-      __builtin_nontemporal_store(sa[1], (bf16x8*)(d + 16));
-    }
-    barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
-    const int qb = clampq(raw);
-    qb_carry = qb;
-    raw = entry(t + 5);     // in by the next step's barrier
-
-    // ---- phase C ----
-    // dV/dK MFMAs of t. Record and row reads of q block t+2 (records first: they seed the first
-    // MFMAs of the next step), with q block t+4's record and Q tile DMAs into stage st placed
-    // between them: the asm blocks keep their order relative to the reads, so the DMAs spread
-    // over the phase instead of reaching the address unit together.
-    {
-      const size_t tile = (size_t)qb * BLOCK * HEAD_DIM;
-      load_init(st2, sc, pc);
-      dma_rec128(recs + (size_t)qb * LD_RECORD_FLOATS, roff, ld_lds + st * LD_BYTES);
-      load_rows(st2, 0);
-      dma_tile(qh + tile, toff, q_lds + st * STAGE_BYTES);
-      load_rows(st2, 4);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      dv_acc[nt] = mfma32(pa[0], db[0][nt], dv_acc[nt]);
-      dk_acc[nt] = mfma32(sa[0], qbt[0][nt], dk_acc[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      dv_acc[nt] = mfma32(pa[1], db[1][nt], dv_acc[nt]);
-      dk_acc[nt] = mfma32(sa[1], qbt[1][nt], dk_acc[nt]);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three record / row reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  for (int t = 0; t < n; t += 4) {
-    step(t, 0, s0, p0, s1, p1);
-    if (t + 1 < n) step(t + 1, 1, s1, p1, s0, p0);
-    if (t + 2 < n) step(t + 2, 2, s0, p0, s1, p1);
-    if (t + 3 < n) step(t + 3, 3, s1, p1, s0, p0);
-  }
+  }  // n > 0
 
   // ---- sum the two q halves of dV/dK through LDS, scale, round, store ----
   // the repeats issued by the last four steps are still in flight: wait, then meet
@@ -407,6 +426,8 @@ bwd_dkdv_kernel(BwdParams p) {
   barrier_lds();
   bf16* outp = (wq == 0 ? p.dv : p.dk) + head + (size_t)j * BLOCK * HEAD_DIM;
   const float oscale = wq == 0 ? 1.0f : p.sm_scale;
+  // this wave's tensor (dV for wq 0, dK for wq 1) in the chunk partial sums: [64][128] fp32
+  float* part = p.dkv_part ? p.dkv_part + ((size_t)item * 2 + wq) * (BLOCK * HEAD_DIM) : nullptr;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int d = 32 * nt + l32;
@@ -417,8 +438,12 @@ bwd_dkdv_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e) {
         const float mine = wq == 0 ? dv_acc[nt][4 * c + e] : dk_acc[nt][4 * c + e];
         const int kv = 32 * wk + 8 * c + 4 * g + e;
-        // padded kv rows are exactly zero by definition
-        outp[(size_t)kv * HEAD_DIM + d] = kv < vb ? (bf16)((mine + o[e]) * oscale) : (bf16)0.0f;
+        float sum = mine + o[e];
+        if (!first) sum += part[kv * HEAD_DIM + d];
+        if (last)  // padded kv rows are exactly zero by definition
+          outp[(size_t)kv * HEAD_DIM + d] = kv < vb ? (bf16)(sum * oscale) : (bf16)0.0f;
+        else
+          part[kv * HEAD_DIM + d] = sum;
       }
     }
   }

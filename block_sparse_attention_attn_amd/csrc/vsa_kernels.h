@@ -95,12 +95,25 @@ struct BwdParams {
   const int64_t* qent;   // [BH*nb, qent_stride]: slot | kv << 32 | vbs[kv] << 48
   bf16* ds;              // [BH, cap, 64*64]
   int cap, qent_stride;  // slots per head (nb * K'), q2k row width K'
+  // q-range chunks of the kv-major kernel (nchunks 0: one launch over whole lists): this launch
+  // takes list positions [bounds[item][chunk], bounds[item][chunk+1]) and carries dV, dK
+  // (unscaled fp32, [item][2][64][128]) in dkv_part from chunk to chunk
+  const int32_t* chunk_bounds;  // [total_items, nchunks + 1]
+  float* dkv_part;
+  int chunk, nchunks;
   int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
   float scale_log2, sm_scale;
 };
 void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 void launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 void launch_bwd_dq_spill(const BwdParams& p, hipStream_t stream);
+
+// ---- q-range chunk bounds: bounds[item][c] = first position of the item's (ascending) k2q list
+// whose q block is >= c * chunk_q, for c = 0 .. nchunks (so bounds[item][nchunks] = the list
+// length, clamped to [0, k2q_stride]) ----
+void launch_chunk_bounds(const int32_t* k2q_idx, const int32_t* k2q_num, int k2q_stride,
+                         int total_items, int nchunks, int chunk_q, int32_t* bounds,
+                         hipStream_t stream);
 
 // ---- dS slot tables (spill mode) ----
 // kbase[bh, kv] = sum of min(max(k2q_num, 0), k2q_stride) over the kv blocks before kv in head bh:

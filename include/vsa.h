@@ -134,7 +134,25 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *                    (exclusive prefix sum of k2q_num inside the head)
  *   VSA_WS_QENT      int64 [B, H, nb, K']: per q2k entry, its dS slot | kv block << 32 |
  *                    vbs[kv block] << 48
- *   VSA_WS_DS        bf16 [B, H, nb*K', 64, 64]: the dS tiles, slot-major */
+ *   VSA_WS_DS        bf16 [B, H, nb*K', 64, 64]: the dS tiles, slot-major
+ * only when the kv-major kernel runs in q-range chunks (below), with C chunks:
+ *   VSA_WS_CHUNK_BOUNDS int32 [B*H*nb, C+1]: per kv item, the position in its k2q list of the
+ *                    first q block of each chunk (the last entry is the list length)
+ *   VSA_WS_DKV_PART  fp32 [B*H*nb, 2, 64, 128]: per kv item, dV then dK (unscaled) summed over
+ *                    the chunks so far
+ *
+ * q-range chunks (q_chunk_blocks argument; 0 = the library's choice): with R = q_chunk_blocks
+ * (> 0), or R = VSA_CHUNK_Q_BLOCKS from VSA_CHUNK_MIN_KV_BLOCKS kv blocks per sequence on when
+ * it is 0, the kv-major kernel runs as C = ceil(nb / R) launches; launch c takes, of every k2q
+ * list, the q blocks in [c*R, (c+1)*R) and carries dK and dV to the next launch in fp32 in the
+ * workspace. The items running together on one XCD then walk a window of R q blocks at a time,
+ * so the Q/dO tiles they share stay in its L2; without chunks, ascending walks of thousands of
+ * entries drift apart and almost every Q/dO tile comes from HBM (the pages' long-sequence
+ * cache-locality mode serves the same purpose). q_chunk_blocks < 0: never chunk. Chunking
+ * changes only the fp32 summation order of dK and dV (one partial sum per chunk); dq is
+ * unaffected. */
+#define VSA_CHUNK_MIN_KV_BLOCKS 4096
+#define VSA_CHUNK_Q_BLOCKS 1024
 #define VSA_ORDER_MIN_KV_BLOCKS 64
 #define VSA_ORDER_BIN_WIDTH 4
 #define VSA_ORDER_MAX_KV_BLOCKS 16384
@@ -149,7 +167,9 @@ typedef enum {
   VSA_WS_KBASE = 6,
   VSA_WS_QENT = 7,
   VSA_WS_DS = 8,
-  VSA_WS_END = 9
+  VSA_WS_CHUNK_BOUNDS = 9,
+  VSA_WS_DKV_PART = 10,
+  VSA_WS_END = 11
 } vsa_bwd_ws_region;
 
 typedef enum { VSA_DQ_RECOMPUTE = 0, VSA_DQ_SPILL = 1 } vsa_dq_mode;
@@ -175,16 +195,18 @@ typedef struct {
   int batch, heads, seqlen, head_dim, num_kv_blocks, max_q_blocks, q2k_stride;
   float sm_scale;
   int dq_mode;            /* vsa_dq_mode */
+  int q_chunk_blocks;     /* q-range chunks of the kv-major kernel, see above; 0 = default */
 } vsa_bwd_args;
 
 /* Bytes of workspace for a backward call. q2k_stride: the row width of the q2k lists the call
- * passes, or 0 when q2k_idx/q2k_num are NULL (derived); dq_mode: a vsa_dq_mode. 0 for an invalid
- * shape. */
-size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int q2k_stride, int dq_mode);
+ * passes, or 0 when q2k_idx/q2k_num are NULL (derived); dq_mode: a vsa_dq_mode; q_chunk_blocks:
+ * as in vsa_bwd_args. 0 for an invalid shape. */
+size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
+                               int q_chunk_blocks);
 /* Byte offset of a workspace region (vsa_bwd_ws_region) for the same arguments; VSA_WS_END gives
  * the total. */
 size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
-                                int region);
+                                int q_chunk_blocks, int region);
 /* Host-only validation of a backward call; reads no device memory. */
 int vsa_bwd_check(const vsa_bwd_args* a);
 int vsa_bwd(const vsa_bwd_args* a, void* stream);
@@ -193,15 +215,18 @@ int vsa_bwd(const vsa_bwd_args* a, void* stream);
  * validates like vsa_bwd. Run on one stream in the order PREPROCESS, INDEX, DKDV, DQ, they
  * enqueue exactly the kernels vsa_bwd enqueues and produce the same results. INDEX derives the
  * q2k lists when they are not given, computes the work orders when num_kv_blocks is in
- * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS] and builds the dS slot tables in
- * VSA_DQ_SPILL mode; otherwise it enqueues nothing. In VSA_DQ_RECOMPUTE mode DKDV and DQ only read
+ * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS], builds the dS slot tables in
+ * VSA_DQ_SPILL mode and the chunk bounds when the kv-major kernel runs in q-range chunks;
+ * otherwise it enqueues nothing. In VSA_DQ_RECOMPUTE mode DKDV and DQ only read
  * what PREPROCESS and INDEX wrote and may run in either order; in VSA_DQ_SPILL mode DQ reads the
  * dS tiles DKDV writes and must follow it. */
 typedef enum {
   VSA_BWD_PREPROCESS = 0,  /* Delta; zero dk/dv rows of kv blocks with an empty k2q list */
-  VSA_BWD_INDEX = 1,       /* q2k derivation (if needed), the length-binned work orders and,
-                              in VSA_DQ_SPILL mode, the dS slot tables */
-  VSA_BWD_DKDV = 2,        /* kv-major kernel: dk, dv (and the dS tiles in VSA_DQ_SPILL mode) */
+  VSA_BWD_INDEX = 1,       /* q2k derivation (if needed), the length-binned work orders, in
+                              VSA_DQ_SPILL mode the dS slot tables, with q-range chunks the
+                              chunk bounds */
+  VSA_BWD_DKDV = 2,        /* kv-major kernel (one launch per q-range chunk): dk, dv (and the
+                              dS tiles in VSA_DQ_SPILL mode) */
   VSA_BWD_DQ = 3           /* q-major kernel: dq = bf16(sm_scale * dS K) */
 } vsa_bwd_stage_id;
 int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream);

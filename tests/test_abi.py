@@ -36,7 +36,9 @@ def test_library_exports_every_declared_function():
 def test_binding_constants_match_the_header():
     text = open(HEADER).read()
     for name, value in (("VSA_ORDER_MIN_KV_BLOCKS", V.ORDER_MIN_KV_BLOCKS),
-                        ("VSA_ORDER_BIN_WIDTH", V.ORDER_BIN_WIDTH)):
+                        ("VSA_ORDER_BIN_WIDTH", V.ORDER_BIN_WIDTH),
+                        ("VSA_CHUNK_MIN_KV_BLOCKS", V.CHUNK_MIN_KV_BLOCKS),
+                        ("VSA_CHUNK_Q_BLOCKS", V.CHUNK_Q_BLOCKS)):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == value, name
 
@@ -82,6 +84,29 @@ def test_workspace_sizes_and_layout():
                        for r in range(V.WS_END + 1))
     assert V.bwd_workspace_bytes(0, 1, 64) == 0
     assert V.bwd_workspace_bytes(1, 1, 64, 0, 7) == 0  # unknown mode
+
+
+def test_workspace_chunk_regions():
+    def offs(B, H, S, kq, chunk):
+        return [V.bwd_workspace_offset(B, H, S, r, kq, V.DQ_RECOMPUTE, chunk)
+                for r in range(V.WS_END + 1)]
+    a256 = lambda x: (x + 255) // 256 * 256
+    # below the default threshold: no chunk regions
+    o = offs(1, 8, 64 * 512, 128, 0)
+    assert o[V.WS_CHUNK_BOUNDS] == o[V.WS_DKV_PART] == o[V.WS_END] == o[V.WS_DS]
+    # from the threshold on, chunks of CHUNK_Q_BLOCKS q blocks: bounds and fp32 dV/dK sums
+    nb = V.CHUNK_MIN_KV_BLOCKS
+    o = offs(1, 2, 64 * nb, 128, 0)
+    c = -(-nb // V.CHUNK_Q_BLOCKS)
+    assert o[V.WS_DKV_PART] - o[V.WS_CHUNK_BOUNDS] == a256(2 * nb * (c + 1) * 4)
+    assert o[V.WS_END] - o[V.WS_DKV_PART] == 2 * nb * 2 * 64 * 128 * 4
+    assert V.bwd_workspace_bytes(1, 2, 64 * nb, 128, V.DQ_RECOMPUTE, -1) == o[V.WS_CHUNK_BOUNDS]
+    # a forced chunk size at any size; one chunk covering every q block is no chunk
+    o = offs(1, 1, 64 * 10, 0, 3)
+    assert o[V.WS_DKV_PART] - o[V.WS_CHUNK_BOUNDS] == a256(10 * 5 * 4)
+    assert o[V.WS_END] - o[V.WS_DKV_PART] == 10 * 2 * 64 * 128 * 4
+    o = offs(1, 1, 64 * 10, 0, 10)
+    assert o[V.WS_END] == o[V.WS_CHUNK_BOUNDS]
     assert V.invert_workspace_bytes(2, 3, 100, 50) == ((2 * 3 * 50 * 4 * 4 + 255) // 256) * 256
     assert V.invert_workspace_bytes(1, 1, 0, 1) == 0
 

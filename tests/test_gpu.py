@@ -307,6 +307,53 @@ def test_backward_edge_cases(name, mode):
         assert np.all(got.float().cpu().numpy()[zero] == 0)
 
 
+@pytest.mark.parametrize("mode", sorted(MODES))
+@pytest.mark.parametrize("case,chunk", [(2, 3), (2, 1), ("odd_blocks_ragged", 2),
+                                        ("empty_q_blocks", 4), ("pool_excludes_three", 5)])
+def test_backward_q_range_chunks(case, chunk, mode):
+    """The kv-major kernel in q-range chunks (q_chunk_blocks): the chunk bounds bit-exact
+    (positions of the chunk starts in each ascending k2q row, from numpy's searchsorted), dq
+    bit-identical to the one-launch call (chunks do not touch the dQ path), dk/dv within the
+    oracle's tolerance, equal to the one-launch results up to the fp32 summation order, and
+    exactly zero wherever the oracle is (unselected kv blocks, padded rows)."""
+    if case == 2:
+        c = workloads.config(2)
+    else:
+        B, H, nb, topk, vbs, pool, empty = EDGE_CASES[case]
+        c = workloads.make_case(B, H, nb, topk, seed=17, vbs=vbs, kv_pool=pool, name=case)
+        for b, h, qb in empty:
+            c.q2k_num[b, h, qb] = 0
+    d = to_dev(c)
+    ro, rl = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    o = torch.from_numpy(O.bf16_rne(ro)).to(torch.bfloat16).to(DEV)
+    lse = torch.from_numpy(rl).to(torch.float32).to(DEV)
+    ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
+    k2q_idx, k2q_num = torch.from_numpy(ridx).to(DEV), torch.from_numpy(rnum).to(DEV)
+    say(f"[backward] {case}, q-range chunks of {chunk} q blocks, dq mode {mode}")
+    runs = {}
+    for qc in (-1, chunk):
+        plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                         out=(nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"])),
+                         dq_mode=MODES[mode], q_chunk_blocks=qc)
+        runs[qc] = plan.run()
+        torch.cuda.synchronize()
+    nch = -(-c.nb // chunk)
+    bounds = plan.region(V.WS_CHUNK_BOUNDS, c.B * c.H * c.nb * (nch + 1)).cpu().numpy()
+    rows = ridx.reshape(-1, ridx.shape[-1])
+    want = np.stack([np.searchsorted(rows[i, :rnum.reshape(-1)[i]], np.arange(nch + 1) * chunk)
+                     for i in range(rows.shape[0])])
+    want[:, nch] = rnum.reshape(-1)
+    assert np.array_equal(bounds.reshape(-1, nch + 1), want)
+    (dq1, dk1, dv1), (dq, dk, dv) = runs[-1], runs[chunk]
+    assert torch.equal(dq, dq1)
+    rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    for name, got, one, ref in (("dk", dk, dk1, rdk), ("dv", dv, dv1, rdv)):
+        check_close(name, got, ref)
+        g, g1 = got.float(), one.float()
+        assert (g - g1).abs().max().item() <= 1e-2 * g1.abs().max().item() + 1e-30
+        assert np.all(got.float().cpu().numpy()[ref == 0] == 0)
+
+
 @pytest.mark.parametrize("give_q2k", [False, True])
 @pytest.mark.parametrize("n", [2, "odd_blocks_ragged"])
 def test_spill_slot_tables_bit_exact(n, give_q2k):
