@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "ORDER_BIN_WIDTH", "CHUNK_MIN_KV_BLOCKS",
-    "CHUNK_Q_BLOCKS", "library_path", "is_built", "is_supported",
+    "CHUNK_Q_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
     "DQ_RECOMPUTE", "DQ_SPILL",
@@ -38,6 +38,7 @@ ORDER_MIN_KV_BLOCKS = 64   # VSA_ORDER_MIN_KV_BLOCKS
 ORDER_BIN_WIDTH = 4        # VSA_ORDER_BIN_WIDTH
 CHUNK_MIN_KV_BLOCKS = 4096  # VSA_CHUNK_MIN_KV_BLOCKS
 CHUNK_Q_BLOCKS = 1024       # VSA_CHUNK_Q_BLOCKS
+FWD_CHUNK_KV_BLOCKS = 512   # VSA_FWD_CHUNK_KV_BLOCKS
 ORDER_MAX_KV_BLOCKS = 16384
 _LOG2E = 1.4426950408889634
 
@@ -53,7 +54,8 @@ class _FwdArgs(ctypes.Structure):
                 ("o", _p), ("lse", _p), ("batch", ctypes.c_int), ("heads", ctypes.c_int),
                 ("seqlen", ctypes.c_int), ("head_dim", ctypes.c_int),
                 ("num_kv_blocks", ctypes.c_int), ("q2k_stride", ctypes.c_int),
-                ("sm_scale", ctypes.c_float)]
+                ("sm_scale", ctypes.c_float), ("workspace", _p),
+                ("workspace_bytes", ctypes.c_size_t), ("kv_chunk_blocks", ctypes.c_int)]
 
 
 class _BwdArgs(ctypes.Structure):
@@ -83,6 +85,7 @@ _SIGNATURES = {
     "vsa_invert_indices": (ctypes.c_int, [_p, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, _p, _p, _p,
                                           ctypes.c_size_t, _p]),
+    "vsa_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "vsa_fwd_check": (ctypes.c_int, [ctypes.POINTER(_FwdArgs)]),
     "vsa_fwd": (ctypes.c_int, [ctypes.POINTER(_FwdArgs), _p]),
     "vsa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
@@ -203,11 +206,20 @@ def invert_indices(q2k_idx: torch.Tensor, q2k_num: torch.Tensor, num_kv_blocks: 
     return k2q_idx, k2q_num
 
 
+def fwd_workspace_bytes(batch: int, heads: int, seqlen: int, kv_chunk_blocks: int = 0) -> int:
+    """Forward workspace bytes (0 when the forward runs as one launch)."""
+    return int(lib().vsa_fwd_workspace_bytes(batch, heads, seqlen, kv_chunk_blocks))
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Tensor,
             q2k_num: torch.Tensor, variable_block_sizes: torch.Tensor,
             sm_scale: Optional[float] = None,
-            out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
-    """Block-sparse forward: returns ``(o bf16 [B,H,S,128], lse fp32 [B,H,S] M form)``."""
+            out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+            kv_chunk_blocks: int = 0, workspace: Optional[torch.Tensor] = None):
+    """Block-sparse forward: returns ``(o bf16 [B,H,S,128], lse fp32 [B,H,S] M form)``.
+    ``kv_chunk_blocks``: kv blocks per kv-range chunk (0: the library's choice, chunks of
+    FWD_CHUNK_KV_BLOCKS from CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch); the
+    workspace it needs is allocated here unless given."""
     _need_gpu(q, "q")
     if q.dim() != 4:
         raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
@@ -231,9 +243,14 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+    need = fwd_workspace_bytes(B, H, S, kv_chunk_blocks)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a = _FwdArgs(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), num.data_ptr(),
                  vbs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, S, D, nb, idx.shape[-1],
-                 float(sm_scale))
+                 float(sm_scale), _ptr(workspace),
+                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                 int(kv_chunk_blocks))
     _check(lib().vsa_fwd(ctypes.byref(a), _stream(q.device)), "vsa_fwd")
     return o, lse
 

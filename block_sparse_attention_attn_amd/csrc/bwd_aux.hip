@@ -197,36 +197,35 @@ __global__ void __launch_bounds__(256) spill_qent_kernel(
       (int64_t)(uint32_t)slot | ((int64_t)kv << 32) | ((int64_t)vb << 48);
 }
 
-// One thread per (item, chunk boundary c = 0 .. nchunks): a binary search of the ascending list.
+// One thread per (item, chunk boundary c = 0 .. nchunks): a binary search of the list.
 __global__ void __launch_bounds__(256) chunk_bounds_kernel(
-    const int32_t* __restrict__ k2q_idx, const int32_t* __restrict__ k2q_num, int k2q_stride,
-    int total_items, int nchunks, int chunk_q, int32_t* __restrict__ bounds) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ num, int stride,
+    int total_items, int nchunks, int width, int32_t* __restrict__ bounds) {
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (size_t)total_items * (nchunks + 1)) return;
   const size_t item = e / (nchunks + 1);
   const int c = (int)(e - item * (nchunks + 1));
-  int m = k2q_num[item];
-  m = m < 0 ? 0 : (m > k2q_stride ? k2q_stride : m);
-  int lo = m;
-  if (c < nchunks) {
-    const long long qlo = (long long)c * chunk_q;
-    const int32_t* list = k2q_idx + item * k2q_stride;
+  int m = num[item];
+  m = m < 0 ? 0 : (m > stride ? stride : m);
+  int lo = c == 0 ? 0 : m;  // the chunks always cover positions 0 .. m - 1
+  if (c > 0 && c < nchunks) {
+    const long long lim = (long long)c * width;
+    const int32_t* list = idx + item * stride;
     int hi = m;
     lo = 0;
-    while (lo < hi) {  // first position with list[pos] >= qlo
+    while (lo < hi) {  // first position with list[pos] >= lim (for an ascending list)
       const int mid = (lo + hi) >> 1;
-      if ((long long)list[mid] < qlo) lo = mid + 1; else hi = mid;
+      if ((long long)list[mid] < lim) lo = mid + 1; else hi = mid;
     }
   }
   bounds[e] = lo;
 }
 
-void launch_chunk_bounds(const int32_t* k2q_idx, const int32_t* k2q_num, int k2q_stride,
-                         int total_items, int nchunks, int chunk_q, int32_t* bounds,
-                         hipStream_t stream) {
+void launch_chunk_bounds(const int32_t* idx, const int32_t* num, int stride, int total_items,
+                         int nchunks, int width, int32_t* bounds, hipStream_t stream) {
   const size_t n = (size_t)total_items * (nchunks + 1);
   hipLaunchKernelGGL(chunk_bounds_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     k2q_idx, k2q_num, k2q_stride, total_items, nchunks, chunk_q, bounds);
+                     idx, num, stride, total_items, nchunks, width, bounds);
 }
 
 void launch_spill_qent(const int32_t* q2k_idx, const int32_t* q2k_num, int q2k_stride,

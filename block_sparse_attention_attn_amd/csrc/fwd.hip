@@ -59,7 +59,22 @@ fwd_kernel(FwdParams p) {
   const int qb = item - bh * p.nb;
   int n = ld_const(p.q2k_num, item);
   n = n < 0 ? 0 : (n > p.q2k_stride ? p.q2k_stride : n);
-  const int32_t* list = p.q2k_idx + (size_t)item * p.q2k_stride;
+  // kv-range chunk: this launch walks list positions [start, start + n), resuming (unless first)
+  // from the state the chunk before left, and finishing (if last) or saving it
+  int start = 0;
+  bool first = true, last = true;
+  if (p.nchunks > 0) {
+    const int32_t* cb = p.chunk_bounds + (size_t)item * (p.nchunks + 1) + p.chunk;
+    int b0 = ld_const(cb, 0), b1 = ld_const(cb, 1);
+    b0 = b0 < 0 ? 0 : (b0 > n ? n : b0);
+    b1 = b1 < b0 ? b0 : (b1 > n ? n : b1);
+    start = b0;
+    n = b1 - b0;
+    first = p.chunk == 0;
+    last = p.chunk == p.nchunks - 1;
+    if (n == 0 && !first && !last) return;  // the state passes through unchanged
+  }
+  const int32_t* list = p.q2k_idx + (size_t)item * p.q2k_stride + start;
   const size_t head = (size_t)bh * p.S * HEAD_DIM;
   const int qrow = qb * BLOCK + 32 * wq + l32;  // this lane's q row (a column of S^T)
 
@@ -98,6 +113,16 @@ fwd_kernel(FwdParams p) {
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
   float m_run = -__builtin_inff();  // of this lane's q column over this wave's kv halves
   float l_run = 0.f;
+  // this wave's state in the chunk workspace: O^T element rows 0..63, then max, sum (lane-major)
+  float* state = p.state ? p.state + ((size_t)item * 4 + w) * FWD_STATE_FLOATS + lane : nullptr;
+  if (!first) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] = state[(16 * dt + i) * 64];
+    m_run = state[64 * 64];
+    l_run = state[65 * 64];
+  }
   const float scale_log2 = p.scale_log2;
 
   // Block t: K in K stage t % 2, V in V stage t % 2. The S^T tile of block t is computed during
@@ -213,6 +238,17 @@ fwd_kernel(FwdParams p) {
     e1 = e2;
     e2 = e3;
     vb0 = vb1;
+  }
+
+  if (!last) {  // save the state for the next chunk, exactly
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no DMA may still write this workgroup's LDS
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) state[(16 * dt + i) * 64] = oacc[dt][i];
+    state[64 * 64] = m_run;
+    state[65 * 64] = l_run;
+    return;
   }
 
   // ---- merge the two kv halves of each q half through LDS, normalise, store ----

@@ -108,6 +108,33 @@ int vsa_invert_indices(const int32_t* q2k_idx, const int32_t* q2k_num, int batch
 // forward
 // ------------------------------------------------------------------------------------------------
 
+namespace {
+
+// kv blocks per kv-range chunk of the forward (0: one launch), like chunk_q_blocks
+int fwd_chunk_kv_blocks(int nb, int kv_chunk_blocks) {
+  if (kv_chunk_blocks < 0) return 0;
+  const int ck = kv_chunk_blocks > 0
+                     ? kv_chunk_blocks
+                     : (nb >= VSA_CHUNK_MIN_KV_BLOCKS ? VSA_FWD_CHUNK_KV_BLOCKS : 0);
+  return ck > 0 && ck < nb ? ck : 0;
+}
+
+size_t fwd_bounds_bytes(size_t items, int nchunks) {
+  return align256(items * (size_t)(nchunks + 1) * sizeof(int32_t));
+}
+
+}  // namespace
+
+size_t vsa_fwd_workspace_bytes(int batch, int heads, int seqlen, int kv_chunk_blocks) {
+  if (!dims_ok(batch, heads, seqlen, seqlen / vsa::BLOCK)) return 0;
+  const int nb = seqlen / vsa::BLOCK;
+  const int ck = fwd_chunk_kv_blocks(nb, kv_chunk_blocks);
+  if (ck == 0) return 0;
+  const size_t items = (size_t)batch * heads * nb;
+  return fwd_bounds_bytes(items, (nb + ck - 1) / ck) +
+         align256(items * 4 * (size_t)vsa::FWD_STATE_FLOATS * sizeof(float));
+}
+
 int vsa_fwd_check(const vsa_fwd_args* a) {
   if (!a) return fail(VSA_EINVAL, "vsa_fwd: null argument struct");
   if (a->head_dim != vsa::HEAD_DIM)
@@ -120,6 +147,11 @@ int vsa_fwd_check(const vsa_fwd_args* a) {
   if (!std::isfinite(a->sm_scale)) return fail(VSA_EINVAL, "vsa_fwd: sm_scale must be finite");
   if (!a->q || !a->k || !a->v || !a->q2k_idx || !a->q2k_num || !a->vbs || !a->o || !a->lse)
     return fail(VSA_EINVAL, "vsa_fwd: null pointer");
+  const size_t need =
+      vsa_fwd_workspace_bytes(a->batch, a->heads, a->seqlen, a->kv_chunk_blocks);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+    return fail(VSA_EINVAL, "vsa_fwd: workspace of " + std::to_string(a->workspace_bytes) +
+                                " bytes, need " + std::to_string(need));
   return VSA_OK;
 }
 
@@ -141,8 +173,30 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
   p.q2k_stride = a->q2k_stride;
   p.items_per_xcd = (p.BH * p.nb + 7) / 8;
   p.scale_log2 = scale_log2(a->sm_scale);
-  vsa::launch_fwd(p, (hipStream_t)stream);
-  return launch_status("vsa_fwd");
+  const int ck = fwd_chunk_kv_blocks(p.nb, a->kv_chunk_blocks);
+  p.nchunks = ck > 0 ? (p.nb + ck - 1) / ck : 0;
+  p.chunk = 0;
+  p.chunk_bounds = nullptr;
+  p.state = nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.nchunks > 0) {
+    const size_t items = (size_t)p.BH * p.nb;
+    int32_t* bounds = (int32_t*)a->workspace;
+    p.chunk_bounds = bounds;
+    p.state = (float*)((char*)a->workspace + fwd_bounds_bytes(items, p.nchunks));
+    vsa::launch_chunk_bounds(a->q2k_idx, a->q2k_num, a->q2k_stride, (int)items, p.nchunks, ck,
+                             bounds, s);
+    const int r = launch_status("vsa_fwd chunk bounds");
+    if (r != VSA_OK) return r;
+  }
+  const int launches = p.nchunks > 0 ? p.nchunks : 1;
+  for (int c = 0; c < launches; ++c) {
+    p.chunk = c;
+    vsa::launch_fwd(p, s);
+    const int r = launch_status("vsa_fwd");
+    if (r != VSA_OK) return r;
+  }
+  return VSA_OK;
 }
 
 // ------------------------------------------------------------------------------------------------

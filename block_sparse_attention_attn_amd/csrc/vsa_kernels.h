@@ -30,7 +30,14 @@ struct FwdParams {
   int BH, S, nb, q2k_stride;
   int items_per_xcd;  // ceil(BH * nb / 8): workgroup ids map XCD-first onto (bh, q block) items
   float scale_log2;
+  // kv-range chunks (nchunks 0: one launch): this launch takes list positions
+  // [bounds[item][chunk], bounds[item][chunk+1]) and carries each wave's state in `state`
+  const int32_t* chunk_bounds;  // [BH * nb, nchunks + 1]
+  float* state;                 // [BH * nb, 4 waves, FWD_STATE_FLOATS]
+  int chunk, nchunks;
 };
+// per wave: 64 lane-major rows of O^T accumulator elements, then the running max and sum rows
+constexpr int FWD_STATE_FLOATS = 66 * 64;
 void launch_fwd(const FwdParams& p, hipStream_t stream);
 
 // ---- backward preprocess: Delta, zero dK/dV rows of empty kv blocks ----
@@ -108,12 +115,13 @@ void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 void launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 void launch_bwd_dq_spill(const BwdParams& p, hipStream_t stream);
 
-// ---- q-range chunk bounds: bounds[item][c] = first position of the item's (ascending) k2q list
-// whose q block is >= c * chunk_q, for c = 0 .. nchunks (so bounds[item][nchunks] = the list
-// length, clamped to [0, k2q_stride]) ----
-void launch_chunk_bounds(const int32_t* k2q_idx, const int32_t* k2q_num, int k2q_stride,
-                         int total_items, int nchunks, int chunk_q, int32_t* bounds,
-                         hipStream_t stream);
+// ---- chunk bounds of block lists (k2q rows for the kv-major kernel, q2k rows for the
+// forward): bounds[item][c] = the binary-search position of c * width in the item's list (the
+// first entry >= c * width when the list is ascending), for c = 0 .. nchunks - 1, and
+// bounds[item][nchunks] = the list length clamped to [0, stride]. Non-decreasing in c for any
+// list, so the chunks partition the list. ----
+void launch_chunk_bounds(const int32_t* idx, const int32_t* num, int stride, int total_items,
+                         int nchunks, int width, int32_t* bounds, hipStream_t stream);
 
 // ---- dS slot tables (spill mode) ----
 // kbase[bh, kv] = sum of min(max(k2q_num, 0), k2q_stride) over the kv blocks before kv in head bh:

@@ -64,7 +64,19 @@ int vsa_invert_indices(const int32_t* q2k_idx, const int32_t* q2k_num, int batch
 /* ------------------------------------------------------------------------------------------ */
 /* Forward (FastVideo sm_100a forward module docstring): o = softmax(q k^T * sm_scale over the
  * selected, unmasked keys) v, rounded to bf16; lse = max(q k^T * sm_scale * log2(e)) + log2(l)
- * ("M form", fp32 [B, H, S]). A q row with no valid key gets o = 0 and lse = -inf. */
+ * ("M form", fp32 [B, H, S]). A q row with no valid key gets o = 0 and lse = -inf.
+ *
+ * kv-range chunks (kv_chunk_blocks; 0 = the library's choice): with R = kv_chunk_blocks (> 0), or
+ * R = VSA_FWD_CHUNK_KV_BLOCKS from VSA_CHUNK_MIN_KV_BLOCKS kv blocks on when it is 0, the forward
+ * runs as C = ceil(nb / R) launches; launch c takes, of every q2k list, the positions from the
+ * first entry >= c*R to the first entry >= (c+1)*R (the kv blocks in [c*R, (c+1)*R) when the
+ * list is ascending) and carries each wave's running O, max and sum to the next launch in fp32
+ * in the workspace, exactly: the results are bitwise those of one launch. The workgroups running
+ * together on one XCD then share a window of R kv blocks, so their K/V tiles stay in its L2.
+ * Any list order is correct; ascending lists give the locality. kv_chunk_blocks < 0: never
+ * chunk. Workspace (vsa_fwd_workspace_bytes, NULL/0 when that is 0): int32 [B*H*nb, C+1] chunk
+ * bounds, then fp32 [B*H*nb, 4, 66, 64] per-wave state. */
+#define VSA_FWD_CHUNK_KV_BLOCKS 512
 typedef struct {
   const void* q;          /* bf16 [B, H, S, 128] */
   const void* k;          /* bf16 [B, H, S, 128] */
@@ -76,8 +88,14 @@ typedef struct {
   float* lse;             /* fp32 [B, H, S], output */
   int batch, heads, seqlen, head_dim, num_kv_blocks, q2k_stride;
   float sm_scale;
+  void* workspace;        /* see above; may be NULL when vsa_fwd_workspace_bytes is 0 */
+  size_t workspace_bytes;
+  int kv_chunk_blocks;    /* kv-range chunks, see above; 0 = default */
 } vsa_fwd_args;
 
+/* Bytes of forward workspace for these sizes and kv_chunk_blocks; 0 when the forward runs as one
+ * launch (or for an invalid shape). */
+size_t vsa_fwd_workspace_bytes(int batch, int heads, int seqlen, int kv_chunk_blocks);
 int vsa_fwd_check(const vsa_fwd_args* a);
 int vsa_fwd(const vsa_fwd_args* a, void* stream);
 

@@ -185,6 +185,45 @@ def test_forward_parity(n):
     _fwd_compare(c, d, o, lse)
 
 
+@pytest.mark.parametrize("case,chunk,shuffle", [(2, 3, False), (2, 1, False), (2, 5, True),
+                                                ("odd_blocks_ragged", 2, False),
+                                                ("empty_q_blocks", 4, True),
+                                                ("pool_excludes_three", 5, False)])
+def test_forward_kv_range_chunks(case, chunk, shuffle):
+    """The forward in kv-range chunks (kv_chunk_blocks): each wave's running O, max and sum pass
+    from launch to launch in fp32, and each launch takes a contiguous run of list positions, so o
+    and lse are bit-identical to one launch, also for lists in no particular order (shuffled)."""
+    if case == 2:
+        c = workloads.config(2)
+    else:
+        B, H, nb, topk, vbs, pool, empty = EDGE_CASES[case]
+        c = workloads.make_case(B, H, nb, topk, seed=17, vbs=vbs, kv_pool=pool, name=case)
+        for b, h, qb in empty:
+            c.q2k_num[b, h, qb] = 0
+    d = to_dev(c)
+    idx = d["q2k_idx"]
+    if shuffle:
+        g = torch.Generator().manual_seed(3)
+        perm = torch.stack([torch.randperm(idx.shape[-1], generator=g)
+                            for _ in range(idx.numel() // idx.shape[-1])])
+        rows = c.q2k_idx.reshape(-1, idx.shape[-1])
+        nums = c.q2k_num.reshape(-1)
+        sh = rows.clone()
+        for i in range(rows.shape[0]):  # permute the valid prefix of each row
+            k = int(nums[i])
+            sh[i, :k] = rows[i, :k][perm[i][perm[i] < k]]
+        idx = sh.reshape(idx.shape).to(DEV)
+    say(f"[forward] {case}, kv-range chunks of {chunk} kv blocks, shuffled {shuffle}")
+    one = V.forward(d["q"], d["k"], d["v"], idx, d["q2k_num"], d["vbs"], kv_chunk_blocks=-1)
+    assert V.fwd_workspace_bytes(c.B, c.H, c.S, chunk) > 0
+    o, lse = V.forward(d["q"], d["k"], d["v"], idx, d["q2k_num"], d["vbs"], kv_chunk_blocks=chunk,
+                       out=(nan_like(d["q"]), nan_like(one[1])))
+    torch.cuda.synchronize()
+    assert torch.equal(o, one[0]) and torch.equal(lse, one[1])
+    if not shuffle:
+        _fwd_compare(c, d, o, lse)
+
+
 def test_forward_ignores_out_of_range_kv_ids():
     """kv ids outside [0, nb) in a q2k list (a caller-contract violation) contribute nothing and
     fault nothing: the forward with such ids inserted in the middle of the lists gives the same
