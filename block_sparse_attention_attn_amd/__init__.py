@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "ORDER_BIN_WIDTH", "CHUNK_MIN_KV_BLOCKS",
-    "CHUNK_Q_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
+    "CHUNK_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
     "DQ_RECOMPUTE", "DQ_SPILL",
@@ -37,7 +37,7 @@ HEAD_DIM = 128
 ORDER_MIN_KV_BLOCKS = 64   # VSA_ORDER_MIN_KV_BLOCKS
 ORDER_BIN_WIDTH = 4        # VSA_ORDER_BIN_WIDTH
 CHUNK_MIN_KV_BLOCKS = 4096  # VSA_CHUNK_MIN_KV_BLOCKS
-CHUNK_Q_BLOCKS = 1024       # VSA_CHUNK_Q_BLOCKS
+CHUNK_BLOCKS = 1024       # VSA_CHUNK_BLOCKS
 FWD_CHUNK_KV_BLOCKS = 512   # VSA_FWD_CHUNK_KV_BLOCKS
 ORDER_MAX_KV_BLOCKS = 16384
 _LOG2E = 1.4426950408889634
@@ -66,12 +66,12 @@ class _BwdArgs(ctypes.Structure):
                 ("heads", ctypes.c_int), ("seqlen", ctypes.c_int), ("head_dim", ctypes.c_int),
                 ("num_kv_blocks", ctypes.c_int), ("max_q_blocks", ctypes.c_int),
                 ("q2k_stride", ctypes.c_int), ("sm_scale", ctypes.c_float),
-                ("dq_mode", ctypes.c_int), ("q_chunk_blocks", ctypes.c_int)]
+                ("dq_mode", ctypes.c_int), ("chunk_blocks", ctypes.c_int)]
 
 
 # workspace regions of the backward (vsa_bwd_ws_region)
 (WS_LSE_DELTA, WS_KV_ORDER, WS_Q_ORDER, WS_Q2K_NUM, WS_Q2K_IDX, WS_BITMAP, WS_KBASE, WS_QENT,
- WS_DS, WS_CHUNK_BOUNDS, WS_DKV_PART, WS_END) = range(12)
+ WS_DS, WS_CHUNK_BOUNDS, WS_DKV_PART, WS_DQ_BOUNDS, WS_DQ_PART, WS_END) = range(14)
 # how the q-major kernel gets dS (vsa_dq_mode): recomputed from Q, K, V, dO, or spilled by the
 # kv-major kernel into the workspace (8 KiB per possible pair)
 DQ_RECOMPUTE, DQ_SPILL = 0, 1
@@ -256,18 +256,18 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
 
 
 def bwd_workspace_bytes(batch: int, heads: int, seqlen: int, q2k_stride: int = 0,
-                        dq_mode: int = DQ_RECOMPUTE, q_chunk_blocks: int = 0) -> int:
+                        dq_mode: int = DQ_RECOMPUTE, chunk_blocks: int = 0) -> int:
     """Workspace bytes of a backward call; ``q2k_stride`` is the row width of the q2k lists the
-    call passes, 0 when the library derives them; ``q_chunk_blocks`` as for ``BwdPlan``."""
+    call passes, 0 when the library derives them; ``chunk_blocks`` as for ``BwdPlan``."""
     return int(lib().vsa_bwd_workspace_bytes(batch, heads, seqlen, q2k_stride, dq_mode,
-                                             q_chunk_blocks))
+                                             chunk_blocks))
 
 
 def bwd_workspace_offset(batch: int, heads: int, seqlen: int, region: int, q2k_stride: int = 0,
-                         dq_mode: int = DQ_RECOMPUTE, q_chunk_blocks: int = 0) -> int:
+                         dq_mode: int = DQ_RECOMPUTE, chunk_blocks: int = 0) -> int:
     """Byte offset of a backward workspace region (WS_LSE_DELTA, WS_KV_ORDER, ...)."""
     return int(lib().vsa_bwd_workspace_offset(batch, heads, seqlen, q2k_stride, dq_mode,
-                                              q_chunk_blocks, region))
+                                              chunk_blocks, region))
 
 
 def bwd_order(k2q_num: torch.Tensor, bin_width: int = ORDER_BIN_WIDTH,
@@ -290,16 +290,18 @@ class BwdPlan:
     ``run()`` enqueues the whole backward (``vsa_bwd``); ``stage(i)`` enqueues one of its stages
     (``vsa_bwd_stage``: PREPROCESS=0, INDEX=1, DKDV=2, DQ=3), all on the current stream. With
     ``q2k_idx``/``q2k_num`` (the forward's metadata, the same selection as k2q) the library skips
-    deriving them. ``q_chunk_blocks``: q blocks per q-range chunk of the kv-major kernel (0: the
-    library's choice, chunks of VSA_CHUNK_Q_BLOCKS from VSA_CHUNK_MIN_KV_BLOCKS kv blocks on;
-    negative: one launch). The plan keeps references to every tensor it points at.
+    deriving them. ``chunk_blocks``: blocks per chunk of the main kernels, q blocks of each k2q
+    list for the kv-major kernel and kv blocks of each q2k list for the recomputing q-major one
+    (0: the library's choice, chunks of CHUNK_BLOCKS for the kv-major kernel alone from
+    CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch each). The plan keeps references to
+    every tensor it points at.
     """
 
     PREPROCESS, INDEX, DKDV, DQ = 0, 1, 2, 3
 
     def __init__(self, grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                  sm_scale=None, order=None, workspace=None, out=None, q2k_idx=None,
-                 q2k_num=None, dq_mode=DQ_RECOMPUTE, q_chunk_blocks=0):
+                 q2k_num=None, dq_mode=DQ_RECOMPUTE, chunk_blocks=0):
         _need_gpu(q, "q")
         if q.dim() != 4:
             raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
@@ -339,7 +341,7 @@ class BwdPlan:
             out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         kq = qidx.shape[-1] if qidx is not None else 0
         if workspace is None:
-            workspace = torch.empty(bwd_workspace_bytes(B, H, S, kq, dq_mode, q_chunk_blocks),
+            workspace = torch.empty(bwd_workspace_bytes(B, H, S, kq, dq_mode, chunk_blocks),
                                     dtype=torch.uint8, device=q.device)
         self.dq, self.dk, self.dv = out
         self.workspace = workspace
@@ -351,7 +353,7 @@ class BwdPlan:
                              self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                              B, H, S, D, nb, idx.shape[-1],
-                             kq, float(sm_scale), int(dq_mode), int(q_chunk_blocks))
+                             kq, float(sm_scale), int(dq_mode), int(chunk_blocks))
         self._ref = ctypes.byref(self.args)
         _check(lib().vsa_bwd_check(self._ref), "vsa_bwd")
 
@@ -366,7 +368,7 @@ class BwdPlan:
         """``count`` elements of workspace region ``r`` (WS_LSE_DELTA, WS_KV_ORDER, ...)."""
         a = self.args
         off = bwd_workspace_offset(a.batch, a.heads, a.seqlen, r, a.q2k_stride if a.q2k_idx else 0,
-                                   a.dq_mode, a.q_chunk_blocks)
+                                   a.dq_mode, a.chunk_blocks)
         nbytes = count * torch.empty(0, dtype=dtype).element_size()
         return self.workspace[off:off + nbytes].view(dtype)
 
@@ -398,18 +400,18 @@ def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
                       out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                       q2k_idx: Optional[torch.Tensor] = None,
                       q2k_num: Optional[torch.Tensor] = None, dq_mode: int = DQ_RECOMPUTE,
-                      q_chunk_blocks: int = 0):
+                      chunk_blocks: int = 0):
     """Backward from k2q metadata (``[B, H, nb, max_q_blocks]`` or ``[B*H*nb, max_q_blocks]``
     plus ``[B, H, nb]`` counts). Returns ``(dq, dk, dv)`` bf16."""
     return BwdPlan(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                    sm_scale=sm_scale, order=order, workspace=workspace, out=out,
                    q2k_idx=q2k_idx, q2k_num=q2k_num, dq_mode=dq_mode,
-                   q_chunk_blocks=q_chunk_blocks).run()
+                   chunk_blocks=chunk_blocks).run()
 
 
 def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
              sm_scale: Optional[float] = None, dq_mode: int = DQ_RECOMPUTE,
-             q_chunk_blocks: int = 0):
+             chunk_blocks: int = 0):
     """Backward from the forward's q2k metadata: inverts to k2q on the GPU, then runs the
     backward with both lists (the q-major dQ kernel walks q2k, the kv-major kernel k2q). The q2k
     rows must not repeat a kv block. Returns ``(dq, dk, dv)``."""
@@ -424,4 +426,4 @@ def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
     k2q_idx, k2q_num = invert_indices(idx, num, nb)
     return backward_from_k2q(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                              sm_scale=sm_scale, q2k_idx=idx, q2k_num=num, dq_mode=dq_mode,
-                             q_chunk_blocks=q_chunk_blocks)
+                             chunk_blocks=chunk_blocks)

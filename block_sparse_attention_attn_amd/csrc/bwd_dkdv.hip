@@ -427,7 +427,7 @@ bwd_dkdv_kernel(BwdParams p) {
   bf16* outp = (wq == 0 ? p.dv : p.dk) + head + (size_t)j * BLOCK * HEAD_DIM;
   const float oscale = wq == 0 ? 1.0f : p.sm_scale;
   // this wave's tensor (dV for wq 0, dK for wq 1) in the chunk partial sums: [64][128] fp32
-  float* part = p.dkv_part ? p.dkv_part + ((size_t)item * 2 + wq) * (BLOCK * HEAD_DIM) : nullptr;
+  float* part = p.part ? p.part + ((size_t)item * 2 + wq) * (BLOCK * HEAD_DIM) : nullptr;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int d = 32 * nt + l32;

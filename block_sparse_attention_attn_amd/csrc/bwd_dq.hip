@@ -61,12 +61,27 @@ bwd_dq_kernel(BwdParams p) {
   if (item < 0 || item >= p.total_items) return;
   int n = ld_const(p.q2k_num, item);
   n = n < 0 ? 0 : (n > p.q2k_stride ? p.q2k_stride : n);
+  // kv-range chunk: this launch walks list positions [start, start + n) and adds to (first:
+  // starts) the fp32 partial dQ of the chunks before, which the last chunk turns into dq
+  int start = 0;
+  bool first = true, last = true;
+  if (p.nchunks > 0) {
+    const int32_t* cb = p.chunk_bounds + (size_t)item * (p.nchunks + 1) + p.chunk;
+    int b0 = ld_const(cb, 0), b1 = ld_const(cb, 1);
+    b0 = b0 < 0 ? 0 : (b0 > n ? n : b0);
+    b1 = b1 < b0 ? b0 : (b1 > n ? n : b1);
+    start = b0;
+    n = b1 - b0;
+    first = p.chunk == 0;
+    last = p.chunk == p.nchunks - 1;
+    if (n == 0 && !first && !last) return;  // nothing to add, nothing to finish
+  }
   const int bh = item / p.nb;
   const int i = item - bh * p.nb;
   const size_t head = (size_t)bh * p.S * HEAD_DIM;
   const bf16* __restrict__ kh = p.k + head;
   const bf16* __restrict__ vh = p.v + head;
-  const int* __restrict__ list = p.q2k_idx + (size_t)item * p.q2k_stride;
+  const int* __restrict__ list = p.q2k_idx + (size_t)item * p.q2k_stride + start;
   auto kvblock = [&](int t) {
     const int kb = ld_const(list, t);
     return kb < 0 ? 0 : (kb >= p.nb ? p.nb - 1 : kb);
@@ -247,6 +262,10 @@ bwd_dq_kernel(BwdParams p) {
   }
   barrier_lds();
   bf16* dqrow = p.dq + head + (size_t)qrow * HEAD_DIM;
+  // this lane's q row of the chunk partial sums: [64][128] fp32 per q block
+  float* prow = p.part ? p.part + (size_t)item * (BLOCK * HEAD_DIM) +
+                             (size_t)(32 * wq + l32) * HEAD_DIM
+                       : nullptr;
   const float sc = p.sm_scale;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -254,16 +273,23 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const f32x4 o = take[(u * 4 + c) * 64 + lane];
-      union {
-        bf16 b[4];
-        s16x4 s;
-      } r;
+      f32x4 sum;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float mine = wk == 0 ? dq_acc[u][4 * c + e] : dq_acc[2 + u][4 * c + e];
-        r.b[e] = (bf16)((mine + o[e]) * sc);
+      for (int e = 0; e < 4; ++e)
+        sum[e] = (wk == 0 ? dq_acc[u][4 * c + e] : dq_acc[2 + u][4 * c + e]) + o[e];
+      const int d0 = 32 * mt + 8 * c + 4 * g;
+      if (!first) sum += *(const f32x4*)(prow + d0);
+      if (last) {
+        union {
+          bf16 b[4];
+          s16x4 s;
+        } r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.b[e] = (bf16)(sum[e] * sc);
+        *(s16x4*)(dqrow + d0) = r.s;
+      } else {
+        *(f32x4*)(prow + d0) = sum;
       }
-      *(s16x4*)(dqrow + 32 * mt + 8 * c + 4 * g) = r.s;
     }
   }
 }

@@ -36,13 +36,18 @@ int launch_status(const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// q blocks per q-range chunk of the kv-major kernel for nb kv blocks and the caller's
-// q_chunk_blocks (0: the library's choice, < 0: off); 0 when it runs as one launch
-int chunk_q_blocks(int nb, int q_chunk_blocks) {
-  if (q_chunk_blocks < 0) return 0;
-  const int cq = q_chunk_blocks > 0 ? q_chunk_blocks
-                                    : (nb >= VSA_CHUNK_MIN_KV_BLOCKS ? VSA_CHUNK_Q_BLOCKS : 0);
-  return cq > 0 && cq < nb ? cq : 0;  // one chunk covering every q block is no chunk
+// blocks per chunk of the main kernels for nb kv blocks and the caller's chunk_blocks (0: the
+// library's choice, < 0: off); 0 when they run as one launch each
+int chunk_blocks_of(int nb, int chunk_blocks) {
+  if (chunk_blocks < 0) return 0;
+  const int cb = chunk_blocks > 0 ? chunk_blocks
+                                  : (nb >= VSA_CHUNK_MIN_KV_BLOCKS ? VSA_CHUNK_BLOCKS : 0);
+  return cb > 0 && cb < nb ? cb : 0;  // one chunk covering every block is no chunk
+}
+// the recomputing q-major kernel runs in chunks only when the caller asks for them (chunk_blocks
+// > 0): at 524288 tokens, chunks of 1024 kv blocks left it unchanged and 2048 gained 3 %
+int dq_chunk_blocks_of(int nb, int chunk_blocks, int dq_mode) {
+  return dq_mode == VSA_DQ_RECOMPUTE && chunk_blocks > 0 ? chunk_blocks_of(nb, chunk_blocks) : 0;
 }
 
 // sm_scale * log2(e) in fp32: the factor that turns q.k into the base-2 exponent of the softmax
@@ -204,7 +209,7 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
 // ------------------------------------------------------------------------------------------------
 
 size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
-                                int q_chunk_blocks, int region) {
+                                int chunk_blocks, int region) {
   if (batch < 1 || heads < 1 || seqlen < vsa::BLOCK || q2k_stride < 0 ||
       (dq_mode != VSA_DQ_RECOMPUTE && dq_mode != VSA_DQ_SPILL) || region < VSA_WS_LSE_DELTA ||
       region > VSA_WS_END)
@@ -214,8 +219,10 @@ size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride
   const bool derive = q2k_stride == 0;
   const bool spill = dq_mode == VSA_DQ_SPILL;
   const size_t kq = derive ? nb : (size_t)q2k_stride;  // q2k row width
-  const int cq = chunk_q_blocks((int)nb, q_chunk_blocks);
+  const int cq = chunk_blocks_of((int)nb, chunk_blocks);
   const size_t nchunks = cq > 0 ? (nb + cq - 1) / cq : 0;
+  const int cqq = dq_chunk_blocks_of((int)nb, chunk_blocks, dq_mode);
+  const size_t dq_nchunks = cqq > 0 ? (nb + cqq - 1) / cqq : 0;
   const size_t sizes[VSA_WS_END] = {
       align256(bh * (size_t)seqlen * 2 * sizeof(float)),                      // lse, Delta
       align256(bh * nb * sizeof(int32_t)),                                    // kv order
@@ -229,6 +236,9 @@ size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride
       nchunks ? align256(bh * nb * (nchunks + 1) * sizeof(int32_t)) : 0,          // bounds
       nchunks ? align256(bh * nb * 2 * (size_t)(vsa::BLOCK * vsa::HEAD_DIM) * sizeof(float))
               : 0,                                                                 // dK/dV
+      dq_nchunks ? align256(bh * nb * (dq_nchunks + 1) * sizeof(int32_t)) : 0,     // dq bounds
+      dq_nchunks ? align256(bh * nb * (size_t)(vsa::BLOCK * vsa::HEAD_DIM) * sizeof(float))
+                 : 0,                                                              // dQ
   };
   size_t off = 0;
   for (int r = 0; r < region; ++r) off += sizes[r];
@@ -236,8 +246,8 @@ size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride
 }
 
 size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
-                               int q_chunk_blocks) {
-  return vsa_bwd_workspace_offset(batch, heads, seqlen, q2k_stride, dq_mode, q_chunk_blocks,
+                               int chunk_blocks) {
+  return vsa_bwd_workspace_offset(batch, heads, seqlen, q2k_stride, dq_mode, chunk_blocks,
                                   VSA_WS_END);
 }
 
@@ -277,7 +287,7 @@ int vsa_bwd_check(const vsa_bwd_args* a) {
   }
   const size_t need = vsa_bwd_workspace_bytes(a->batch, a->heads, a->seqlen,
                                               a->q2k_idx ? a->q2k_stride : 0, a->dq_mode,
-                                              a->q_chunk_blocks);
+                                              a->chunk_blocks);
   if (a->workspace_bytes < need)
     return fail(VSA_EINVAL, "vsa_bwd: workspace of " + std::to_string(a->workspace_bytes) +
                                 " bytes, need " + std::to_string(need));
@@ -316,7 +326,9 @@ struct WsView {
   int64_t* qent;
   vsa::bf16* ds;
   int32_t* chunk_bounds;
-  float* dkv_part;
+  float* part;
+  int32_t* dq_bounds;
+  float* dq_part;
 };
 
 WsView ws_view(const vsa_bwd_args* a) {
@@ -324,14 +336,15 @@ WsView ws_view(const vsa_bwd_args* a) {
   const int kq = a->q2k_idx ? a->q2k_stride : 0;
   auto at = [&](int r) {
     return ws + vsa_bwd_workspace_offset(a->batch, a->heads, a->seqlen, kq, a->dq_mode,
-                                         a->q_chunk_blocks, r);
+                                         a->chunk_blocks, r);
   };
   return WsView{(float*)at(VSA_WS_LSE_DELTA), (int32_t*)at(VSA_WS_KV_ORDER),
                 (int32_t*)at(VSA_WS_Q_ORDER),  (int32_t*)at(VSA_WS_Q2K_NUM),
                 (int32_t*)at(VSA_WS_Q2K_IDX),  (uint32_t*)at(VSA_WS_BITMAP),
                 (int32_t*)at(VSA_WS_KBASE),    (int64_t*)at(VSA_WS_QENT),
                 (vsa::bf16*)at(VSA_WS_DS),     (int32_t*)at(VSA_WS_CHUNK_BOUNDS),
-                (float*)at(VSA_WS_DKV_PART)};
+                (float*)at(VSA_WS_DKV_PART),   (int32_t*)at(VSA_WS_DQ_BOUNDS),
+                (float*)at(VSA_WS_DQ_PART)};
 }
 
 vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
@@ -367,11 +380,11 @@ vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
   m.items_per_xcd = (m.total_items + 7) / 8;
   m.sm_scale = a->sm_scale;
   m.scale_log2 = scale_log2(a->sm_scale);
-  const int cq = chunk_q_blocks(a->num_kv_blocks, a->q_chunk_blocks);
+  const int cq = chunk_blocks_of(a->num_kv_blocks, a->chunk_blocks);
   m.nchunks = cq > 0 ? (a->num_kv_blocks + cq - 1) / cq : 0;
   m.chunk = 0;
   m.chunk_bounds = m.nchunks ? ws.chunk_bounds : nullptr;
-  m.dkv_part = m.nchunks ? ws.dkv_part : nullptr;
+  m.part = m.nchunks ? ws.part : nullptr;
   return m;
 }
 
@@ -427,11 +440,20 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
         const int r = launch_status("vsa_bwd dS slot table");
         if (r != VSA_OK) return r;
       }
-      const int cq = chunk_q_blocks(nb, a->q_chunk_blocks);
-      if (cq > 0) {
-        vsa::launch_chunk_bounds(a->k2q_idx, a->k2q_num, a->max_q_blocks, BH * nb,
-                                 (nb + cq - 1) / cq, cq, ws.chunk_bounds, s);
+      const int cb = chunk_blocks_of(nb, a->chunk_blocks);
+      if (cb > 0) {
+        const int nchunks = (nb + cb - 1) / cb;
+        vsa::launch_chunk_bounds(a->k2q_idx, a->k2q_num, a->max_q_blocks, BH * nb, nchunks, cb,
+                                 ws.chunk_bounds, s);
         const int r = launch_status("vsa_bwd chunk bounds");
+        if (r != VSA_OK) return r;
+      }
+      const int cbq = dq_chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode);
+      if (cbq > 0) {
+        const vsa::BwdParams m = main_params(a, ws);
+        vsa::launch_chunk_bounds(m.q2k_idx, m.q2k_num, m.q2k_stride, BH * nb,
+                                 (nb + cbq - 1) / cbq, cbq, ws.dq_bounds, s);
+        const int r = launch_status("vsa_bwd dq chunk bounds");
         if (r != VSA_OK) return r;
       }
       return VSA_OK;
@@ -447,12 +469,25 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       }
       return VSA_OK;
     }
-    case VSA_BWD_DQ:
-      if (a->dq_mode == VSA_DQ_SPILL)
-        vsa::launch_bwd_dq_spill(main_params(a, ws), s);
-      else
-        vsa::launch_bwd_dq(main_params(a, ws), s);
-      return launch_status("vsa_bwd dq kernel");
+    case VSA_BWD_DQ: {
+      vsa::BwdParams m = main_params(a, ws);
+      if (a->dq_mode == VSA_DQ_SPILL) {
+        vsa::launch_bwd_dq_spill(m, s);
+        return launch_status("vsa_bwd dq kernel");
+      }
+      const int cbq = dq_chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode);
+      m.nchunks = cbq > 0 ? (nb + cbq - 1) / cbq : 0;
+      m.chunk_bounds = m.nchunks ? ws.dq_bounds : nullptr;
+      m.part = m.nchunks ? ws.dq_part : nullptr;
+      const int launches = m.nchunks > 0 ? m.nchunks : 1;
+      for (int c = 0; c < launches; ++c) {
+        m.chunk = c;
+        vsa::launch_bwd_dq(m, s);
+        const int r = launch_status("vsa_bwd dq kernel");
+        if (r != VSA_OK) return r;
+      }
+      return VSA_OK;
+    }
     default:
       return fail(VSA_EINVAL, "vsa_bwd_stage: unknown stage " + std::to_string(stage));
   }

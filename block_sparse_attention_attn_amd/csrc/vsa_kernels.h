@@ -104,9 +104,9 @@ struct BwdParams {
   int cap, qent_stride;  // slots per head (nb * K'), q2k row width K'
   // q-range chunks of the kv-major kernel (nchunks 0: one launch over whole lists): this launch
   // takes list positions [bounds[item][chunk], bounds[item][chunk+1]) and carries dV, dK
-  // (unscaled fp32, [item][2][64][128]) in dkv_part from chunk to chunk
+  // (unscaled fp32, [item][2][64][128]) in part from chunk to chunk
   const int32_t* chunk_bounds;  // [total_items, nchunks + 1]
-  float* dkv_part;
+  float* part;
   int chunk, nchunks;
   int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
   float scale_log2, sm_scale;

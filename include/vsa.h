@@ -153,24 +153,32 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *   VSA_WS_QENT      int64 [B, H, nb, K']: per q2k entry, its dS slot | kv block << 32 |
  *                    vbs[kv block] << 48
  *   VSA_WS_DS        bf16 [B, H, nb*K', 64, 64]: the dS tiles, slot-major
- * only when the kv-major kernel runs in q-range chunks (below), with C chunks:
+ * only when the main kernels run in chunks (below), with C chunks:
  *   VSA_WS_CHUNK_BOUNDS int32 [B*H*nb, C+1]: per kv item, the position in its k2q list of the
  *                    first q block of each chunk (the last entry is the list length)
  *   VSA_WS_DKV_PART  fp32 [B*H*nb, 2, 64, 128]: per kv item, dV then dK (unscaled) summed over
  *                    the chunks so far
+ *   VSA_WS_DQ_BOUNDS int32 [B*H*nb, C+1]: per q item, the same for its q2k list and kv blocks
+ *                    (VSA_DQ_RECOMPUTE mode with chunk_blocks > 0)
+ *   VSA_WS_DQ_PART   fp32 [B*H*nb, 64, 128]: per q item, dQ (unscaled) summed over the chunks so
+ *                    far (VSA_DQ_RECOMPUTE mode with chunk_blocks > 0)
  *
- * q-range chunks (q_chunk_blocks argument; 0 = the library's choice): with R = q_chunk_blocks
- * (> 0), or R = VSA_CHUNK_Q_BLOCKS from VSA_CHUNK_MIN_KV_BLOCKS kv blocks per sequence on when
- * it is 0, the kv-major kernel runs as C = ceil(nb / R) launches; launch c takes, of every k2q
- * list, the q blocks in [c*R, (c+1)*R) and carries dK and dV to the next launch in fp32 in the
- * workspace. The items running together on one XCD then walk a window of R q blocks at a time,
- * so the Q/dO tiles they share stay in its L2; without chunks, ascending walks of thousands of
- * entries drift apart and almost every Q/dO tile comes from HBM (the pages' long-sequence
- * cache-locality mode serves the same purpose). q_chunk_blocks < 0: never chunk. Chunking
- * changes only the fp32 summation order of dK and dV (one partial sum per chunk); dq is
- * unaffected. */
+ * Chunks (chunk_blocks argument; 0 = the library's choice): with R = chunk_blocks (> 0) each
+ * main kernel runs as C = ceil(nb / R) launches; with 0, the kv-major kernel alone does, with
+ * R = VSA_CHUNK_BLOCKS, from VSA_CHUNK_MIN_KV_BLOCKS kv blocks per sequence on (at 524288 tokens
+ * its chunks saved 7-12 %, while the q-major kernel gained at most 3 %). Launch c of the kv-major
+ * kernel takes, of every
+ * k2q list, the q blocks in [c*R, (c+1)*R); launch c of the recomputing q-major kernel takes, of
+ * every q2k list, the positions from the first entry >= c*R to the first entry >= (c+1)*R (the kv
+ * blocks in [c*R, (c+1)*R) for an ascending list; any order is correct). Each carries its
+ * partial sums to the next launch in fp32 in the workspace. The items running together on one
+ * XCD then walk a window of R blocks at a time, so the tiles they share stay in its L2; without
+ * chunks, ascending walks of thousands of entries drift apart and almost every Q/dO (K/V) tile
+ * comes from HBM (the pages' long-sequence cache-locality mode serves the same purpose).
+ * chunk_blocks < 0: never chunk. Chunking changes only the fp32 summation order of the chunked
+ * sums. The dS-reading q-major kernel (VSA_DQ_SPILL) always runs as one launch. */
 #define VSA_CHUNK_MIN_KV_BLOCKS 4096
-#define VSA_CHUNK_Q_BLOCKS 1024
+#define VSA_CHUNK_BLOCKS 1024
 #define VSA_ORDER_MIN_KV_BLOCKS 64
 #define VSA_ORDER_BIN_WIDTH 4
 #define VSA_ORDER_MAX_KV_BLOCKS 16384
@@ -187,7 +195,9 @@ typedef enum {
   VSA_WS_DS = 8,
   VSA_WS_CHUNK_BOUNDS = 9,
   VSA_WS_DKV_PART = 10,
-  VSA_WS_END = 11
+  VSA_WS_DQ_BOUNDS = 11,
+  VSA_WS_DQ_PART = 12,
+  VSA_WS_END = 13
 } vsa_bwd_ws_region;
 
 typedef enum { VSA_DQ_RECOMPUTE = 0, VSA_DQ_SPILL = 1 } vsa_dq_mode;
@@ -213,18 +223,18 @@ typedef struct {
   int batch, heads, seqlen, head_dim, num_kv_blocks, max_q_blocks, q2k_stride;
   float sm_scale;
   int dq_mode;            /* vsa_dq_mode */
-  int q_chunk_blocks;     /* q-range chunks of the kv-major kernel, see above; 0 = default */
+  int chunk_blocks;       /* blocks per chunk of the main kernels, see above; 0 = default */
 } vsa_bwd_args;
 
 /* Bytes of workspace for a backward call. q2k_stride: the row width of the q2k lists the call
- * passes, or 0 when q2k_idx/q2k_num are NULL (derived); dq_mode: a vsa_dq_mode; q_chunk_blocks:
+ * passes, or 0 when q2k_idx/q2k_num are NULL (derived); dq_mode: a vsa_dq_mode; chunk_blocks:
  * as in vsa_bwd_args. 0 for an invalid shape. */
 size_t vsa_bwd_workspace_bytes(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
-                               int q_chunk_blocks);
+                               int chunk_blocks);
 /* Byte offset of a workspace region (vsa_bwd_ws_region) for the same arguments; VSA_WS_END gives
  * the total. */
 size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride, int dq_mode,
-                                int q_chunk_blocks, int region);
+                                int chunk_blocks, int region);
 /* Host-only validation of a backward call; reads no device memory. */
 int vsa_bwd_check(const vsa_bwd_args* a);
 int vsa_bwd(const vsa_bwd_args* a, void* stream);
@@ -243,9 +253,10 @@ typedef enum {
   VSA_BWD_INDEX = 1,       /* q2k derivation (if needed), the length-binned work orders, in
                               VSA_DQ_SPILL mode the dS slot tables, with q-range chunks the
                               chunk bounds */
-  VSA_BWD_DKDV = 2,        /* kv-major kernel (one launch per q-range chunk): dk, dv (and the
-                              dS tiles in VSA_DQ_SPILL mode) */
-  VSA_BWD_DQ = 3           /* q-major kernel: dq = bf16(sm_scale * dS K) */
+  VSA_BWD_DKDV = 2,        /* kv-major kernel (one launch per chunk): dk, dv (and the dS tiles
+                              in VSA_DQ_SPILL mode) */
+  VSA_BWD_DQ = 3           /* q-major kernel (VSA_DQ_RECOMPUTE: one launch per chunk):
+                              dq = bf16(sm_scale * dS K) */
 } vsa_bwd_stage_id;
 int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream);
 

@@ -38,7 +38,7 @@ def test_binding_constants_match_the_header():
     for name, value in (("VSA_ORDER_MIN_KV_BLOCKS", V.ORDER_MIN_KV_BLOCKS),
                         ("VSA_ORDER_BIN_WIDTH", V.ORDER_BIN_WIDTH),
                         ("VSA_CHUNK_MIN_KV_BLOCKS", V.CHUNK_MIN_KV_BLOCKS),
-                        ("VSA_CHUNK_Q_BLOCKS", V.CHUNK_Q_BLOCKS)):
+                        ("VSA_CHUNK_BLOCKS", V.CHUNK_BLOCKS)):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == value, name
 
@@ -94,19 +94,34 @@ def test_workspace_chunk_regions():
     # below the default threshold: no chunk regions
     o = offs(1, 8, 64 * 512, 128, 0)
     assert o[V.WS_CHUNK_BOUNDS] == o[V.WS_DKV_PART] == o[V.WS_END] == o[V.WS_DS]
-    # from the threshold on, chunks of CHUNK_Q_BLOCKS q blocks: bounds and fp32 dV/dK sums
+    # from the threshold on, chunks of CHUNK_BLOCKS q blocks for the kv-major kernel: bounds and
+    # fp32 dV/dK sums; the q-major kernel's chunks only on request
     nb = V.CHUNK_MIN_KV_BLOCKS
     o = offs(1, 2, 64 * nb, 128, 0)
-    c = -(-nb // V.CHUNK_Q_BLOCKS)
+    c = -(-nb // V.CHUNK_BLOCKS)
     assert o[V.WS_DKV_PART] - o[V.WS_CHUNK_BOUNDS] == a256(2 * nb * (c + 1) * 4)
-    assert o[V.WS_END] - o[V.WS_DKV_PART] == 2 * nb * 2 * 64 * 128 * 4
+    assert o[V.WS_END] == o[V.WS_DQ_BOUNDS] == o[V.WS_DKV_PART] + 2 * nb * 2 * 64 * 128 * 4
     assert V.bwd_workspace_bytes(1, 2, 64 * nb, 128, V.DQ_RECOMPUTE, -1) == o[V.WS_CHUNK_BOUNDS]
-    # a forced chunk size at any size; one chunk covering every q block is no chunk
+    o = offs(1, 2, 64 * nb, 128, V.CHUNK_BLOCKS)  # requested: both kernels
+    assert o[V.WS_DQ_PART] - o[V.WS_DQ_BOUNDS] == a256(2 * nb * (c + 1) * 4)
+    assert o[V.WS_END] - o[V.WS_DQ_PART] == 2 * nb * 64 * 128 * 4
+    # the dS-reading q-major kernel runs as one launch: no dQ chunk regions in spill mode
+    sp = [V.bwd_workspace_offset(1, 2, 64 * nb, r, 128, V.DQ_SPILL, 0) for r in range(V.WS_END + 1)]
+    assert sp[V.WS_DQ_BOUNDS] == sp[V.WS_END] == sp[V.WS_DKV_PART] + 2 * nb * 2 * 64 * 128 * 4
+    # a forced chunk size at any size; one chunk covering every block is no chunk
     o = offs(1, 1, 64 * 10, 0, 3)
     assert o[V.WS_DKV_PART] - o[V.WS_CHUNK_BOUNDS] == a256(10 * 5 * 4)
-    assert o[V.WS_END] - o[V.WS_DKV_PART] == 10 * 2 * 64 * 128 * 4
+    assert o[V.WS_DQ_BOUNDS] - o[V.WS_DKV_PART] == 10 * 2 * 64 * 128 * 4
+    assert o[V.WS_END] - o[V.WS_DQ_PART] == 10 * 64 * 128 * 4
     o = offs(1, 1, 64 * 10, 0, 10)
     assert o[V.WS_END] == o[V.WS_CHUNK_BOUNDS]
+    # the forward's kv-range chunks: bounds, then per-wave state of 66 x 64 floats
+    nbf = V.CHUNK_MIN_KV_BLOCKS
+    cf = -(-nbf // V.FWD_CHUNK_KV_BLOCKS)
+    assert V.fwd_workspace_bytes(1, 2, 64 * nbf) == a256(2 * nbf * (cf + 1) * 4) + 2 * nbf * 4 * 66 * 64 * 4
+    assert V.fwd_workspace_bytes(1, 2, 64 * nbf, -1) == 0
+    assert V.fwd_workspace_bytes(1, 2, 64 * 512) == 0
+    assert V.fwd_workspace_bytes(1, 1, 64 * 10, 4) == a256(10 * 4 * 4) + 10 * 4 * 66 * 64 * 4
     assert V.invert_workspace_bytes(2, 3, 100, 50) == ((2 * 3 * 50 * 4 * 4 + 255) // 256) * 256
     assert V.invert_workspace_bytes(1, 1, 0, 1) == 0
 

@@ -350,11 +350,12 @@ def test_backward_edge_cases(name, mode):
 @pytest.mark.parametrize("case,chunk", [(2, 3), (2, 1), ("odd_blocks_ragged", 2),
                                         ("empty_q_blocks", 4), ("pool_excludes_three", 5)])
 def test_backward_q_range_chunks(case, chunk, mode):
-    """The kv-major kernel in q-range chunks (q_chunk_blocks): the chunk bounds bit-exact
-    (positions of the chunk starts in each ascending k2q row, from numpy's searchsorted), dq
-    bit-identical to the one-launch call (chunks do not touch the dQ path), dk/dv within the
-    oracle's tolerance, equal to the one-launch results up to the fp32 summation order, and
-    exactly zero wherever the oracle is (unselected kv blocks, padded rows)."""
+    """The main kernels in chunks (chunk_blocks): the chunk bounds bit-exact (positions of the
+    chunk starts in each ascending k2q row and, in recompute mode, q2k row, from numpy's
+    searchsorted), all three gradients within the oracle's tolerance, equal to the one-launch
+    results up to the fp32 summation order (dq bit-identical in spill mode, whose q-major kernel
+    runs as one launch), and exactly zero wherever the oracle is (unselected kv blocks, padded
+    rows, empty q rows)."""
     if case == 2:
         c = workloads.config(2)
     else:
@@ -373,20 +374,29 @@ def test_backward_q_range_chunks(case, chunk, mode):
     for qc in (-1, chunk):
         plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
                          out=(nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"])),
-                         dq_mode=MODES[mode], q_chunk_blocks=qc)
+                         dq_mode=MODES[mode], chunk_blocks=qc)
         runs[qc] = plan.run()
         torch.cuda.synchronize()
     nch = -(-c.nb // chunk)
-    bounds = plan.region(V.WS_CHUNK_BOUNDS, c.B * c.H * c.nb * (nch + 1)).cpu().numpy()
-    rows = ridx.reshape(-1, ridx.shape[-1])
-    want = np.stack([np.searchsorted(rows[i, :rnum.reshape(-1)[i]], np.arange(nch + 1) * chunk)
-                     for i in range(rows.shape[0])])
-    want[:, nch] = rnum.reshape(-1)
-    assert np.array_equal(bounds.reshape(-1, nch + 1), want)
+
+    def want_bounds(idx, num):
+        rows, nums = idx.reshape(-1, idx.shape[-1]), num.reshape(-1)
+        w = np.stack([np.searchsorted(rows[i, :nums[i]], np.arange(nch + 1) * chunk)
+                      for i in range(rows.shape[0])])
+        w[:, nch] = nums
+        return w
+    n_items = c.B * c.H * c.nb
+    bounds = plan.region(V.WS_CHUNK_BOUNDS, n_items * (nch + 1)).cpu().numpy()
+    assert np.array_equal(bounds.reshape(-1, nch + 1), want_bounds(ridx, rnum))
     (dq1, dk1, dv1), (dq, dk, dv) = runs[-1], runs[chunk]
-    assert torch.equal(dq, dq1)
+    if MODES[mode] == V.DQ_SPILL:
+        assert torch.equal(dq, dq1)
+    else:  # the q2k lists derived on the device: ascending, as the oracle's
+        qb = plan.region(V.WS_DQ_BOUNDS, n_items * (nch + 1)).cpu().numpy()
+        qidx, qnum = O.invert_indices(ridx, rnum, c.nb)
+        assert np.array_equal(qb.reshape(-1, nch + 1), want_bounds(qidx, qnum))
     rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
-    for name, got, one, ref in (("dk", dk, dk1, rdk), ("dv", dv, dv1, rdv)):
+    for name, got, one, ref in (("dq", dq, dq1, rdq), ("dk", dk, dk1, rdk), ("dv", dv, dv1, rdv)):
         check_close(name, got, ref)
         g, g1 = got.float(), one.float()
         assert (g - g1).abs().max().item() <= 1e-2 * g1.abs().max().item() + 1e-30
