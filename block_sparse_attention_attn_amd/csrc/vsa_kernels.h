@@ -32,9 +32,10 @@ struct FwdParams {
   float scale_log2;
   // kv-range chunks (nchunks 0: one launch): this launch takes list positions
   // [bounds[item][chunk], bounds[item][chunk+1]) and carries each wave's state in `state`
-  const int32_t* chunk_bounds;  // [BH * nb, nchunks + 1]
-  float* state;                 // [BH * nb, 4 waves, FWD_STATE_FLOATS]
-  int chunk, nchunks;
+  // (defaults: one launch, so a caller that predates the chunks cannot leave them undefined)
+  const int32_t* chunk_bounds = nullptr;  // [BH * nb, nchunks + 1]
+  float* state = nullptr;                 // [BH * nb, 4 waves, FWD_STATE_FLOATS]
+  int chunk = 0, nchunks = 0;
 };
 // per wave: 64 lane-major rows of O^T accumulator elements, then the running max and sum rows
 constexpr int FWD_STATE_FLOATS = 66 * 64;
@@ -105,9 +106,10 @@ struct BwdParams {
   // q-range chunks of the kv-major kernel (nchunks 0: one launch over whole lists): this launch
   // takes list positions [bounds[item][chunk], bounds[item][chunk+1]) and carries dV, dK
   // (unscaled fp32, [item][2][64][128]) in part from chunk to chunk
-  const int32_t* chunk_bounds;  // [total_items, nchunks + 1]
-  float* part;
-  int chunk, nchunks;
+  // (defaults: one launch, so a caller that predates the chunks cannot leave them undefined)
+  const int32_t* chunk_bounds = nullptr;  // [total_items, nchunks + 1]
+  float* part = nullptr;
+  int chunk = 0, nchunks = 0;
   int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
   float scale_log2, sm_scale;
 };
