@@ -39,7 +39,10 @@
 //   * dV and dK are accumulated per q half and the halves are summed through LDS once per item;
 //   * work ids map XCD-first: workgroup ids go round-robin over the 8 XCDs, so XCD x runs a
 //     contiguous slice of the (ordered) item list -- one head per XCD when B*H = 8 -- and that
-//     head's Q/dO traffic stays in one XCD's L2.
+//     head's Q/dO traffic stays in one XCD's L2;
+//   * long lists run in q-range chunks, one launch each: the items take the part of their list
+//     inside the chunk's q range and carry dK, dV between launches as fp32 partial sums, so the
+//     items on an XCD walk one window of q blocks at a time and keep sharing its L2.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 

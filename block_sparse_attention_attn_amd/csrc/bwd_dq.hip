@@ -24,7 +24,8 @@
 // exp2/convert work of kv block t and its K^T transposed reads (ds_read_b64_tr_b16), then the
 // dQ^T += K^T dS^T MFMAs of kv block t interleaved with the K/V row reads of kv block t+2: every
 // MFMA's LDS operands are requested a phase before it issues. dS^T stays in registers as the B
-// operand. The two kv halves' partial dQ^T are summed through LDS once per q block.
+// operand. The two kv halves' partial dQ^T are summed through LDS once per q block. On request the
+// lists run in kv-range chunks, one launch each, dQ carried between launches as fp32 partial sums.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
