@@ -40,6 +40,17 @@ namespace {
 constexpr int TILE = 16384;         // one [64][128] bf16 tile
 constexpr float RESCALE_GAP = 8.f;  // raise the running max only when exceeded by this much
 
+__device__ __forceinline__ bf16x8 neg8(bf16x8 v) {  // exact: flips the eight sign bits
+  union {
+    bf16x8 b;
+    uint32_t u[4];
+  } r;
+  r.b = v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.u[i] ^= 0x80008000u;
+  return r.b;
+}
+
 }  // namespace
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -88,6 +99,16 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = qr[2 * s + g];
   }
+  // The softmax below wants a positive scale. A negative one is moved into Q (negating a bf16 is
+  // exact, and so is the negated MFMA sum, so every score s * scale keeps its value); a zero one
+  // becomes the least normal float, which changes every finite score by at most 2^-126 |s|.
+  float scale_log2 = p.scale_log2;
+  if (scale_log2 < 0.f) {
+    scale_log2 = -scale_log2;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = neg8(qf[s]);
+  }
+  scale_log2 = fmaxf(scale_log2, 1.17549435e-38f);
 
   // list entry t (clamped to the list; an out-of-range kv id is read as block 0, masked entirely)
   auto kv_raw = [&](int t) { return ld_const(list, t < n ? t : n - 1); };
@@ -104,11 +125,34 @@ fwd_kernel(FwdParams p) {
     dma_tile(p.v + head + tile_of(kb), toff, lds0 + (2 + st) * TILE);
   };
   const int kv_l = 32 * wk + l32;  // this lane's kv row of the A operand of S^T
+  // LDS byte addresses of this lane's operand reads in stage 0 of the rings: the K rows (A operand
+  // of S^T: chunk 2s + g of kv row kv_l) and the V^T operands of k-step 0 (d tile dt, row half h).
+  // The stage (one tile further) and the V^T k-step (16 rows = 4 KiB further, where the swizzle
+  // repeats) differ by constants, which the reads carry as immediate offsets; the loop is unrolled
+  // by two so the stage is a constant. The empty asm keeps the addresses in registers.
+  uint32_t ka_at[8], va_at[4][2];
+  {
+    const uint32_t base = lds_addr((VSA_LDS char*)kv_s);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) ka_at[s] = base + tile_byte(kv_l, 2 * s + g);
+    const int r0 = 32 * wk + 4 * g + (t16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int col = 32 * dt + 16 * (grp & 1) + 4 * (t16 & 3);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        va_at[dt][h] = base + 2 * TILE + tile_elem_byte(r0 + 8 * h, col);
+        asm volatile("" : "+v"(va_at[dt][h]));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(ka_at[s]));
+  }
   // A operand of S^T (K rows) from K stage st
   auto read_k = [&](int st, bf16x8 (&ka)[8]) __attribute__((always_inline)) {
-    const VSA_LDS char* kt = (const VSA_LDS char*)kv_s + st * TILE;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) ka[s] = *(const VSA_LDS bf16x8*)(kt + tile_byte(kv_l, 2 * s + g));
+    for (int s = 0; s < 8; ++s)
+      ka[s] = *(const VSA_LDS bf16x8*)(uintptr_t)(ka_at[s] + st * TILE);
   };
 
   f32x16 oacc[4];
@@ -126,7 +170,6 @@ fwd_kernel(FwdParams p) {
     m_run = state[64 * 64];
     l_run = state[65 * 64];
   }
-  const float scale_log2 = p.scale_log2;
 
   // Block t: K in K stage t % 2, V in V stage t % 2. The S^T tile of block t is computed during
   // step t-1 (the prologue for t = 0), so step t overlaps the softmax of t with the S^T MFMAs of
@@ -153,8 +196,7 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) sacc = mfma32(ka[s], qf[s], sacc);
   }
-  for (int t = 0; t < n; ++t) {
-    const int st = t & 1;
+  auto step = [&](int t, int st) __attribute__((always_inline)) {
     // K of t+1 and V of t landed (own DMAs, then the barrier: everyone's); everyone is done with
     // K of t and V of t-1
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -170,24 +212,23 @@ fwd_kernel(FwdParams p) {
     issue_k(e2, st);
     // V^T operands of O^T += V^T P^T: k-step c, slot j is kv 32wk + 16c + 8(j/4) + 4g + j%4 (the
     // D-layout order of S^T); d tile dt, lane's d = 32dt + l32
-    const VSA_LDS char* vt = (const VSA_LDS char*)kv_s + (2 + st) * TILE;
     bf16x8 va[4][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int r0 = 32 * wk + 16 * c + 4 * g + (t16 >> 2);
+      const uint32_t o = st * TILE + c * 4096;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int col = 32 * dt + 16 * (grp & 1) + 4 * (t16 & 3);
-        va[dt][c] = join(lds_read_tr(vt + tile_elem_byte(r0, col)),
-                         lds_read_tr(vt + tile_elem_byte(r0 + 8, col)));
-      }
+      for (int dt = 0; dt < 4; ++dt)
+        va[dt][c] = join(lds_read_tr((const VSA_LDS void*)(uintptr_t)(va_at[dt][0] + o)),
+                         lds_read_tr((const VSA_LDS void*)(uintptr_t)(va_at[dt][1] + o)));
     }
     issue_v(e1, st ^ 1);
 
     // softmax of block t. S^T element i is kv 32wk + 8(i/4) + 4g + i%4, q = this lane's column.
+    // The scores stay unscaled (the scale is positive, see above): the block max of s * scale is
+    // the max of s times scale (rounding is monotone), and each exponent is one fma(s, scale, -m).
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = sacc[i] * scale_log2;
+    for (int i = 0; i < 16; ++i) x[i] = sacc[i];
     if (vb < BLOCK) {  // ragged or invalid block: mask kv rows >= vb
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -199,6 +240,7 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
     mx = pair_max32(mx);
+    mx *= scale_log2;
     // raise the running max (and rescale) only when this block's max exceeds it by the gap;
     // both lanes of a q column decide alike, and the branch is taken by the whole wave
     const bool raise = mx > m_run + RESCALE_GAP;
@@ -221,7 +263,7 @@ fwd_kernel(FwdParams p) {
     float rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scale_log2, -m_use));
       rs += pv[i];
     }
     l_run += pair_sum32(rs);
@@ -241,7 +283,13 @@ fwd_kernel(FwdParams p) {
     e1 = e2;
     e2 = e3;
     vb0 = vb1;
+  };
+  int t = 0;
+  for (; t + 1 < n; t += 2) {
+    step(t, 0);
+    step(t + 1, 1);
   }
+  if (t < n) step(t, 0);
 
   if (!last) {  // save the state for the next chunk, exactly
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no DMA may still write this workgroup's LDS

@@ -16,6 +16,7 @@ Gates (per tensor):
 Small workloads are compared in full; the 32k and 65k-token workloads on sampled blocks, each
 computed by the oracle one block at a time, plus invariants that hold at any size.
 """
+import dataclasses
 import itertools
 import json
 
@@ -244,6 +245,22 @@ def test_forward_ignores_out_of_range_kv_ids():
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
     assert torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.3])
+def test_forward_scale_sign_and_zero(scale):
+    """The forward with a negative, a zero and a large positive sm_scale (the kernel keeps its
+    scores unscaled and needs a positive factor: a negative one moves into Q, a zero one becomes
+    the least normal float) against the oracle at that scale, on the ragged config with empty kv
+    blocks. At zero every valid key weighs the same: lse = log2(#valid keys)."""
+    c = dataclasses.replace(workloads.config(2), sm_scale=scale)
+    d = to_dev(c)
+    say(f"[forward] sm_scale {scale}")
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"], sm_scale=scale,
+                       out=(nan_like(d["q"]), nan_like(torch.empty(c.B, c.H, c.S, dtype=torch.float32,
+                                                                   device=DEV))))
+    torch.cuda.synchronize()
+    _fwd_compare(c, d, o, lse)
 
 
 # -----------------------------------------------------------------------------------------------
