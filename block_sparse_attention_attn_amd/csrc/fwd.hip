@@ -236,6 +236,11 @@ fwd_kernel(FwdParams p) {
         x[i] = kv < vb ? x[i] : -__builtin_inff();
       }
     }
+    // the first half of the S^T MFMAs of t+1 under the block max, the second half under the
+    // exponentials (no MFMA-free stretch while the max and the rescale test run)
+    f32x16 snext = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) snext = mfma32(ka[s], qf[s], snext);
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
@@ -256,9 +261,8 @@ fwd_kernel(FwdParams p) {
     }
     const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
     // exponentials of t under the S^T MFMAs of t+1, then the O^T MFMAs of t
-    f32x16 snext = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) snext = mfma32(ka[s], qf[s], snext);
+    for (int s = 4; s < 8; ++s) snext = mfma32(ka[s], qf[s], snext);
     float pv[16];
     float rs = 0.f;
 #pragma unroll
