@@ -364,6 +364,34 @@ def test_backward_edge_cases(name, mode):
 
 
 @pytest.mark.parametrize("mode", sorted(MODES))
+def test_rows_without_valid_keys(mode):
+    """q blocks whose every selected kv block is fully padded (vbs 0): their rows have no valid
+    key, so the forward gives o = 0 and lse = -inf, and the backward (given that lse) gives their
+    dq rows exactly 0 and no NaN anywhere, although the kv-major kernel's P of such a row is not
+    finite (the padded kv rows of dK/dV and the padded slots of dS never reach an output)."""
+    c = workloads.make_case(1, 2, 6, 3, seed=29, vbs=[64, 0, 64, 0, 40, 64], name="no_valid_keys")
+    c.q2k_idx[0, 0, 2] = torch.tensor([1, 0, 0], dtype=torch.int32)  # only kv block 1
+    c.q2k_num[0, 0, 2] = 1
+    c.q2k_idx[0, 1, 5] = torch.tensor([3, 1, 0], dtype=torch.int32)  # kv blocks 3 and 1
+    c.q2k_num[0, 1, 5] = 2
+    d = to_dev(c)
+    say(f"[forward] rows without valid keys")
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    torch.cuda.synchronize()
+    _fwd_compare(c, d, o, lse)
+    for h, qb in ((0, 2), (1, 5)):
+        rows = slice(qb * 64, (qb + 1) * 64)
+        assert torch.all(o[0, h, rows] == 0)
+        assert torch.all(lse[0, h, rows] == -float("inf"))
+    dq, dk, dv, rdq, rdk, rdv = _bwd_small(c, "rows without valid keys", MODES[mode])
+    for got, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
+        g = got.float().cpu().numpy()
+        assert np.all(np.isfinite(g))
+        assert np.all(g[ref == 0] == 0)
+    assert torch.all(dq[0, 0, 128:192] == 0) and torch.all(dq[0, 1, 320:384] == 0)
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
 @pytest.mark.parametrize("case,chunk", [(2, 3), (2, 1), ("odd_blocks_ragged", 2),
                                         ("empty_q_blocks", 4), ("pool_excludes_three", 5)])
 def test_backward_q_range_chunks(case, chunk, mode):
