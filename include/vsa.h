@@ -87,7 +87,7 @@ typedef struct {
   void* o;                /* bf16 [B, H, S, 128], output */
   float* lse;             /* fp32 [B, H, S], output */
   int batch, heads, seqlen, head_dim, num_kv_blocks, q2k_stride;
-  float sm_scale;
+  float sm_scale;         /* finite; negative and zero are allowed (zero acts as 2^-126) */
   void* workspace;        /* see above; may be NULL when vsa_fwd_workspace_bytes is 0 */
   size_t workspace_bytes;
   int kv_chunk_blocks;    /* kv-range chunks, see above; 0 = default */
@@ -221,7 +221,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   int batch, heads, seqlen, head_dim, num_kv_blocks, max_q_blocks, q2k_stride;
-  float sm_scale;
+  float sm_scale;         /* finite, |sm_scale * log2 e| >= 2^-120 (the records divide lse by it) */
   int dq_mode;            /* vsa_dq_mode */
   int chunk_blocks;       /* blocks per chunk of the main kernels, see above; 0 = default */
 } vsa_bwd_args;

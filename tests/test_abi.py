@@ -169,6 +169,8 @@ def test_bwd_check_accepts_a_valid_call():
     (dict(max_q_blocks=0), VSA_EINVAL),
     (dict(sm_scale=float("nan")), VSA_EINVAL),
     (dict(sm_scale=float("inf")), VSA_EINVAL),
+    (dict(sm_scale=0.0), VSA_EINVAL),
+    (dict(sm_scale=-1e-37), VSA_EINVAL),
     (dict(q=None), VSA_EINVAL),
     (dict(lse=None), VSA_EINVAL),
     (dict(k2q_idx=None), VSA_EINVAL),

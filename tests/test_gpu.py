@@ -283,21 +283,21 @@ def _bwd_small(c, label, mode=V.DQ_RECOMPUTE):
     out = (nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"]))
     say(f"[backward] {label} (q2k derived from k2q, dq mode {mode})")
     plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
-                     workspace=ws, out=out, dq_mode=mode)
+                     sm_scale=c.sm_scale, workspace=ws, out=out, dq_mode=mode)
     dq, dk, dv = plan.run()
     torch.cuda.synchronize()
     # the same call with the forward's q2k lists given: bit-identical results
     say(f"[backward] {label} (q2k given)")
     given = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num,
-                                d["vbs"], q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"],
-                                dq_mode=mode)
+                                d["vbs"], sm_scale=c.sm_scale, q2k_idx=d["q2k_idx"],
+                                q2k_num=d["q2k_num"], dq_mode=mode)
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv), given):
         assert torch.equal(a, b)
     if mode == V.DQ_SPILL:
         # dk, dv come from the same kernel arithmetic in both modes: identical bits
         other = V.backward_from_k2q(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num,
-                                    d["vbs"], dq_mode=V.DQ_RECOMPUTE)
+                                    d["vbs"], sm_scale=c.sm_scale, dq_mode=V.DQ_RECOMPUTE)
         torch.cuda.synchronize()
         assert torch.equal(dk, other[1]) and torch.equal(dv, other[2])
     rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
@@ -361,6 +361,14 @@ def test_backward_edge_cases(name, mode):
     for got, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
         zero = ref == 0
         assert np.all(got.float().cpu().numpy()[zero] == 0)
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_backward_negative_scale(mode):
+    """The backward with a negative sm_scale (the records hold lse / scale_log2, negative here)
+    against the oracle at that scale, on the ragged config with empty kv blocks."""
+    c = dataclasses.replace(workloads.config(2), sm_scale=-0.0883883)
+    _bwd_small(c, "negative sm_scale", MODES[mode])
 
 
 @pytest.mark.parametrize("mode", sorted(MODES))
