@@ -27,6 +27,9 @@
 //     contraction index is permuted to match); V^T comes from ds_read_b64_tr_b16.
 //   * K and V tiles arrive by global_load_lds_dwordx4 into two-stage LDS rings, K two blocks and
 //     V one block ahead: the S^T MFMAs of block t+1 run under the softmax of block t.
+//   * The loop is unrolled by two so the ring stages are constants: each lane's LDS operand
+//     addresses are computed once, and the stage rides as an immediate offset. Scores stay
+//     unscaled: the block max is taken on raw scores and each exponent is one fma.
 //   * Long lists run in kv-range chunks, one launch each, each wave carrying its running O^T,
 //     max and sum to the next launch exactly: the workgroups on an XCD then share one window of
 //     K/V tiles at a time, and the results are those of one launch, bit for bit.
