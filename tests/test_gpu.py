@@ -383,7 +383,7 @@ def test_rows_without_valid_keys(mode):
     c.q2k_idx[0, 1, 5] = torch.tensor([3, 1, 0], dtype=torch.int32)  # kv blocks 3 and 1
     c.q2k_num[0, 1, 5] = 2
     d = to_dev(c)
-    say(f"[forward] rows without valid keys")
+    say("[forward] rows without valid keys")
     o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
     torch.cuda.synchronize()
     _fwd_compare(c, d, o, lse)
