@@ -5,6 +5,7 @@ case (dense attention = torch's scaled_dot_product_attention in float64 with aut
 finite differences of the forward, closed forms, invariants of the softmax gradient, exact zeros
 that the FastVideo backward test page requires, and small hand-worked metadata fixtures.
 """
+import dataclasses
 import itertools
 import json
 import os
@@ -86,6 +87,29 @@ def test_masked_ragged_matches_sdpa_with_mask(seed):
     _close(dv, ref_dv)
     # the literal dense mask of the page's reference agrees with the torch-built one
     assert np.array_equal(O.dense_keep_mask(c.q2k_idx, c.q2k_num, c.vbs, c.S), mask.numpy())
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.3])
+def test_masked_ragged_any_scale_matches_sdpa(scale):
+    """The masked ragged case at a negative, a zero and a large positive sm_scale (the scales the
+    GPU tests use) against SDPA with the same scale and mask; lse against scipy's logsumexp of
+    the masked scores."""
+    c = _case(nb=6, topk=3, H=2, seed=5, vbs=[64, 37, 64, 50, 64, 1], kv_pool=[0, 1, 2, 3, 5])
+    c = dataclasses.replace(c, sm_scale=scale)
+    mask = _mask_torch(c)
+    o, lse = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    ref_o, ref_dq, ref_dk, ref_dv = _sdpa_grads(c, mask)
+    _close(o, ref_o)
+    s = scale * np.einsum("bhid,bhjd->bhij", O.f64(c.q), O.f64(c.k))
+    s = np.where(mask.numpy(), s, -np.inf)
+    _close(lse, scipy.special.logsumexp(s, axis=-1) * O.LOG2E)
+    dq, dk, dv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    _close(dv, ref_dv)
+    if scale == 0.0:  # dq and dk carry the scale
+        assert not dq.any() and not dk.any()
+    else:
+        _close(dq, ref_dq)
+        _close(dk, ref_dk)
 
 
 # ---------------------------------------------------------------------------------------------
