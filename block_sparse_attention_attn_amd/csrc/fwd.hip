@@ -206,6 +206,10 @@ fwd_kernel(FwdParams p) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), visible to the compiler
     asm volatile("s_barrier" ::: "memory");
     const int vb = vb0;
+    // Raised wave priority from here to the rescale test: of the two waves sharing a SIMD, the one
+    // issuing its operand reads, DMAs and first S^T MFMAs goes first, the other's exponentials
+    // fill in behind (5 % faster than no priority, 1.155 against 1.219 ms at 32768 tokens).
+    __builtin_amdgcn_s_setprio(1);
 
     // Each DMA follows the LDS reads of its kind (the asm keeps its place among them), so the
     // reads of this step are requested first and the two DMA groups reach the address unit
@@ -262,6 +266,7 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
     }
+    __builtin_amdgcn_s_setprio(0);
     const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
     // exponentials of t under the S^T MFMAs of t+1, then the O^T MFMAs of t
 #pragma unroll
