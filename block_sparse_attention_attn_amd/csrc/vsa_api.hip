@@ -113,6 +113,9 @@ int vsa_invert_indices(const int32_t* q2k_idx, const int32_t* q2k_num, int batch
 // forward
 // ------------------------------------------------------------------------------------------------
 
+}  // extern "C"
+
+// helpers: C++ linkage, internal to this file
 namespace {
 
 // kv blocks per kv-range chunk of the forward (0: one launch), like chunk_q_blocks
@@ -129,6 +132,8 @@ size_t fwd_bounds_bytes(size_t items, int nchunks) {
 }
 
 }  // namespace
+
+extern "C" {
 
 size_t vsa_fwd_workspace_bytes(int batch, int heads, int seqlen, int kv_chunk_blocks) {
   if (!dims_ok(batch, heads, seqlen, seqlen / vsa::BLOCK)) return 0;
@@ -312,6 +317,9 @@ int vsa_bwd_order(const int32_t* k2q_num, int batch, int heads, int num_kv_block
   return launch_status("vsa_bwd_order");
 }
 
+}  // extern "C"
+
+// helpers: C++ linkage, internal to this file
 namespace {
 
 bool uses_device_order(const vsa_bwd_args* a) {
@@ -497,6 +505,8 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
 }
 
 }  // namespace
+
+extern "C" {
 
 int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream) {
   const int st = vsa_bwd_check(a);

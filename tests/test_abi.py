@@ -4,6 +4,8 @@ right status before anything is launched (validation never touches the device)."
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -31,6 +33,19 @@ def test_library_exports_every_declared_function():
         assert hasattr(handle, n), f"libvsa.so does not export {n}"
     # and the binding declares exactly those
     assert sorted(V._SIGNATURES) == names
+
+
+@pytest.mark.skipif(shutil.which("nm") is None, reason="nm not available")
+def test_library_exports_no_unprefixed_c_symbols():
+    """Every function the library exports under a plain C name is part of the declared API
+    (vsa_*): the host-side helpers have internal linkage, so no generic name (run_stage, ...)
+    can clash with a caller's symbols. C++ names are mangled into the vsa namespace."""
+    out = subprocess.run(["nm", "-D", "--defined-only", V.library_path()], check=True,
+                         capture_output=True, text=True).stdout
+    plain = [f[2] for f in (l.split() for l in out.splitlines())
+             if len(f) == 3 and f[1] == "T" and not f[2].startswith("_Z")]
+    assert plain and all(n.startswith("vsa_") for n in plain), plain
+    assert sorted(plain) == _declared_functions()
 
 
 def test_binding_constants_match_the_header():
