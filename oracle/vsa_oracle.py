@@ -98,9 +98,11 @@ def selection(q2k_idx, q2k_num, nkv: int) -> np.ndarray:
     num = i64(q2k_num)
     B, H, nq, K = idx.shape
     sel = np.zeros((B, H, nq, nkv), dtype=bool)
-    valid = np.arange(K)[None, None, None, :] < num[..., None]
-    b, h, qb, t = np.nonzero(valid)
-    sel[b, h, qb, idx[b, h, qb, t]] = True
+    rows = np.broadcast_to(np.arange(nq)[:, None], (nq, K))
+    for b in range(B):
+        for h in range(H):
+            counted = np.arange(K)[None, :] < num[b, h][:, None]   # [nq, K]
+            sel[b, h, rows[counted], idx[b, h][counted]] = True
     return sel
 
 
@@ -117,7 +119,7 @@ def invert_indices(q2k_idx, q2k_num, nkv: int):
     k2q_idx = np.zeros((B, H, nkv, nq), dtype=np.int32)
     for b in range(B):
         for h in range(H):
-            rel = sel[b, h].T                         # [nkv, nq]: row kb lists its q blocks
+            rel = np.ascontiguousarray(sel[b, h].T)   # [nkv, nq]: row kb lists its q blocks
             for kb in range(nkv):
                 qbs = np.flatnonzero(rel[kb])         # ascending by construction
                 k2q_num[b, h, kb] = qbs.size
@@ -303,3 +305,81 @@ def delta(o, do) -> np.ndarray:
     """Delta[b, h, i] = sum_d o[b,h,i,d] * dO[b,h,i,d] for the o given (the backward's
     preprocess row sum, taken on whatever o the caller holds), float64."""
     return np.sum(f64(o) * f64(do), axis=-1)
+
+
+def kvblock_backward(q, k, v, do, q2k_idx, q2k_num, vbs, sm_scale: float, kvblocks,
+                     precision: str = "float64", progress=None):
+    """dk and dv rows of chosen kv blocks, straight from their definition [bwd-test, reference:
+    the gradient of sum(o * grad_o)]:
+
+        dV_j = sum_i P_ij^T dO_i,   dK_j = sm_scale * sum_i dS_ij^T Q_i,
+        dS_ij = P_ij * (dP_ij - Delta_i),  dP_ij = dO_i V_j^T,  Delta_i = rowsum(o_i * dO_i),
+
+    summed over every q block i whose counted q2k entries name block j, where P_ij is the
+    block-j columns of q block i's softmax over its full key set. Only those columns of the
+    gradient are formed, so a kv block costs the softmax statistics and o of the q blocks that
+    select it; q blocks selecting several of the chosen kv blocks are computed once.
+
+    The softmax of q block i runs over the whole 64-row tiles of its selected kv blocks, with the
+    scores of padded rows (at or past vbs) set to -inf: the masked-dense form of [bwd-test].
+
+    ``precision``: "float64", or "float32" for the work over a q block's full key set (its scores,
+    exp(s - max), their row sum and o = P V), as the largest workloads need (about 2e-7
+    relative); every product with the chosen kv blocks stays float64. ``progress``: called with
+    (done, total) q blocks now and then. Works on torch CPU tensors (threaded).
+    Returns {(b, h, kb): (dk [64, D], dv [64, D])}.
+    """
+    import torch
+
+    def t64(x):
+        return x.detach().to("cpu", torch.float64) if isinstance(x, torch.Tensor) \
+            else torch.from_numpy(np.asarray(x, dtype=np.float64))
+
+    wd = torch.float64 if precision == "float64" else torch.float32
+    idx, num, vb = i64(q2k_idx), i64(q2k_num), i64(vbs)
+    nb = vb.shape[0]
+    counted = np.arange(idx.shape[-1])[None, :] < num[..., None]     # [B, H, nq, K]
+    out = {}
+    heads = sorted({(b, h) for b, h, _ in kvblocks})
+    for b, h in heads:
+        want = sorted({kb for bb, hh, kb in kvblocks if (bb, hh) == (b, h)})
+        Q, K, V, DO = (t64(x[b, h]) for x in (q, k, v, do))
+        D = Q.shape[-1]
+        Kb = K.to(wd).reshape(nb, BLOCK, D)
+        Vb = V.to(wd).reshape(nb, BLOCK, D)
+        acc = {kb: (torch.zeros(BLOCK, D, dtype=torch.float64),
+                    torch.zeros(BLOCK, D, dtype=torch.float64)) for kb in want}
+        sel_rows = counted[b, h] & np.isin(idx[b, h], want)
+        qblocks = np.flatnonzero(sel_rows.any(axis=1)).tolist()
+        for n_done, qb in enumerate(qblocks):
+            if progress is not None and n_done % 200 == 0:
+                progress(n_done, len(qblocks))
+            blocks = np.unique(idx[b, h, qb, :num[b, h, qb]])
+            blocks_t = torch.from_numpy(blocks)
+            qi = Q[qb * BLOCK:(qb + 1) * BLOCK]
+            doi = DO[qb * BLOCK:(qb + 1) * BLOCK]
+            # scores of every row of the selected tiles, (K q^T)^T: one tall product
+            s = sm_scale * (torch.index_select(Kb, 0, blocks_t).reshape(-1, D) @ qi.to(wd).T).T
+            if (vb[blocks] < BLOCK).any():
+                rows_ok = torch.from_numpy(
+                    (np.arange(BLOCK)[None, :] < vb[blocks][:, None]).reshape(-1))
+                s = s.masked_fill(~rows_ok[None, :], float("-inf"))
+            m = s.max(dim=1, keepdim=True).values
+            e = torch.exp(s - m)
+            l = e.sum(dim=1, keepdim=True).to(torch.float64)
+            o = (e @ torch.index_select(Vb, 0, blocks_t).reshape(-1, D)).to(torch.float64) / l
+            delta_i = (o * doi).sum(dim=1, keepdim=True)
+            for pos in np.flatnonzero(np.isin(blocks, want)).tolist():
+                kb = int(blocks[pos])
+                nvalid = int(vb[kb])
+                if nvalid <= 0:
+                    continue
+                pj = e[:, pos * BLOCK:pos * BLOCK + nvalid].to(torch.float64) / l
+                vj = V[kb * BLOCK:kb * BLOCK + nvalid]
+                dsj = pj * (doi @ vj.T - delta_i)
+                dk_acc, dv_acc = acc[kb]
+                dk_acc[:nvalid] += sm_scale * (dsj.T @ qi)
+                dv_acc[:nvalid] += pj.T @ doi
+        for kb in want:
+            out[(b, h, kb)] = (acc[kb][0].numpy(), acc[kb][1].numpy())
+    return out

@@ -276,30 +276,35 @@ def test_invert_matches_hand_worked_fixture():
     assert idx.tolist() == g["k2q_idx"] and num.tolist() == g["k2q_num"]
 
 
-def _invert_by_stable_sort(q2k_idx, q2k_num, nkv):
-    """An independent construction (the route of the page's test helper): stable-sort the
-    (row, q block) keys of every counted selection, count per row, and place them by rank."""
-    idx = torch.as_tensor(q2k_idx).long()
-    num = torch.as_tensor(q2k_num).long()
-    B, H, nq, K = idx.shape
-    valid = torch.arange(K).view(1, 1, 1, K) < num.view(B, H, nq, 1)
-    row = (torch.arange(B * H).view(B, H, 1, 1) * nkv + idx)[valid]
-    qb = torch.arange(nq).view(1, 1, nq, 1).expand(B, H, nq, K)[valid]
-    order = torch.sort(row * nq + qb, stable=True).indices
-    row, qb = row[order], qb[order]
-    counts = torch.bincount(row, minlength=B * H * nkv)
-    starts = torch.cumsum(counts, 0) - counts
-    slot = torch.arange(row.numel()) - starts[row]
-    out = torch.zeros(B * H * nkv, nq, dtype=torch.int32)
-    out[row, slot] = qb.to(torch.int32)
-    return out.view(B, H, nkv, nq).numpy(), counts.view(B, H, nkv).to(torch.int32).numpy()
+def _invert_by_scanning_rows(q2k_idx, q2k_num, nkv):
+    """A second construction of the inversion, from the definition of a k2q row: walk the q
+    blocks of each (b, h) in increasing order and append each one to the list of every kv block
+    its counted q2k entries name, unless that list already ends with it (a repeated id). Lists
+    built this way are ascending without any sorting; they are then written out zero-padded."""
+    idx = np.asarray(q2k_idx, dtype=np.int64)
+    num = np.asarray(q2k_num, dtype=np.int64)
+    B, H, nq, _ = idx.shape
+    out_idx = np.zeros((B, H, nkv, nq), dtype=np.int32)
+    out_num = np.zeros((B, H, nkv), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            lists = {}
+            for qb in range(nq):
+                for kb in idx[b, h, qb, :num[b, h, qb]].tolist():
+                    lst = lists.setdefault(kb, [])
+                    if not lst or lst[-1] != qb:
+                        lst.append(qb)
+            for kb, lst in lists.items():
+                out_num[b, h, kb] = len(lst)
+                out_idx[b, h, kb, :len(lst)] = lst
+    return out_idx, out_num
 
 
 @pytest.mark.parametrize("n", [1, 2])
-def test_invert_matches_sort_construction_and_invariants(n):
+def test_invert_matches_row_scan_construction_and_invariants(n):
     c = workloads.config(n)
     idx, num = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
-    ridx, rnum = _invert_by_stable_sort(c.q2k_idx, c.q2k_num, c.nb)
+    ridx, rnum = _invert_by_scanning_rows(c.q2k_idx, c.q2k_num, c.nb)
     assert np.array_equal(idx, ridx) and np.array_equal(num, rnum)
     assert int(num.sum()) == int(c.q2k_num.sum())
     B, H = c.B, c.H
@@ -310,6 +315,40 @@ def test_invert_matches_sort_construction_and_invariants(n):
             assert listed.count(qb) == 1 and listed == sorted(listed)
     if n == 2:
         assert np.all(num[:, :, 4] == 0) and np.all(num[:, :, 11] == 0)
+
+
+def test_invert_row_scan_with_duplicates_and_rectangular_shape():
+    """Repeated kv ids in a q2k row, counts below the row width (entries past a count are never
+    read) and nq != nkv: both constructions agree."""
+    g = torch.Generator().manual_seed(9)
+    B, H, nq, nkv, K = 2, 3, 40, 70, 9
+    idx = torch.randint(0, nkv, (B, H, nq, K), generator=g, dtype=torch.int32)
+    idx[..., 1] = idx[..., 0]
+    num = torch.randint(0, K + 1, (B, H, nq), generator=g, dtype=torch.int32)
+    got = O.invert_indices(idx, num, nkv)
+    want = _invert_by_scanning_rows(idx.numpy(), num.numpy(), nkv)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_delta_is_the_p_weighted_mean_of_dp():
+    """Delta_i = rowsum(o_i * dO_i) equals sum_j P_ij dP_ij with dP = dO V^T, because o = P V.
+    P here is torch's softmax of the masked scores (mask built by torch ops), o comes from
+    SDPA; the oracle's delta() only sees o and dO. Ragged blocks, an unselected kv block."""
+    c = _case(nb=6, topk=3, H=2, B=2, seed=13, vbs=[64, 37, 64, 50, 64, 1],
+              kv_pool=[0, 1, 2, 3, 5])
+    mask = _mask_torch(c)
+    q, k, v, do = (t.to(torch.float64) for t in (c.q, c.k, c.v, c.do))
+    s = c.sm_scale * q @ k.transpose(-1, -2)
+    p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)
+    dp = do @ v.transpose(-1, -2)
+    want = (p * dp).sum(-1).numpy()
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask,
+                                                         scale=c.sm_scale)
+    got = O.delta(o, c.do)
+    _close(got, want, 1e-12)
+    # and it is what the oracle's own gradient subtracts: the dS row sums vanish with it
+    ds = p * (dp - torch.from_numpy(got)[..., None])
+    assert ds.sum(-1).abs().max().item() <= 1e-12 * max(1.0, ds.abs().max().item())
 
 
 def test_work_order_matches_hand_worked_fixture_and_invariants():
