@@ -248,6 +248,25 @@ def test_sampled_backward_matches_full():
         assert np.allclose(sdkv[(b, h, kb)][1], dv[b, h, kb * 64:(kb + 1) * 64], atol=1e-13)
 
 
+@pytest.mark.parametrize("precision,tol", [("float64", 1e-13), ("float32", 1e-5)])
+def test_kvblock_backward_matches_full(precision, tol):
+    """The per-kv-block gradient (used at sizes where the full backward is out of reach) equals
+    the full backward's rows: ragged blocks, an unselected block, a block sharing q blocks with
+    another requested one, in both precisions."""
+    c = workloads.config(2)
+    dq, dk, dv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    kbs = [(0, 1, 7), (1, 0, 15), (0, 0, 4), (1, 1, 0), (0, 1, 15), (0, 1, 3)]
+    got = O.kvblock_backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale, kbs,
+                             precision)
+    assert sorted(got) == sorted(kbs)
+    for (b, h, kb), (gk, gv) in got.items():
+        rows = slice(kb * 64, (kb + 1) * 64)
+        _close(gk, dk[b, h, rows], tol * np.abs(dk[b, h]).max() / max(np.abs(dk[b, h, rows]).max(), 1e-30))
+        _close(gv, dv[b, h, rows], tol * np.abs(dv[b, h]).max() / max(np.abs(dv[b, h, rows]).max(), 1e-30))
+    assert not got[(0, 0, 4)][0].any() and not got[(0, 0, 4)][1].any()   # selected by nobody
+    assert not got[(1, 0, 15)][0][37:].any()                              # padded rows
+
+
 # ---------------------------------------------------------------------------------------------
 # rounding helper
 # ---------------------------------------------------------------------------------------------
