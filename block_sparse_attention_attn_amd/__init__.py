@@ -29,7 +29,7 @@ __all__ = [
     "CHUNK_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
-    "DQ_RECOMPUTE", "DQ_SPILL",
+    "DQ_RECOMPUTE", "DQ_SPILL", "default_dq_mode",
 ]
 
 BLOCK = 64
@@ -152,6 +152,40 @@ def _act(t: torch.Tensor, name: str, shape) -> None:
         raise RuntimeError(f"{name} must be contiguous")
 
 
+def _same_device(t: torch.Tensor, name: str, device: torch.device) -> None:
+    _need_gpu(t, name)
+    if t.device != device:
+        raise RuntimeError(f"{name} is on {t.device}, expected {device}")
+
+
+def _out(t: torch.Tensor, name: str, shape, dtype, device: torch.device) -> torch.Tensor:
+    """A caller-supplied output: on the device, of the dtype and shape, contiguous (the kernels
+    write it through a raw pointer, so anything else would be written out of bounds)."""
+    _same_device(t, name, device)
+    if t.dtype != dtype:
+        raise RuntimeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise RuntimeError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+    return t
+
+
+def _workspace(t: Optional[torch.Tensor], need: int, device: torch.device,
+               what: str) -> torch.Tensor:
+    """The caller's workspace (a contiguous uint8 tensor of at least `need` bytes on the device),
+    or a new one."""
+    if t is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _same_device(t, f"{what} workspace", device)
+    if t.dtype != torch.uint8 or not t.is_contiguous():
+        raise RuntimeError(f"{what} workspace must be a contiguous uint8 tensor, got {t.dtype}"
+                           f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    if t.numel() < need:
+        raise RuntimeError(f"{what} workspace holds {t.numel()} bytes, needs {need}")
+    return t
+
+
 def _idx(t: torch.Tensor, name: str) -> torch.Tensor:
     """Metadata: an integer GPU tensor, converted to contiguous int32 (value-preserving)."""
     _need_gpu(t, name)
@@ -191,14 +225,15 @@ def invert_indices(q2k_idx: torch.Tensor, q2k_num: torch.Tensor, num_kv_blocks: 
                            "[B, H, nq, topk] and [B, H, nq]")
     B, H, nq, topk = idx.shape
     dev = idx.device
+    _same_device(num, "q2k_num", dev)
     if out is None:
         k2q_idx = torch.empty((B, H, num_kv_blocks, nq), dtype=torch.int32, device=dev)
         k2q_num = torch.empty((B, H, num_kv_blocks), dtype=torch.int32, device=dev)
     else:
-        k2q_idx, k2q_num = out
+        k2q_idx = _out(out[0], "k2q_idx out", (B, H, num_kv_blocks, nq), torch.int32, dev)
+        k2q_num = _out(out[1], "k2q_num out", (B, H, num_kv_blocks), torch.int32, dev)
     need = invert_workspace_bytes(B, H, nq, num_kv_blocks)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev, "invert_indices")
     st = lib().vsa_invert_indices(idx.data_ptr(), num.data_ptr(), B, H, nq, topk, num_kv_blocks,
                                   k2q_idx.data_ptr(), k2q_num.data_ptr(), workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), _stream(dev))
@@ -224,11 +259,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
     if q.dim() != 4:
         raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
     B, H, S, D = q.shape
+    dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _act(t, n, (B, H, S, D))
+        _same_device(t, n, dev)
     idx = _idx(q2k_idx, "q2k_idx")
     num = _idx(q2k_num, "q2k_num")
     vbs = _idx(variable_block_sizes, "variable_block_sizes")
+    for t, n in ((idx, "q2k_idx"), (num, "q2k_num"), (vbs, "variable_block_sizes")):
+        _same_device(t, n, dev)
     nb = vbs.numel()
     if idx.dim() != 4:
         idx = idx.view(B, H, -1, idx.shape[-1])
@@ -240,12 +279,13 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         o = torch.empty_like(q)
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     else:
-        o, lse = out
+        o = _out(out[0], "o out", (B, H, S, D), torch.bfloat16, dev)
+        lse = _out(out[1], "lse out", (B, H, S), torch.float32, dev)
     need = fwd_workspace_bytes(B, H, S, kv_chunk_blocks)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if need or workspace is not None:
+        workspace = _workspace(workspace, need, dev, "forward")
     a = _FwdArgs(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), num.data_ptr(),
                  vbs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, S, D, nb, idx.shape[-1],
                  float(sm_scale), _ptr(workspace),
@@ -270,6 +310,24 @@ def bwd_workspace_offset(batch: int, heads: int, seqlen: int, region: int, q2k_s
                                               chunk_blocks, region))
 
 
+def default_dq_mode(batch: int, heads: int, seqlen: int, q2k_stride: int = 0,
+                    chunk_blocks: int = 0, device=None) -> int:
+    """The dQ mode a backward call uses when the caller names none: DQ_SPILL (dQ from the dS
+    tiles the kv-major kernel writes: one GEMM per pair, the faster mode) when its workspace --
+    8 KiB per possible pair, B*H*nb*K tiles for q2k rows of width K (nb when the library derives
+    them) plus the slot tables -- takes at most half of the device's free memory and the spill's
+    size limits hold (at most 65535 kv blocks, nb*K below 2^31); DQ_RECOMPUTE otherwise. At
+    32768 tokens with top-k 128 the spill workspace is 4 GiB; at 524288 tokens with top-k 2048
+    it would be 1 TiB, so that size recomputes."""
+    nb = seqlen // BLOCK
+    kq = q2k_stride if q2k_stride > 0 else nb
+    if nb > 65535 or nb * kq >= 1 << 31:
+        return DQ_RECOMPUTE
+    need = bwd_workspace_bytes(batch, heads, seqlen, q2k_stride, DQ_SPILL, chunk_blocks)
+    free = torch.cuda.mem_get_info(device)[0]
+    return DQ_SPILL if need <= free // 2 else DQ_RECOMPUTE
+
+
 def bwd_order(k2q_num: torch.Tensor, bin_width: int = ORDER_BIN_WIDTH,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Length-binned work order ``[B*H*nb]`` int32 of item ids (b*H + h)*nb + kv."""
@@ -277,8 +335,8 @@ def bwd_order(k2q_num: torch.Tensor, bin_width: int = ORDER_BIN_WIDTH,
     if num.dim() != 3:
         raise RuntimeError("k2q_num must be [B, H, nb]")
     B, H, nb = num.shape
-    order = out if out is not None else torch.empty(B * H * nb, dtype=torch.int32,
-                                                    device=num.device)
+    order = (_out(out, "order out", (B * H * nb,), torch.int32, num.device) if out is not None
+             else torch.empty(B * H * nb, dtype=torch.int32, device=num.device))
     _check(lib().vsa_bwd_order(num.data_ptr(), B, H, nb, bin_width, order.data_ptr(),
                                _stream(num.device)), "vsa_bwd_order")
     return order
@@ -301,20 +359,24 @@ class BwdPlan:
 
     def __init__(self, grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                  sm_scale=None, order=None, workspace=None, out=None, q2k_idx=None,
-                 q2k_num=None, dq_mode=DQ_RECOMPUTE, chunk_blocks=0):
+                 q2k_num=None, dq_mode=None, chunk_blocks=0):
         _need_gpu(q, "q")
         if q.dim() != 4:
             raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
         B, H, S, D = q.shape
+        dev = q.device
         for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (grad_o, "grad_o")):
             _act(t, n, (B, H, S, D))
-        _need_gpu(lse, "lse")
+            _same_device(t, n, dev)
+        _same_device(lse, "lse", dev)
         if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * S:
             raise RuntimeError(f"lse must be contiguous float32 holding [B, H, S] = {B * H * S} "
                                f"values, got {lse.dtype} with {lse.numel()}")
         idx = _idx(k2q_idx, "k2q_idx")
         num = _idx(k2q_num, "k2q_num")
         vbs = _idx(variable_block_sizes, "variable_block_sizes")
+        for t, n in ((idx, "k2q_idx"), (num, "k2q_num"), (vbs, "variable_block_sizes")):
+            _same_device(t, n, dev)
         nb = vbs.numel()
         if S != BLOCK * nb:
             raise RuntimeError(f"seqlen {S} must equal num_kv_blocks ({nb}) * {BLOCK}")
@@ -325,6 +387,7 @@ class BwdPlan:
             raise RuntimeError(f"k2q_num must hold {B * H * nb} counts, got {num.numel()}")
         if order is not None:
             order = _idx(order, "order")
+            _same_device(order, "order", dev)
             if order.numel() != B * H * nb:
                 raise RuntimeError(f"order must hold {B * H * nb} item ids")
         qidx = qnum = None
@@ -333,16 +396,23 @@ class BwdPlan:
         if q2k_idx is not None:
             qidx = _idx(q2k_idx, "q2k_idx")
             qnum = _idx(q2k_num, "q2k_num")
+            _same_device(qidx, "q2k_idx", dev)
+            _same_device(qnum, "q2k_num", dev)
             if qidx.numel() != B * H * nb * qidx.shape[-1] or qnum.numel() != B * H * nb:
                 raise RuntimeError(f"q2k metadata must be [{B},{H},{nb},stride] and [{B},{H},{nb}]")
         if sm_scale is None:
             sm_scale = 1.0 / math.sqrt(D)
+        kq = qidx.shape[-1] if qidx is not None else 0
+        if dq_mode is None:
+            dq_mode = default_dq_mode(B, H, S, kq, chunk_blocks, dev)
         if out is None:
             out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-        kq = qidx.shape[-1] if qidx is not None else 0
-        if workspace is None:
-            workspace = torch.empty(bwd_workspace_bytes(B, H, S, kq, dq_mode, chunk_blocks),
-                                    dtype=torch.uint8, device=q.device)
+        else:
+            out = tuple(_out(t, f"{n} out", (B, H, S, D), torch.bfloat16, dev)
+                        for t, n in zip(out, ("dq", "dk", "dv")))
+        workspace = _workspace(workspace, bwd_workspace_bytes(B, H, S, kq, dq_mode, chunk_blocks),
+                               dev, "backward")
+        self.dq_mode = dq_mode
         self.dq, self.dk, self.dv = out
         self.workspace = workspace
         self.device = q.device
@@ -381,16 +451,6 @@ class BwdPlan:
         n = a.batch * a.heads * a.seqlen * 2
         return self.region(WS_LSE_DELTA, n, torch.float32).view(a.batch, a.heads, nb, 2, BLOCK)
 
-    def scale_log2(self) -> float:
-        """fp32(sm_scale * log2 e), the factor the records divide lse by."""
-        return float(torch.tensor(self.args.sm_scale, dtype=torch.float32)
-                     * torch.tensor(1.4426950408889634, dtype=torch.float32))
-
-    def delta(self) -> torch.Tensor:
-        """Delta as fp32 [B, H, S], read out of the records (valid after PREPROCESS)."""
-        a = self.args
-        return -self.lse_delta()[:, :, :, 1, :].reshape(a.batch, a.heads, a.seqlen)
-
 
 def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                       o: torch.Tensor, lse: torch.Tensor, k2q_idx: torch.Tensor,
@@ -399,10 +459,11 @@ def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
                       workspace: Optional[torch.Tensor] = None,
                       out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                       q2k_idx: Optional[torch.Tensor] = None,
-                      q2k_num: Optional[torch.Tensor] = None, dq_mode: int = DQ_RECOMPUTE,
+                      q2k_num: Optional[torch.Tensor] = None, dq_mode: Optional[int] = None,
                       chunk_blocks: int = 0):
     """Backward from k2q metadata (``[B, H, nb, max_q_blocks]`` or ``[B*H*nb, max_q_blocks]``
-    plus ``[B, H, nb]`` counts). Returns ``(dq, dk, dv)`` bf16."""
+    plus ``[B, H, nb]`` counts). Returns ``(dq, dk, dv)`` bf16. ``dq_mode`` None picks
+    ``default_dq_mode`` (the dS spill when its workspace fits)."""
     return BwdPlan(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                    sm_scale=sm_scale, order=order, workspace=workspace, out=out,
                    q2k_idx=q2k_idx, q2k_num=q2k_num, dq_mode=dq_mode,
@@ -410,11 +471,13 @@ def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
 
 
 def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
-             sm_scale: Optional[float] = None, dq_mode: int = DQ_RECOMPUTE,
+             sm_scale: Optional[float] = None, dq_mode: Optional[int] = None,
              chunk_blocks: int = 0):
     """Backward from the forward's q2k metadata: inverts to k2q on the GPU, then runs the
     backward with both lists (the q-major dQ kernel walks q2k, the kv-major kernel k2q). The q2k
-    rows must not repeat a kv block. Returns ``(dq, dk, dv)``."""
+    rows must not repeat a kv block. ``dq_mode`` None picks ``default_dq_mode``: with the q2k
+    rows given, the dS spill needs 8 KiB per (q block, q2k slot), 4 GiB at 32768 tokens with
+    top-k 128. Returns ``(dq, dk, dv)``."""
     B, H = q.shape[0], q.shape[1]
     idx = _idx(q2k_idx, "q2k_idx")
     num = _idx(q2k_num, "q2k_num")

@@ -139,7 +139,7 @@ bwd_dq_kernel(BwdParams p) {
 
   // A kv block with padded rows (vbs < 64): once its tiles have landed, zero those K and V rows
   // in LDS (they may hold anything), then meet at a barrier before anyone reads them. Rare: a
-  // uniform branch taken only for ragged blocks.
+  // uniform branch taken only for ragged blocks. Returns the block's vbs (its step masks dS^T).
   auto zero_padding = [&](int t, int st) __attribute__((always_inline)) {
     const int vb = ld_const(p.vbs, kvblock(t));
     if (vb < BLOCK) {
@@ -150,15 +150,18 @@ bwd_dq_kernel(BwdParams p) {
       }
       barrier_lds();
     }
+    return vb;
   };
 
   if (n > 0) {
     f32x16 s0, p0, s1, p1;
     bf16x8 ka0[8], va0[8], ka1[8], va1[8];
+    // vbs of the kv block in each ring stage (set when its padding is zeroed, two steps ahead)
+    int vbs0 = BLOCK, vbs1 = BLOCK, vbs2 = BLOCK, vbs3 = BLOCK;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stages 0..2 landed (own DMAs)
     barrier_lds();
-    zero_padding(0, 0);
-    if (n > 1) zero_padding(1, 1);
+    vbs0 = zero_padding(0, 0);
+    if (n > 1) vbs1 = zero_padding(1, 1);
     load_rows(0, ka0, va0);
     s0 = f32x16{};
     p0 = f32x16{};
@@ -173,12 +176,12 @@ bwd_dq_kernel(BwdParams p) {
     // S^T/dP^T of t are in (sc, pc) and the row operands of t+1 in (ka, va). The last steps use
     // stale (in-bounds, quiescent) stages for throwaway work, keeping the body branch-free.
     auto step = [&](int t, int st, int st2, int st3, f32x16& sc, f32x16& pc, f32x16& sn,
-                    f32x16& pn, bf16x8* ka, bf16x8* va, bf16x8* kn, bf16x8* vn)
-                    __attribute__((always_inline)) {
+                    f32x16& pn, bf16x8* ka, bf16x8* va, bf16x8* kn, bf16x8* vn, int vb_t,
+                    int& vb_ahead) __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stage t+2 landed (own DMAs)
       barrier_lds();  // ... everyone's; everyone is done with stage st3 (kv block t-1)
       if (t + 3 < n) issue(t + 3, st3);
-      if (t + 2 < n) zero_padding(t + 2, st2);  // before anyone reads kv block t+2
+      if (t + 2 < n) vb_ahead = zero_padding(t + 2, st2);  // before anyone reads kv block t+2
       VSA_LDS char* kt = kr + st * STAGE_BYTES;
 
       // ---- phase B: S^T/dP^T of kv block t+1; dS^T of kv block t; K^T reads of t ----
@@ -202,13 +205,21 @@ bwd_dq_kernel(BwdParams p) {
         sn = mfma32(ka[s], qf[s], sn);
         pn = mfma32(va[s], df[s], pn);
       }
-      // dS^T of kv block t. Padded kv rows need no mask here: their K and V rows are zero in
-      // LDS, so dP^T is 0, dS^T is finite, and their K^T rows add nothing to dQ.
+      // dS^T of kv block t. A padded kv row has a zero K row, so its score is 0 and its P is
+      // exp2(-lse_q): infinite once lse_q <= -128 (every valid score below about -88), and inf
+      // times the zero K^T row would put NaN into dQ. So a ragged block (a uniform branch, rare)
+      // sets the dS^T of its padded rows to exactly 0. Element e is kv row
+      // 32*wk + 8*(e/4) + 4*g + e%4.
       float dsv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pe = __builtin_amdgcn_exp2f(sc[e] * scale_log2 - lse_q);
         dsv[e] = pe * (pc[e] + ndelta_q);
+      }
+      if (vb_t < BLOCK) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          dsv[e] = 32 * wk + 8 * (e >> 2) + 4 * g + (e & 3) < vb_t ? dsv[e] : 0.0f;
       }
       bf16x8 b[2];
 #pragma unroll
@@ -237,10 +248,10 @@ bwd_dq_kernel(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     };
     for (int t = 0; t < n; t += 4) {
-      step(t, 0, 2, 3, s0, p0, s1, p1, ka1, va1, ka0, va0);
-      if (t + 1 < n) step(t + 1, 1, 3, 0, s1, p1, s0, p0, ka0, va0, ka1, va1);
-      if (t + 2 < n) step(t + 2, 2, 0, 1, s0, p0, s1, p1, ka1, va1, ka0, va0);
-      if (t + 3 < n) step(t + 3, 3, 1, 2, s1, p1, s0, p0, ka0, va0, ka1, va1);
+      step(t, 0, 2, 3, s0, p0, s1, p1, ka1, va1, ka0, va0, vbs0, vbs2);
+      if (t + 1 < n) step(t + 1, 1, 3, 0, s1, p1, s0, p0, ka0, va0, ka1, va1, vbs1, vbs3);
+      if (t + 2 < n) step(t + 2, 2, 0, 1, s0, p0, s1, p1, ka1, va1, ka0, va0, vbs2, vbs0);
+      if (t + 3 < n) step(t + 3, 3, 1, 2, s1, p1, s0, p0, ka0, va0, ka1, va1, vbs3, vbs1);
     }
   }
 

@@ -304,14 +304,15 @@ def _bwd_small(c, label, mode=V.DQ_RECOMPUTE):
     for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
         assert got.dtype == torch.bfloat16
         check_close(name, got, ref)
-    # Delta from the preprocess, on the bf16 o it was given
+    # Delta from the preprocess (the records hold -Delta), on the bf16 o it was given
     rdelta = O.delta(o.cpu(), c.do)
-    gd = plan.delta().cpu().double().numpy()
+    gd = -plan.lse_delta()[:, :, :, 1, :].reshape(c.B, c.H, c.S).cpu().double().numpy()
     assert np.abs(gd - rdelta).max() <= 1e-5 * max(1.0, np.abs(rdelta).max())
-    # the records also carry -lse / scale_log2, divided in IEEE fp32 (torch's division rounds
-    # the same way)
+    # the records also carry -lse / scale_log2 with scale_log2 = fp32(sm_scale * log2 e), divided
+    # in IEEE fp32 (torch's division rounds the same way)
     glse = plan.lse_delta()[:, :, :, 0, :].reshape(c.B, c.H, c.S)
-    c2 = torch.tensor(plan.scale_log2(), dtype=torch.float32)
+    c2 = (torch.tensor(c.sm_scale, dtype=torch.float32)
+          * torch.tensor(1.4426950408889634, dtype=torch.float32))
     assert torch.equal(glse.cpu(), -(lse.cpu() / c2))
     return dq, dk, dv, rdq, rdk, rdv
 
@@ -397,6 +398,44 @@ def test_rows_without_valid_keys(mode):
         assert np.all(np.isfinite(g))
         assert np.all(g[ref == 0] == 0)
     assert torch.all(dq[0, 0, 128:192] == 0) and torch.all(dq[0, 1, 320:384] == 0)
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_backward_very_negative_lse(mode):
+    """Every valid score below -88 (lse < -128 in base 2) with ragged kv blocks: a padded kv row
+    (zero K row, score 0) then has P = exp2(-lse) = inf in fp32, and nothing of it may reach an
+    output (inf times a zero K row, or times dP - Delta = 0, is NaN). Scores that negative come
+    from a key direction u shared by all keys that q opposes (q = -14 u + noise). With V = 0
+    the gradient is exact and simple: o = 0, so Delta = 0 and dP = 0, every dS is 0 and dq, dk
+    are exactly zero, while dv = P^T dO is compared with the oracle."""
+    c = workloads.make_case(1, 2, 6, 3, seed=41, vbs=[64, 40, 64, 17, 64, 64], name="neg_lse")
+    g = torch.Generator().manual_seed(5)
+    u = torch.randn(c.H, 1, 128, generator=g)
+    k = u + torch.randn(c.H, c.S, 128, generator=g)
+    q = -14.0 * u + torch.randn(c.H, c.S, 128, generator=g)
+    c = dataclasses.replace(c, q=q[None].to(torch.bfloat16).contiguous(),
+                            k=k[None].to(torch.bfloat16).contiguous(),
+                            v=torch.zeros_like(c.v))
+    _, rl = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    assert rl.max() < -128
+    say(f"[backward] lse below -128 (max {rl.max():.1f}), V = 0, dq mode {mode}")
+    d = to_dev(c)
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+    assert np.abs(lse.cpu().double().numpy() - rl).max() <= LSE_ABS_TOL
+    ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
+    k2q_idx, k2q_num = torch.from_numpy(ridx).to(DEV), torch.from_numpy(rnum).to(DEV)
+    for give in (False, True):
+        extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"]) if give else {}
+        dq, dk, dv = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num,
+                               d["vbs"], out=(nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"])),
+                               dq_mode=MODES[mode], **extra).run()
+        torch.cuda.synchronize()
+        assert torch.all(dq == 0) and torch.all(dk == 0)
+        _, _, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+        check_close("dv", dv, rdv)
+        assert np.all(dv.float().cpu().numpy()[rdv == 0] == 0)
 
 
 @pytest.mark.parametrize("mode", sorted(MODES))
@@ -562,16 +601,39 @@ def _end_to_end(c, mode=V.DQ_RECOMPUTE, give_q2k=False):
     return d, o, lse, (k2q_idx, k2q_num), plan, (dq, dk, dv)
 
 
-def _sampled_checks(c, o, lse, grads, qblocks, kvblocks):
+def _sampled_checks(c, o, lse, grads, qblocks, kvblocks, precision="float64"):
+    """o, lse and dq of the q blocks, dk and dv of the kv blocks, each against the oracle
+    computed for that block alone (a kv block sums the contributions of every q block that
+    selects it, each with its full softmax)."""
     dq, dk, dv = grads
-    _fwd_compare(c, None, o, lse, qblocks=qblocks)
-    sdq, sdkv = O.backward_sampled(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale,
-                                   qblocks=qblocks, kvblocks=kvblocks)
-    for (b, h, qb), ref in sdq.items():
-        check_close(f"dq[{b},{h},{qb}]", dq[b, h, qb * 64:(qb + 1) * 64], ref)
-    for (b, h, kb), (rk, rv) in sdkv.items():
-        check_close(f"dk[{b},{h},{kb}]", dk[b, h, kb * 64:(kb + 1) * 64], rk)
-        check_close(f"dv[{b},{h},{kb}]", dv[b, h, kb * 64:(kb + 1) * 64], rv)
+    if qblocks:
+        _fwd_compare(c, None, o, lse, qblocks=qblocks)
+        sdq, _ = O.backward_sampled(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs,
+                                    c.sm_scale, qblocks=qblocks, kvblocks=())
+        for (b, h, qb), ref in sdq.items():
+            check_close(f"dq[{b},{h},{qb}]", dq[b, h, qb * 64:(qb + 1) * 64], ref)
+    if kvblocks:
+        say(f"  oracle for {len(kvblocks)} kv blocks ({precision})")
+        sdkv = O.kvblock_backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale,
+                                  kvblocks, precision,
+                                  progress=lambda i, n: say(f"    q block {i} of {n}"))
+        for (b, h, kb), (rk, rv) in sorted(sdkv.items()):
+            check_close(f"dk[{b},{h},{kb}]", dk[b, h, kb * 64:(kb + 1) * 64], rk)
+            check_close(f"dv[{b},{h},{kb}]", dv[b, h, kb * 64:(kb + 1) * 64], rv)
+
+
+def _spread(c, n, seed):
+    """n (b, h, block) samples spread over the heads: the first and last block of the first
+    and last head, the rest drawn at random (seeded)."""
+    g = np.random.default_rng(seed)
+    heads = [(b, h) for b in range(c.B) for h in range(c.H)]
+    out = [(*heads[0], 0), (*heads[-1], c.nb - 1), (*heads[0], c.nb - 1), (*heads[-1], 0)]
+    while len(out) < n:
+        b, h = heads[len(out) % len(heads)]
+        blk = int(g.integers(1, c.nb - 1))
+        if (b, h, blk) not in out:
+            out.append((b, h, blk))
+    return out
 
 
 def _invariants(c, grads):
@@ -590,6 +652,7 @@ def _invariants(c, grads):
     assert ((dvs - dos).abs() <= 2e-3 * mass + 1e-6).all()
 
 
+@pytest.mark.timeout(900)
 def test_config3_32k_end_to_end_sampled():
     c = workloads.config(3)
     say("[end-to-end] config 3 (B=1 H=8 S=32768, 25%, dS spill, q2k given)")
@@ -599,10 +662,10 @@ def test_config3_32k_end_to_end_sampled():
     assert np.array_equal(plan.region(V.WS_KV_ORDER, n).cpu().numpy(),
                           O.work_order(k2q_num.cpu(), V.ORDER_BIN_WIDTH))
     _invariants(c, grads)
-    _sampled_checks(c, o, lse, grads, qblocks=[(0, 0, 0), (0, 3, 200), (0, 7, 511)],
-                    kvblocks=[(0, 0, 1), (0, 5, 300), (0, 7, 511)])
+    _sampled_checks(c, o, lse, grads, qblocks=_spread(c, 8, 31), kvblocks=_spread(c, 8, 37))
 
 
+@pytest.mark.timeout(900)
 def test_config4_65k_order_stability_sampled():
     c = workloads.config(4)
     say("[end-to-end] config 4 (B=1 H=8 S=65536, 12.5%, device work order)")
@@ -624,8 +687,7 @@ def test_config4_65k_order_stability_sampled():
     for x, y in zip(grads, again):
         assert torch.equal(x, y)
     dq, dk, dv = grads
-    _sampled_checks(c, o, lse, grads, qblocks=[(0, 1, 7), (0, 6, 1023)],
-                    kvblocks=[(0, 2, 0), (0, 7, 777)])
+    _sampled_checks(c, o, lse, grads, qblocks=_spread(c, 8, 41), kvblocks=_spread(c, 8, 43))
     del plan, again
     # the dS spill with the forward's q2k lists: the same dk, dv bits, dq on samples, and
     # run-to-run identical
@@ -639,7 +701,7 @@ def test_config4_65k_order_stability_sampled():
     torch.cuda.synchronize()
     for x, y in zip(g2, g3):
         assert torch.equal(x, y)
-    _sampled_checks(c, o, lse, g2, qblocks=[(0, 1, 7), (0, 6, 1023)], kvblocks=[])
+    _sampled_checks(c, o, lse, g2, qblocks=_spread(c, 8, 41), kvblocks=[])
 
 
 def _head(c, h):
@@ -650,14 +712,36 @@ def _head(c, h):
                                q2k_idx=c.q2k_idx[:, sl], q2k_num=c.q2k_num[:, sl])
 
 
-def test_config5_524k_end_to_end_sampled():
-    """524288 tokens, 8192 kv blocks, top-k 2048, inputs x0.5, last kv block 40 valid tokens.
-    o, lse and dq on sampled q blocks against the oracle (each one q block of one head); dk and dv
-    through the invariants and the exact zeros of the ragged block (one kv block's dk needs the
-    softmax of the ~2048 q blocks that select it, out of the oracle's reach here)."""
+@pytest.fixture(scope="module")
+def c5_run():
+    """524288 tokens, 8192 kv blocks, top-k 2048, inputs x0.5, last kv block 40 valid tokens:
+    GPU forward -> invert -> backward (default chunked dK/dV launches), run once for the tests
+    below."""
     c = workloads.config(5)
     say("[end-to-end] config 5 (B=1 H=8 S=524288, 25%, ragged last block)")
-    d, o, lse, _, plan, grads = _end_to_end(c)
+    d, o, lse, (k2q_idx, k2q_num), plan, grads = _end_to_end(c)
+    yield c, d, o, lse, (k2q_idx, k2q_num), plan, grads
+    del d, o, lse, k2q_idx, k2q_num, plan, grads
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_config5_524k_invert_bit_exact(c5_run):
+    """The 2 GiB k2q of the 524288-token workload, bit-exact against the oracle's inversion."""
+    c, _, _, _, (k2q_idx, k2q_num), _, _ = c5_run
+    say("  k2q vs oracle")
+    ridx, rnum = O.invert_indices(c.q2k_idx, c.q2k_num, c.nb)
+    assert np.array_equal(k2q_num.cpu().numpy(), rnum)
+    for h in range(c.H):  # one head (256 MiB) at a time
+        assert np.array_equal(k2q_idx[:, h].cpu().numpy(), ridx[:, h]), h
+
+
+@pytest.mark.timeout(900)
+def test_config5_524k_end_to_end_sampled(c5_run):
+    """o, lse and dq on sampled q blocks against the oracle (each one q block of one head);
+    the invariants and the exact zeros of the ragged block; dk and dv of the default chunked
+    dK/dV launches against one launch, within the fp32 reordering bound."""
+    c, d, o, lse, (k2q_idx, k2q_num), plan, grads = c5_run
     dq, dk, dv = grads
     _invariants(c, grads)
     last = (c.nb - 1) * 64
@@ -677,3 +761,86 @@ def test_config5_524k_end_to_end_sampled():
     ms = ev[0].elapsed_time(ev[1])
     say(f"  backward chain {ms:.1f} ms, {c.pairs * 5 * 2 * 64 * 64 * 128 / ms / 1e9:.1f} TFLOPS "
         f"on selected blocks")
+    # the same backward as one launch per kernel: dk, dv equal up to the fp32 summation order of
+    # the chunk partial sums, dq bitwise (its kernel does not run in chunks by default)
+    say("  one-launch dK/dV for comparison")
+    one = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                    dq_mode=V.DQ_RECOMPUTE, chunk_blocks=-1).run()
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], dq)
+    for name, g1, g in (("dk", one[1], dk), ("dv", one[2], dv)):
+        diff = (g.float() - g1.float()).abs()
+        say(f"  {name}: chunked vs one launch max|diff| {diff.max().item():.3e}, "
+            f"mean {diff.mean().item():.3e}, mean|one| {g1.float().abs().mean().item():.3e}")
+        assert diff.max().item() <= 1e-2 * g1.float().abs().max().item()
+        assert diff.mean().item() <= 1e-3 * g1.float().abs().mean().item()
+    del one
+
+
+@pytest.mark.timeout(900)
+def test_config5_524k_kv_blocks_vs_oracle(c5_run):
+    """dk and dv of the default chunked dK/dV path at full size against the oracle: the ragged
+    last kv block (40 valid tokens) and an interior kv block of one head. Each kv block sums the
+    contributions of the ~2048 q blocks that select it, each with its softmax over 131072 keys:
+    the oracle runs those full-key-set products in float32 (every product with the sampled kv
+    blocks in float64), a few minutes of CPU."""
+    c, _, _, _, _, _, grads = c5_run
+    dq, dk, dv = grads
+    h = 5
+    ch = _head(c, h)
+    sub = (dq[:, h:h + 1], dk[:, h:h + 1], dv[:, h:h + 1])
+    say(f"  kv blocks {c.nb - 1} (ragged) and 2900 of head {h}")
+    _sampled_checks(ch, None, None, sub, qblocks=[], kvblocks=[(0, 0, c.nb - 1), (0, 0, 2900)],
+                    precision="float32")
+
+
+def test_binding_rejects_bad_outputs_and_workspaces():
+    """Caller-supplied outputs and workspaces go to the kernels as raw pointers, so the binding
+    refuses any of the wrong dtype, shape, device or layout before anything is launched."""
+    c = workloads.config(1)
+    d = to_dev(c)
+    say("[binding] bad outputs / workspaces")
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
+    torch.cuda.synchronize()
+    fwd_bad = [
+        (torch.empty_like(d["q"], dtype=torch.float32), lse),               # o dtype
+        (d["q"].new_empty(c.B, c.H, c.S, 64), lse),                          # o shape
+        (torch.empty_like(d["q"]).transpose(2, 3).contiguous().transpose(2, 3), lse),  # layout
+        (torch.empty_like(c.q), lse),                                        # o on the host
+        (torch.empty_like(d["q"]), lse.to(torch.float64)),                   # lse dtype
+        (torch.empty_like(d["q"]), lse[..., :-1]),                           # lse shape
+    ]
+    for out in fwd_bad:
+        with pytest.raises(RuntimeError):
+            V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"], out=out)
+    with pytest.raises(RuntimeError):  # a workspace on the host
+        V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"],
+                  kv_chunk_blocks=1, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(RuntimeError):  # a workspace too small
+        V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"],
+                  kv_chunk_blocks=1, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    for out in ((k2q_idx.to(torch.int64), k2q_num), (k2q_idx[..., :-1], k2q_num),
+                (k2q_idx, k2q_num.cpu())):
+        with pytest.raises(RuntimeError):
+            V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb, out=out)
+    with pytest.raises(RuntimeError):
+        V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb,
+                         workspace=torch.empty(64, dtype=torch.float32, device=DEV))
+    args = (d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"])
+    good = (torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]))
+    for i, bad in enumerate((good[0].float(), good[1][:, :, :-64], torch.empty_like(c.v))):
+        out = list(good)
+        out[i] = bad
+        with pytest.raises(RuntimeError):
+            V.BwdPlan(*args, out=tuple(out), dq_mode=V.DQ_SPILL)
+    for ws in (torch.empty(1 << 20, dtype=torch.uint8),
+               torch.empty(1 << 20, dtype=torch.int32, device=DEV),
+               torch.empty(8, dtype=torch.uint8, device=DEV)):
+        with pytest.raises(RuntimeError):
+            V.BwdPlan(*args, workspace=ws, dq_mode=V.DQ_SPILL)
+    # the same call with valid buffers runs, and the default dq mode is the dS spill here
+    plan = V.BwdPlan(*args, out=good)
+    assert plan.dq_mode == V.DQ_SPILL
+    plan.run()
+    torch.cuda.synchronize()
