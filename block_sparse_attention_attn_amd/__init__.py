@@ -29,7 +29,7 @@ __all__ = [
     "CHUNK_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
-    "DQ_RECOMPUTE", "DQ_SPILL", "default_dq_mode",
+    "DQ_RECOMPUTE", "DQ_SPILL", "default_dq_mode", "backward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 BLOCK = 64
@@ -95,7 +95,9 @@ _SIGNATURES = {
     "vsa_bwd_stage": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), ctypes.c_int, _p]),
     "vsa_bwd_order": (ctypes.c_int, [_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      _p, _p]),
+    "vsa_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), _p]),
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20  # VSA_NOALLOC_SCRATCH_BYTES
 
 
 def library_path() -> str:
@@ -490,3 +492,43 @@ def backward(grad_o, q, k, v, o, lse, q2k_idx, q2k_num, variable_block_sizes,
     return backward_from_k2q(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes,
                              sm_scale=sm_scale, q2k_idx=idx, q2k_num=num, dq_mode=dq_mode,
                              chunk_blocks=chunk_blocks)
+
+
+def backward_noalloc(grad_o, q, k, v, o, lse, k2q_idx, k2q_num, variable_block_sizes, out,
+                     sm_scale: Optional[float] = None, q2k_idx: Optional[torch.Tensor] = None,
+                     q2k_num: Optional[torch.Tensor] = None, dq_mode: int = DQ_RECOMPUTE,
+                     chunk_blocks: int = 0):
+    """``vsa_bwd_noalloc``: the backward with its workspace in the library's static scratch
+    (NOALLOC_SCRATCH_BYTES per GPU), for callers that cannot allocate. ``out`` = (dq, dk, dv) must
+    be given; the metadata must already be contiguous int32 on the device (nothing is converted
+    or allocated here). Calls on one GPU share the scratch, so calls that overlap there race.
+    Raises if the call's workspace would not fit the scratch."""
+    B, H, S, D = q.shape
+    dev = q.device
+    for t, n in ((k2q_idx, "k2q_idx"), (k2q_num, "k2q_num"), (variable_block_sizes, "vbs"),
+                 (q2k_idx, "q2k_idx"), (q2k_num, "q2k_num")):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise RuntimeError(f"{n} must be contiguous int32 for backward_noalloc")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (grad_o, "grad_o")):
+        _act(t, n, (B, H, S, D))
+        _same_device(t, n, dev)
+    _same_device(lse, "lse", dev)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * S:
+        raise RuntimeError("lse must be contiguous float32 holding [B, H, S] values")
+    dq, dk, dv = (_out(t, f"{n} out", (B, H, S, D), torch.bfloat16, dev)
+                  for t, n in zip(out, ("dq", "dk", "dv")))
+    for t, n in ((k2q_idx, "k2q_idx"), (k2q_num, "k2q_num"), (variable_block_sizes, "vbs")):
+        _same_device(t, n, dev)
+    nb = variable_block_sizes.numel()
+    if (q2k_idx is None) != (q2k_num is None):
+        raise RuntimeError("give both q2k_idx and q2k_num, or neither")
+    kq = q2k_idx.shape[-1] if q2k_idx is not None else 0
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    a = _BwdArgs(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), grad_o.data_ptr(),
+                 lse.data_ptr(), k2q_idx.data_ptr(), k2q_num.data_ptr(), _ptr(q2k_idx),
+                 _ptr(q2k_num), variable_block_sizes.data_ptr(), None, dq.data_ptr(),
+                 dk.data_ptr(), dv.data_ptr(), None, 0, B, H, S, D, nb, k2q_idx.shape[-1], kq,
+                 float(sm_scale), int(dq_mode), int(chunk_blocks))
+    _check(lib().vsa_bwd_noalloc(ctypes.byref(a), _stream(dev)), "vsa_bwd_noalloc")
+    return dq, dk, dv

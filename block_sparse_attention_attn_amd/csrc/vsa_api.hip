@@ -13,6 +13,7 @@
 // keeps the items running together on one XCD in step, for L2 reuse of Q/dO).
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/vsa.h"
@@ -524,6 +525,70 @@ int vsa_bwd(const vsa_bwd_args* a, void* stream) {
     if (r != VSA_OK) return r;
   }
   return VSA_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// backward without a caller workspace
+// ------------------------------------------------------------------------------------------------
+
+// The workspace of vsa_bwd_noalloc: device memory of this code object, one copy per GPU that
+// loads the library, held until the process ends. Host code never uses this name as an address
+// (on the host it is only a stand-in); the device address comes from hipGetSymbolAddress, per
+// device, below.
+static __device__ __align__(256) char scratch[VSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, resolved on the first call there.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VSA_ELAUNCH, std::string("vsa_bwd_noalloc: hipGetDevice: ") +
+                                                    hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VSA_EUNSUPPORTED, "vsa_bwd_noalloc: device id " + std::to_string(dev) +
+                                      " above the supported " + std::to_string(kMaxDevices - 1));
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(VSA_ELAUNCH, std::string("vsa_bwd_noalloc: hipGetSymbolAddress: ") +
+                                   hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vsa_bwd_noalloc(const vsa_bwd_args* a, void* stream) {
+  if (!a) return fail(VSA_EINVAL, "vsa_bwd_noalloc: null argument struct");
+  const size_t need = vsa_bwd_workspace_bytes(a->batch, a->heads, a->seqlen,
+                                              a->q2k_idx ? a->q2k_stride : 0, a->dq_mode,
+                                              a->chunk_blocks);
+  if (need > (size_t)VSA_NOALLOC_SCRATCH_BYTES)
+    return fail(VSA_EUNSUPPORTED,
+                "vsa_bwd_noalloc: this call needs " + std::to_string(need) +
+                    " bytes of workspace, above the static scratch of " +
+                    std::to_string((size_t)VSA_NOALLOC_SCRATCH_BYTES) +
+                    " bytes; use vsa_bwd with a workspace");
+  void* ws = nullptr;
+  const int r = scratch_of_current_device(&ws);
+  if (r != VSA_OK) return r;
+  vsa_bwd_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = VSA_NOALLOC_SCRATCH_BYTES;
+  return vsa_bwd(&b, stream);
 }
 
 }  // extern "C"

@@ -56,6 +56,8 @@ def test_binding_constants_match_the_header():
                         ("VSA_CHUNK_BLOCKS", V.CHUNK_BLOCKS)):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == value, name
+    m = re.search(r"#define\s+VSA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == V.NOALLOC_SCRATCH_BYTES
 
 
 def test_status_strings():
