@@ -22,8 +22,11 @@ bracketed by HIP events on the stream it runs on (torch's current stream, which 
   cpu_baseline= the float64 CPU oracle's backward on a bounded sample of the same workload.
 
 The headline workload is B=1 H=8 S=32768 D=128, 25 % density (default); --workload 4 selects
-S=65536 at 12.5 % density. The line also carries the other headline workload's backward TFLOPS.
---workload 5 times the 524288-token case (recompute dQ mode; use few steps, e.g. --steps 3
+S=65536 at 12.5 % density. The line also carries, under `secondary`, the other headline workload
+and the 524288-token workload (recompute dQ mode, 2 steps after 1 warm-up; --no-524k skips it).
+`api_backward_ms` times the public V.backward() on its defaults (inverting q2k, default dQ mode,
+outputs and workspace from torch's caching allocator), i.e. invert + backward chain.
+--workload 5 times the 524288-token case alone (recompute dQ mode; use few steps, e.g. --steps 3
 --warmup 1: a step is a few seconds).
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -87,7 +90,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_workload(n, steps, warmup, dq_mode):
+def run_workload(n, steps, warmup, dq_mode, api_steps=0):
     import torch
 
     import block_sparse_attention_attn_amd as V
@@ -164,6 +167,22 @@ def run_workload(n, steps, warmup, dq_mode):
     res["fwd_tflops"] = pairs * 2 * GEMM_FLOP / (res["fwd_ms"] * 1e-3) / 1e12
     del plan
     torch.cuda.empty_cache()
+    if api_steps:
+        # the public entry a caller uses, on its defaults: inverts q2k, picks the dQ mode
+        # (default_dq_mode) and allocates outputs and workspace through torch's caching allocator
+        for _ in range(2):
+            V.backward(do, q, k, v, o, lse, idx, num, vbs)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(api_steps):
+            V.backward(do, q, k, v, o, lse, idx, num, vbs)
+        a1.record()
+        torch.cuda.synchronize()
+        res["api_backward_ms"] = a0.elapsed_time(a1) / api_steps
+        res["api_dq_mode"] = "spill" if V.default_dq_mode(c.B, c.H, c.S, idx.shape[-1]) == V.DQ_SPILL \
+            else "recompute"
+        torch.cuda.empty_cache()
     return res, c
 
 
@@ -206,6 +225,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=(3, 4, 5))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-524k", action="store_true",
+                    help="skip the 524288-token secondary leg (about a minute, mostly input "
+                         "generation)")
     ap.add_argument("--dq-mode", choices=("spill", "recompute"), default="spill",
                     help="dQ from dS tiles the dK/dV kernel spills to the workspace (8 KiB per "
                          "pair), or recomputed from Q, K, V, dO")
@@ -236,18 +258,28 @@ def main():
         log("[bench] workload 5: the dS tiles would need 1 TiB of workspace; dq is recomputed")
         args.dq_mode = "recompute"
     mode = V.DQ_SPILL if args.dq_mode == "spill" else V.DQ_RECOMPUTE
-    res, case = run_workload(args.workload, args.steps, args.warmup, mode)
+    res, case = run_workload(args.workload, args.steps, args.warmup, mode,
+                             api_steps=10 if args.workload != 5 else 0)
     log(f"[bench] {json.dumps(res)}")
     secondary = None
     if not args.no_secondary and args.workload != 5:
-        other = 4 if args.workload == 3 else 3
-        log(f"[bench] secondary workload {other}")
-        r2, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2), mode)
-        log(f"[bench] {json.dumps(r2)}")
-        secondary = dict(workload=WORKLOAD_TEXT[other], bwd_tflops=round(r2["bwd_tflops"], 2),
-                         bwd_ms=round(r2["bwd_ms"], 4), dkdv_ms=round(r2["dkdv_ms"], 4),
-                         dq_ms=round(r2["dq_ms"], 4),
-                         frac_of_peak=round(r2["bwd_tflops"] / PEAK_BF16_TFLOPS, 4))
+        secondary = []
+        others = [4 if args.workload == 3 else 3]
+        if not args.no_524k:
+            others.append(5)
+        for other in others:
+            log(f"[bench] secondary workload {other}")
+            if other == 5:  # a step takes about 1.6 s; the dS tiles would need 1 TiB
+                r2, _ = run_workload(5, 2, 1, V.DQ_RECOMPUTE)
+            else:
+                r2, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2), mode)
+            log(f"[bench] {json.dumps(r2)}")
+            secondary.append(dict(
+                workload=WORKLOAD_TEXT[other], steps=2 if other == 5 else max(5, args.steps // 2),
+                bwd_tflops=round(r2["bwd_tflops"], 2), bwd_ms=round(r2["bwd_ms"], 4),
+                fwd_ms=round(r2["fwd_ms"], 4), dkdv_ms=round(r2["dkdv_ms"], 4),
+                dq_ms=round(r2["dq_ms"], 4),
+                frac_of_peak=round(r2["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)))
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
@@ -281,6 +313,8 @@ def main():
         "frac_of_peak": round(res["bwd_tflops"] / PEAK_BF16_TFLOPS, 4),
         "breakdown_ms": {k: round(res[k], 4) for k in ("invert_ms", "fwd_ms", "pre_ms", "index_ms",
                                                       "dkdv_ms", "dq_ms", "bwd_ms")},
+        "api_backward_ms": round(res["api_backward_ms"], 4) if "api_backward_ms" in res else None,
+        "api_dq_mode": res.get("api_dq_mode"),
         "roofline": {
             "kernel": "bwd_dkdv_kernel",
             "bound": "mfma",

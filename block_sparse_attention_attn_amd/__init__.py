@@ -317,17 +317,30 @@ def default_dq_mode(batch: int, heads: int, seqlen: int, q2k_stride: int = 0,
     """The dQ mode a backward call uses when the caller names none: DQ_SPILL (dQ from the dS
     tiles the kv-major kernel writes: one GEMM per pair, the faster mode) when its workspace --
     8 KiB per possible pair, B*H*nb*K tiles for q2k rows of width K (nb when the library derives
-    them) plus the slot tables -- takes at most half of the device's free memory and the spill's
-    size limits hold (at most 65535 kv blocks, nb*K below 2^31); DQ_RECOMPUTE otherwise. At
-    32768 tokens with top-k 128 the spill workspace is 4 GiB; at 524288 tokens with top-k 2048
-    it would be 1 TiB, so that size recomputes."""
+    them) plus the slot tables -- takes at most 1/8 of the device's memory and the spill's size
+    limits hold (at most 65535 kv blocks, nb*K below 2^31); DQ_RECOMPUTE otherwise. The choice
+    depends only on the shape and the device (not on the memory free at the time), so a given
+    call always runs the same kernels and gives the same bits. On MI355X (288 GB): 32768 tokens
+    with top-k 128 spill into 4 GiB, 65536 tokens into 8 GiB; 524288 tokens with top-k 2048 would
+    need 1 TiB and recompute."""
     nb = seqlen // BLOCK
     kq = q2k_stride if q2k_stride > 0 else nb
     if nb > 65535 or nb * kq >= 1 << 31:
         return DQ_RECOMPUTE
     need = bwd_workspace_bytes(batch, heads, seqlen, q2k_stride, DQ_SPILL, chunk_blocks)
-    free = torch.cuda.mem_get_info(device)[0]
-    return DQ_SPILL if need <= free // 2 else DQ_RECOMPUTE
+    total = _total_memory(device)
+    return DQ_SPILL if need <= total // 8 else DQ_RECOMPUTE
+
+
+_TOTAL_MEMORY = {}
+
+
+def _total_memory(device) -> int:
+    dev = torch.device(device if device is not None else "cuda")
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx not in _TOTAL_MEMORY:
+        _TOTAL_MEMORY[idx] = torch.cuda.get_device_properties(idx).total_memory
+    return _TOTAL_MEMORY[idx]
 
 
 def bwd_order(k2q_num: torch.Tensor, bin_width: int = ORDER_BIN_WIDTH,

@@ -39,7 +39,9 @@
 //   * dV and dK are accumulated per q half and the halves are summed through LDS once per item;
 //   * work ids map XCD-first: workgroup ids go round-robin over the 8 XCDs, so XCD x runs a
 //     contiguous slice of the (ordered) item list -- one head per XCD when B*H = 8 -- and that
-//     head's Q/dO traffic stays in one XCD's L2;
+//     head's Q/dO traffic stays in one XCD's L2; when the Q/dO of the heads running at once
+//     would overflow half of the shared memory-side cache, the slices run in rounds in which
+//     XCD pairs share a head (xcd_work_id), so fewer heads are live at a time;
 //   * long lists run in q-range chunks, one launch each: the items take the part of their list
 //     inside the chunk's q range and carry dK, dV between launches as fp32 partial sums, so the
 //     items on an XCD walk one window of q blocks at a time and keep sharing its L2.
@@ -89,7 +91,7 @@ bwd_dkdv_kernel(BwdParams p) {
   const int t16 = lane & 15;  // lane inside the group
 
   // XCD-first work id: blockIdx.x % 8 is the XCD the dispatcher sends the workgroup to.
-  const int wid = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);
+  const int wid = xcd_work_id(p.items_per_xcd, p.kv_rounds);
   if (wid >= p.total_items) return;
   const int item = p.kv_order ? ld_const(p.kv_order, wid) : wid;
   if (item < 0 || item >= p.total_items) return;  // a malformed order entry: skip, never fault

@@ -140,6 +140,22 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
       : "memory");
 }
 
+// Work id of the calling workgroup in an XCD-aware launch of 8 * items_per_xcd workgroups. The
+// dispatcher sends workgroup b to XCD b % 8, each XCD taking its workgroups in order, so XCD x
+// runs local indices li = b / 8 = 0, 1, ... . With one round XCD x runs the contiguous work ids
+// [x * items_per_xcd, (x + 1) * items_per_xcd): one slice of the (head-major) item list, so an
+// XCD's L2 sees few heads. With R rounds the item list is cut into 8R slices of C =
+// items_per_xcd / R ids and XCD x runs slice 8r + x in round r (8r + (x ^ 1) in odd rounds, so an
+// XCD pair alternates the first and second halves of a head): at any time the eight XCDs share
+// fewer heads, whose tiles then stay in the memory-side cache (MALL) that all XCDs share.
+__device__ __forceinline__ int xcd_work_id(int items_per_xcd, int rounds) {
+  const int x = blockIdx.x & 7, li = blockIdx.x >> 3;
+  if (rounds <= 1) return x * items_per_xcd + li;
+  const int c = items_per_xcd / rounds;
+  const int r = li / c, j = li - r * c;
+  return (8 * r + ((r & 1) ? (x ^ 1) : x)) * c + j;
+}
+
 // Index of the calling wave inside its workgroup, as a value the compiler knows to be uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

@@ -111,6 +111,8 @@ struct BwdParams {
   float* part = nullptr;
   int chunk = 0, nchunks = 0;
   int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
+  // rounds of the kv-major kernel's XCD mapping (xcd_work_id); items_per_xcd is a multiple
+  int kv_rounds = 1;
   float scale_log2, sm_scale;
 };
 void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
