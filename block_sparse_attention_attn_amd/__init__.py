@@ -244,7 +244,8 @@ def invert_indices(q2k_idx: torch.Tensor, q2k_num: torch.Tensor, num_kv_blocks: 
 
 
 def fwd_workspace_bytes(batch: int, heads: int, seqlen: int, kv_chunk_blocks: int = 0) -> int:
-    """Forward workspace bytes (0 when the forward runs as one launch)."""
+    """Forward workspace bytes: the fp16 copy of v (2 bytes per element) and, with kv-range chunks,
+    the chunk bounds and per-wave state."""
     return int(lib().vsa_fwd_workspace_bytes(batch, heads, seqlen, kv_chunk_blocks))
 
 
@@ -255,8 +256,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
             kv_chunk_blocks: int = 0, workspace: Optional[torch.Tensor] = None):
     """Block-sparse forward: returns ``(o bf16 [B,H,S,128], lse fp32 [B,H,S] M form)``.
     ``kv_chunk_blocks``: kv blocks per kv-range chunk (0: the library's choice, chunks of
-    FWD_CHUNK_KV_BLOCKS from CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch); the
-    workspace it needs is allocated here unless given."""
+    FWD_CHUNK_KV_BLOCKS from CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch). The
+    workspace (``fwd_workspace_bytes``: the fp16 copy of v, and the chunk state) is allocated
+    here unless given."""
     _need_gpu(q, "q")
     if q.dim() != 4:
         raise RuntimeError(f"q must be 4-D, got {q.dim()} dims")
@@ -286,8 +288,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
         o = _out(out[0], "o out", (B, H, S, D), torch.bfloat16, dev)
         lse = _out(out[1], "lse out", (B, H, S), torch.float32, dev)
     need = fwd_workspace_bytes(B, H, S, kv_chunk_blocks)
-    if need or workspace is not None:
-        workspace = _workspace(workspace, need, dev, "forward")
+    workspace = _workspace(workspace, need, dev, "forward")
     a = _FwdArgs(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), num.data_ptr(),
                  vbs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, S, D, nb, idx.shape[-1],
                  float(sm_scale), _ptr(workspace),

@@ -23,8 +23,13 @@
 //   * The running max is only raised when a block's max exceeds it by more than 8 (in log2
 //     units): the exponentials then stay below 2^8, O^T and the sum are rescaled rarely, and the
 //     final o = O / l and lse = max + log2(l) are unchanged in exact arithmetic.
-//   * P^T (bf16) is the B operand of O^T += V^T P^T straight from the D layout of S^T (the kv
-//     contraction index is permuted to match); V^T comes from ds_read_b64_tr_b16.
+//   * P^T is the B operand of O^T += V^T P^T straight from the D layout of S^T (the kv
+//     contraction index is permuted to match); V^T comes from ds_read_b64_tr_b16. That product
+//     runs in fp16 (v_mfma_f32_32x32x16_f16, the bf16 rate): P < 2^8 fits, and fp16's 11-bit
+//     significand rounds P 8x finer than bf16 would. V^T comes from an fp16 copy of V made by a
+//     pre-pass, each head scaled by a power of two 2^-e into [2^14, 2^15) at its largest |v|, so
+//     the copy is exact (bf16's 8 bits fit) for every |v| >= 2^-28 max; the epilogue multiplies
+//     o by 2^e exactly.
 //   * K and V tiles arrive by global_load_lds_dwordx4 into two-stage LDS rings, K two blocks and
 //     V one block ahead: the S^T MFMAs of block t+1 run under the softmax of block t.
 //   * The loop is unrolled by two so the ring stages are constants: each lane's LDS operand
@@ -125,7 +130,7 @@ fwd_kernel(FwdParams p) {
     dma_tile(p.k + head + tile_of(kb), toff, lds0 + st * TILE);
   };
   auto issue_v = [&](int kb, int st) __attribute__((always_inline)) {
-    dma_tile(p.v + head + tile_of(kb), toff, lds0 + (2 + st) * TILE);
+    dma_tile(p.v16 + head + tile_of(kb), toff, lds0 + (2 + st) * TILE);
   };
   const int kv_l = 32 * wk + l32;  // this lane's kv row of the A operand of S^T
   // LDS byte addresses of this lane's operand reads in stage 0 of the rings: the K rows (A operand
@@ -219,14 +224,14 @@ fwd_kernel(FwdParams p) {
     issue_k(e2, st);
     // V^T operands of O^T += V^T P^T: k-step c, slot j is kv 32wk + 16c + 8(j/4) + 4g + j%4 (the
     // D-layout order of S^T); d tile dt, lane's d = 32dt + l32
-    bf16x8 va[4][2];
+    f16x8 va[4][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint32_t o = st * TILE + c * 4096;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        va[dt][c] = join(lds_read_tr((const VSA_LDS void*)(uintptr_t)(va_at[dt][0] + o)),
-                         lds_read_tr((const VSA_LDS void*)(uintptr_t)(va_at[dt][1] + o)));
+        va[dt][c] = join_f16(lds_read_tr((const VSA_LDS void*)(uintptr_t)(va_at[dt][0] + o)),
+                             lds_read_tr((const VSA_LDS void*)(uintptr_t)(va_at[dt][1] + o)));
     }
     issue_v(e1, st ^ 1);
 
@@ -281,10 +286,10 @@ fwd_kernel(FwdParams p) {
     l_run += pair_sum32(rs);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const bf16x8 pb = pack8(pv[8 * c + 0], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
-                              pv[8 * c + 4], pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
+      const f16x8 pb = pack8_f16(pv[8 * c + 0], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
+                                 pv[8 * c + 4], pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma32(va[dt][c], pb, oacc[dt]);
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma32_f16(va[dt][c], pb, oacc[dt]);
     }
     // the next step's entry and row count: issued after every LDS read of this step is consumed
     // (a scalar load in flight would make the compiler wait for all LDS reads at once)
@@ -344,6 +349,8 @@ fwd_kernel(FwdParams p) {
   const float a_o = m_o == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_o - m);
   const float l = a_me * l_run + a_o * l_o;
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
+  // O^T accumulated P v16 = P v * 2^-e: scale back exactly after normalising
+  const int vexp = f16_head_exponent(ld_const(p.v_amax, bh));
   bf16* orow = p.o + head + (size_t)qrow * HEAD_DIM;
   auto finish = [&](const f32x16& mine, int u, int dt) __attribute__((always_inline)) {
 #pragma unroll
@@ -354,7 +361,8 @@ fwd_kernel(FwdParams p) {
         s16x4 s;
       } r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r.b[e] = (bf16)((a_me * mine[4 * c + e] + a_o * o2[e]) * inv_l);
+      for (int e = 0; e < 4; ++e)
+        r.b[e] = (bf16)__builtin_ldexpf((a_me * mine[4 * c + e] + a_o * o2[e]) * inv_l, vexp);
       // element 4c + e of tile dt is d = 32dt + 8c + 4g + e
       *(s16x4*)(orow + 32 * dt + 8 * c + 4 * g) = r.s;
     }
@@ -368,6 +376,81 @@ fwd_kernel(FwdParams p) {
   }
   if (wk == 0 && g == 0)
     p.lse[(size_t)bh * p.S + qrow] = l > 0.f ? m + __builtin_log2f(l) : -__builtin_inff();
+}
+
+namespace {
+
+// One workgroup per (bh, 64-row tile): each thread takes four 16-byte chunks of the 16 KiB tile.
+// |x| of a bf16 is its bit pattern with the sign cleared, and for non-negative values the bit
+// patterns order like the values, so the max is an integer max (fp32 bits = bf16 bits << 16). The
+// tile's max goes to tmax[tile]; no atomics (thousands of them on one word per head serialise).
+__global__ void __launch_bounds__(256) v_tile_absmax_kernel(const bf16* __restrict__ v,
+                                                            uint32_t* __restrict__ tmax) {
+  __shared__ uint32_t wmax[4];
+  const i32x4* src = (const i32x4*)(v + (size_t)blockIdx.x * BLOCK * HEAD_DIM);
+  uint32_t m = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const i32x4 x = src[c * 256 + threadIdx.x];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = (uint32_t)x[e];
+      m = max(m, max(u & 0x7FFFu, (u >> 16) & 0x7FFFu));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    tmax[blockIdx.x] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16;
+}
+
+// One workgroup per head: amax[bh] = max over the head's tile maxima.
+__global__ void __launch_bounds__(256) v_head_absmax_kernel(const uint32_t* __restrict__ tmax,
+                                                            int tiles_per_head,
+                                                            uint32_t* __restrict__ amax) {
+  __shared__ uint32_t wmax[4];
+  const uint32_t* t = tmax + (size_t)blockIdx.x * tiles_per_head;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < tiles_per_head; i += 256) m = max(m, t[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) amax[blockIdx.x] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+}
+
+__global__ void __launch_bounds__(256) v16_convert_kernel(const bf16* __restrict__ v,
+                                                          int tiles_per_head,
+                                                          const uint32_t* __restrict__ amax,
+                                                          f16* __restrict__ v16) {
+  const int tile = blockIdx.x;
+  const int e = f16_head_exponent(ld_const(amax, tile / tiles_per_head));
+  const size_t base = (size_t)tile * BLOCK * HEAD_DIM;
+  const bf16x8* src = (const bf16x8*)(v + base);
+  f16x8* dst = (f16x8*)(v16 + base);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bf16x8 x = src[c * 256 + threadIdx.x];
+    f16x8 y;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = (f16)__builtin_ldexpf((float)x[k], -e);
+    dst[c * 256 + threadIdx.x] = y;
+  }
+}
+
+}  // namespace
+
+void launch_v16(const bf16* v, int BH, int S, uint32_t* amax, uint32_t* tmax, f16* v16,
+               hipStream_t stream) {
+  const int tiles_per_head = S / BLOCK;
+  hipLaunchKernelGGL(v_tile_absmax_kernel, dim3(BH * tiles_per_head), dim3(256), 0, stream, v,
+                     tmax);
+  hipLaunchKernelGGL(v_head_absmax_kernel, dim3(BH), dim3(256), 0, stream,
+                     (const uint32_t*)tmax, tiles_per_head, amax);
+  hipLaunchKernelGGL(v16_convert_kernel, dim3(BH * tiles_per_head), dim3(256), 0, stream, v,
+                     tiles_per_head, (const uint32_t*)amax, v16);
 }
 
 void launch_fwd(const FwdParams& p, hipStream_t stream) {

@@ -132,6 +132,16 @@ size_t fwd_bounds_bytes(size_t items, int nchunks) {
   return align256(items * (size_t)(nchunks + 1) * sizeof(int32_t));
 }
 
+// The forward workspace starts with the V pre-pass: each head's max |v| bits, then the fp16 copy
+// of v ([B, H, S, 128], 2 bytes per element).
+size_t fwd_amax_bytes(size_t bh, int seqlen) {  // per head, then per 64-row tile
+  return align256(bh * sizeof(uint32_t)) +
+         align256(bh * (size_t)(seqlen / vsa::BLOCK) * sizeof(uint32_t));
+}
+size_t fwd_v16_bytes(size_t bh, int seqlen) {
+  return align256(bh * (size_t)seqlen * vsa::HEAD_DIM * 2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,10 +149,12 @@ extern "C" {
 size_t vsa_fwd_workspace_bytes(int batch, int heads, int seqlen, int kv_chunk_blocks) {
   if (!dims_ok(batch, heads, seqlen, seqlen / vsa::BLOCK)) return 0;
   const int nb = seqlen / vsa::BLOCK;
+  const size_t bh = (size_t)batch * heads;
+  const size_t v16 = fwd_amax_bytes(bh, seqlen) + fwd_v16_bytes(bh, seqlen);
   const int ck = fwd_chunk_kv_blocks(nb, kv_chunk_blocks);
-  if (ck == 0) return 0;
-  const size_t items = (size_t)batch * heads * nb;
-  return fwd_bounds_bytes(items, (nb + ck - 1) / ck) +
+  if (ck == 0) return v16;
+  const size_t items = bh * nb;
+  return v16 + fwd_bounds_bytes(items, (nb + ck - 1) / ck) +
          align256(items * 4 * (size_t)vsa::FWD_STATE_FLOATS * sizeof(float));
 }
 
@@ -160,7 +172,7 @@ int vsa_fwd_check(const vsa_fwd_args* a) {
     return fail(VSA_EINVAL, "vsa_fwd: null pointer");
   const size_t need =
       vsa_fwd_workspace_bytes(a->batch, a->heads, a->seqlen, a->kv_chunk_blocks);
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+  if (!a->workspace || a->workspace_bytes < need)
     return fail(VSA_EINVAL, "vsa_fwd: workspace of " + std::to_string(a->workspace_bytes) +
                                 " bytes, need " + std::to_string(need));
   return VSA_OK;
@@ -190,11 +202,23 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
   p.chunk_bounds = nullptr;
   p.state = nullptr;
   hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)a->workspace;
+  uint32_t* amax = (uint32_t*)ws;
+  uint32_t* tmax = (uint32_t*)(ws + align256((size_t)p.BH * sizeof(uint32_t)));
+  vsa::f16* v16 = (vsa::f16*)(ws + fwd_amax_bytes(p.BH, p.S));
+  p.v_amax = amax;
+  p.v16 = v16;
+  vsa::launch_v16(p.v, p.BH, p.S, amax, tmax, v16, s);
+  {
+    const int r = launch_status("vsa_fwd v pre-pass");
+    if (r != VSA_OK) return r;
+  }
+  ws += fwd_amax_bytes(p.BH, p.S) + fwd_v16_bytes(p.BH, p.S);
   if (p.nchunks > 0) {
     const size_t items = (size_t)p.BH * p.nb;
-    int32_t* bounds = (int32_t*)a->workspace;
+    int32_t* bounds = (int32_t*)ws;
     p.chunk_bounds = bounds;
-    p.state = (float*)((char*)a->workspace + fwd_bounds_bytes(items, p.nchunks));
+    p.state = (float*)(ws + fwd_bounds_bytes(items, p.nchunks));
     vsa::launch_chunk_bounds(a->q2k_idx, a->q2k_num, a->q2k_stride, (int)items, p.nchunks, ck,
                              bounds, s);
     const int r = launch_status("vsa_fwd chunk bounds");

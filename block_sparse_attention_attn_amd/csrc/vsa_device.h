@@ -34,6 +34,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef _Float16 f16;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
 #define VSA_LDS __attribute__((address_space(3)))
 
@@ -44,11 +46,25 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 // Two transposed 8-byte LDS reads joined into one 8-element MFMA operand.
 __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
   union {
     s16x4 h[2];
     bf16x8 v;
+  } u;
+  u.h[0] = lo;
+  u.h[1] = hi;
+  return u.v;
+}
+
+__device__ __forceinline__ f16x8 join_f16(s16x4 lo, s16x4 hi) {
+  union {
+    s16x4 h[2];
+    f16x8 v;
   } u;
   u.h[0] = lo;
   u.h[1] = hi;
@@ -85,6 +101,33 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   r[6] = (bf16)a6;
   r[7] = (bf16)a7;
   return r;
+}
+
+// Eight fp32 values to one f16x8 operand, round-to-nearest-even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ f16x8 pack8_f16(float a0, float a1, float a2, float a3, float a4,
+                                           float a5, float a6, float a7) {
+  f16x8 r;
+  r[0] = (f16)a0;
+  r[1] = (f16)a1;
+  r[2] = (f16)a2;
+  r[3] = (f16)a3;
+  r[4] = (f16)a4;
+  r[5] = (f16)a5;
+  r[6] = (f16)a6;
+  r[7] = (f16)a7;
+  return r;
+}
+
+// The power-of-two exponent e that brings a head's largest |value| (fp32 bits `amax_bits`, as
+// kept by an atomicMax on the bit pattern of non-negative floats) into [2^14, 2^15): an fp16 copy
+// x * 2^-e then holds every bf16 value of magnitude >= 2^-28 * max exactly (8 significant bits in
+// fp16's normal range). 0 for an all-zero head and for inf/NaN (those propagate either way).
+__device__ __forceinline__ int f16_head_exponent(uint32_t amax_bits) {
+  const int ex = (int)((amax_bits >> 23) & 0xFF);
+  if (ex == 255 || amax_bits == 0) return 0;
+  // floor(log2(max)) for normal and subnormal fp32 values
+  const int l2 = ex > 0 ? ex - 127 : -118 - __builtin_clz(amax_bits & 0x7FFFFF);
+  return l2 - 14;
 }
 
 // ---------------------------------------------------------------------------------------------

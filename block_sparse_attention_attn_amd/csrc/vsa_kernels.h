@@ -27,6 +27,10 @@ struct FwdParams {
   const int32_t* vbs;      // [nkv]
   bf16* o;
   float* lse;
+  // fp16 copy of v, each head scaled by 2^-e with e = f16_head_exponent(v_amax[bh]) (the P V
+  // product runs in fp16: see launch_v16)
+  const f16* v16;
+  const uint32_t* v_amax;  // [BH]: bits of each head's max |v|
   int BH, S, nb, q2k_stride;
   int items_per_xcd;  // ceil(BH * nb / 8): workgroup ids map XCD-first onto (bh, q block) items
   float scale_log2;
@@ -40,6 +44,11 @@ struct FwdParams {
 // per wave: 64 lane-major rows of O^T accumulator elements, then the running max and sum rows
 constexpr int FWD_STATE_FLOATS = 66 * 64;
 void launch_fwd(const FwdParams& p, hipStream_t stream);
+// The forward's V pre-pass: tmax[bh * S/64 + t] = bits of max |v| over 64-row tile t, amax[bh]
+// = their max over the head, then v16 = fp16(v * 2^-e) with e = f16_head_exponent(amax[bh]).
+// Three launches; v and v16 are [BH, S, 128].
+void launch_v16(const bf16* v, int BH, int S, uint32_t* amax, uint32_t* tmax, f16* v16,
+                hipStream_t stream);
 
 // ---- backward preprocess: Delta, zero dK/dV rows of empty kv blocks ----
 // The main kernels read a q block's row statistics as one record of LD_RECORD_FLOATS floats per

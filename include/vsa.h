@@ -74,8 +74,15 @@ int vsa_invert_indices(const int32_t* q2k_idx, const int32_t* q2k_num, int batch
  * in the workspace, exactly: the results are bitwise those of one launch. The workgroups running
  * together on one XCD then share a window of R kv blocks, so their K/V tiles stay in its L2.
  * Any list order is correct; ascending lists give the locality. kv_chunk_blocks < 0: never
- * chunk. Workspace (vsa_fwd_workspace_bytes, NULL/0 when that is 0): int32 [B*H*nb, C+1] chunk
- * bounds, then fp32 [B*H*nb, 4, 66, 64] per-wave state. */
+ * chunk.
+ *
+ * The P v product runs on fp16 operands (same MFMA rate as bf16, 8x finer rounding of P): a
+ * pre-pass writes an fp16 copy of v into the workspace, each head scaled by the power of two that
+ * brings its largest |v| into [2^14, 2^15), so every bf16 value of v with |v| >= 2^-28 * max|v|
+ * of its head is copied exactly; o is scaled back exactly. Workspace (vsa_fwd_workspace_bytes,
+ * 256-byte aligned regions): uint32 [B*H] per-head and [B*H*nb] per-tile max |v| bits, fp16
+ * [B, H, S, 128] scaled copy of v, then with chunks int32 [B*H*nb, C+1] chunk bounds and fp32 [B*H*nb, 4, 66, 64]
+ * per-wave state. */
 #define VSA_FWD_CHUNK_KV_BLOCKS 512
 typedef struct {
   const void* q;          /* bf16 [B, H, S, 128] */
@@ -88,13 +95,12 @@ typedef struct {
   float* lse;             /* fp32 [B, H, S], output */
   int batch, heads, seqlen, head_dim, num_kv_blocks, q2k_stride;
   float sm_scale;         /* finite; negative and zero are allowed (zero acts as 2^-126) */
-  void* workspace;        /* see above; may be NULL when vsa_fwd_workspace_bytes is 0 */
+  void* workspace;        /* see above; at least vsa_fwd_workspace_bytes */
   size_t workspace_bytes;
   int kv_chunk_blocks;    /* kv-range chunks, see above; 0 = default */
 } vsa_fwd_args;
 
-/* Bytes of forward workspace for these sizes and kv_chunk_blocks; 0 when the forward runs as one
- * launch (or for an invalid shape). */
+/* Bytes of forward workspace for these sizes and kv_chunk_blocks (0 for an invalid shape). */
 size_t vsa_fwd_workspace_bytes(int batch, int heads, int seqlen, int kv_chunk_blocks);
 int vsa_fwd_check(const vsa_fwd_args* a);
 int vsa_fwd(const vsa_fwd_args* a, void* stream);

@@ -132,13 +132,19 @@ def test_workspace_chunk_regions():
     assert o[V.WS_END] - o[V.WS_DQ_PART] == 10 * 64 * 128 * 4
     o = offs(1, 1, 64 * 10, 0, 10)
     assert o[V.WS_END] == o[V.WS_CHUNK_BOUNDS]
-    # the forward's kv-range chunks: bounds, then per-wave state of 66 x 64 floats
+    # the forward: per-head max |v| bits and the fp16 copy of v, then with kv-range chunks the
+    # bounds and per-wave state of 66 x 64 floats
+    def v16(bh, S):
+        return a256(bh * 4) + a256(bh * (S // 64) * 4) + a256(bh * S * 128 * 2)
     nbf = V.CHUNK_MIN_KV_BLOCKS
     cf = -(-nbf // V.FWD_CHUNK_KV_BLOCKS)
-    assert V.fwd_workspace_bytes(1, 2, 64 * nbf) == a256(2 * nbf * (cf + 1) * 4) + 2 * nbf * 4 * 66 * 64 * 4
-    assert V.fwd_workspace_bytes(1, 2, 64 * nbf, -1) == 0
-    assert V.fwd_workspace_bytes(1, 2, 64 * 512) == 0
-    assert V.fwd_workspace_bytes(1, 1, 64 * 10, 4) == a256(10 * 4 * 4) + 10 * 4 * 66 * 64 * 4
+    assert V.fwd_workspace_bytes(1, 2, 64 * nbf) == (v16(2, 64 * nbf) + a256(2 * nbf * (cf + 1) * 4)
+                                                     + 2 * nbf * 4 * 66 * 64 * 4)
+    assert V.fwd_workspace_bytes(1, 2, 64 * nbf, -1) == v16(2, 64 * nbf)
+    assert V.fwd_workspace_bytes(1, 2, 64 * 512) == v16(2, 64 * 512)
+    assert V.fwd_workspace_bytes(1, 1, 64 * 10, 4) == (v16(1, 640) + a256(10 * 4 * 4)
+                                                       + 10 * 4 * 66 * 64 * 4)
+    assert V.fwd_workspace_bytes(1, 1, 63) == 0
     assert V.invert_workspace_bytes(2, 3, 100, 50) == ((2 * 3 * 50 * 4 * 4 + 255) // 256) * 256
     assert V.invert_workspace_bytes(1, 1, 0, 1) == 0
 
@@ -214,13 +220,15 @@ def test_bwd_and_stage_fail_before_launch_on_bad_args():
 
 def test_fwd_check():
     fake = 0x10000
+    need = V.fwd_workspace_bytes(1, 1, 256)
     base = dict(q=fake, k=fake, v=fake, q2k_idx=fake, q2k_num=fake, vbs=fake, o=fake, lse=fake,
                 batch=1, heads=1, seqlen=256, head_dim=128, num_kv_blocks=4, q2k_stride=2,
-                sm_scale=0.088)
+                sm_scale=0.088, workspace=fake, workspace_bytes=need)
     L = V.lib()
     assert L.vsa_fwd_check(ctypes.byref(V._FwdArgs(**base))) == VSA_OK
     for over, st in ((dict(head_dim=256), VSA_EUNSUPPORTED), (dict(q2k_stride=0), VSA_EINVAL),
-                     (dict(o=None), VSA_EINVAL), (dict(seqlen=255), VSA_EINVAL)):
+                     (dict(o=None), VSA_EINVAL), (dict(seqlen=255), VSA_EINVAL),
+                     (dict(workspace=None), VSA_EINVAL), (dict(workspace_bytes=need - 1), VSA_EINVAL)):
         assert L.vsa_fwd_check(ctypes.byref(V._FwdArgs(**{**base, **over}))) == st
         assert L.vsa_fwd(ctypes.byref(V._FwdArgs(**{**base, **over})), None) == st
 
