@@ -71,7 +71,11 @@ class _BwdArgs(ctypes.Structure):
 
 # workspace regions of the backward (vsa_bwd_ws_region)
 (WS_LSE_DELTA, WS_KV_ORDER, WS_Q_ORDER, WS_Q2K_NUM, WS_Q2K_IDX, WS_BITMAP, WS_KBASE, WS_QENT,
- WS_DS, WS_CHUNK_BOUNDS, WS_DKV_PART, WS_DQ_BOUNDS, WS_DQ_PART, WS_END) = range(14)
+ WS_DS, WS_CHUNK_BOUNDS, WS_DKV_PART, WS_DQ_BOUNDS, WS_DQ_PART, WS_STATS, WS_SCALES, WS_Q16,
+ WS_K16, WS_DO16, WS_V16, WS_END) = range(20)
+# words of a head's entry in WS_SCALES (vsa.h): the fp16 operands are q 2^-eq, k 2^-ek, v 2^-ev,
+# dO 2^-eo, P 2^pp and dS 2^es; c = fp32(sm_scale log2 e) 2^(eq + ek), stored as fp32 bits
+SC_EQ, SC_EK, SC_EV, SC_EO, SC_PP, SC_ES, SC_C = range(7)
 # how the q-major kernel gets dS (vsa_dq_mode): recomputed from Q, K, V, dO, or spilled by the
 # kv-major kernel into the workspace (8 KiB per possible pair)
 DQ_RECOMPUTE, DQ_SPILL = 0, 1
@@ -460,12 +464,18 @@ class BwdPlan:
 
     def lse_delta(self) -> torch.Tensor:
         """The workspace's per-q-block statistics records as fp32 [B, H, nb, 2, 64] (valid after
-        PREPROCESS): -lse / scale_log2 of the block's 64 rows, then -Delta of its 64 rows, where
-        scale_log2 = fp32(sm_scale * log2 e)."""
+        PREPROCESS): (pp - lse) / c of the block's 64 rows, then -Delta * 2^-(eo + ev) of its 64
+        rows, with the head's words of ``scales()``."""
         a = self.args
         nb = a.seqlen // BLOCK
         n = a.batch * a.heads * a.seqlen * 2
         return self.region(WS_LSE_DELTA, n, torch.float32).view(a.batch, a.heads, nb, 2, BLOCK)
+
+    def scales(self) -> torch.Tensor:
+        """The per-head operand scales as int32 [B, H, 8] (valid after PREPROCESS): words SC_EQ,
+        SC_EK, SC_EV, SC_EO, SC_PP, SC_ES, then SC_C (fp32 bits) and 0."""
+        a = self.args
+        return self.region(WS_SCALES, a.batch * a.heads * 8, torch.int32).view(a.batch, a.heads, 8)
 
 
 def backward_from_k2q(grad_o: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -1,10 +1,13 @@
-// bwd_aux.hip -- the streaming kernels around the backward's main kernel (gfx950):
+// bwd_aux.hip -- the streaming kernels around the backward's main kernels (gfx950):
 //   preprocess  Delta = rowsum(bf16(o) * dO) in fp32, and the exact-zero dK/dV rows of kv blocks
 //               that no q block selects (FastVideo sm_100a backward commit message, the
-//               preprocess sentence; launch header, the delta field of the argument struct).
-//               Delta is stored in a 512-byte record per q block: -lse/scale_log2 of its 64
-//               rows, then -Delta of its 64 rows, the initial accumulator values of the
-//               kv-major kernel's S and dP MFMAs;
+//               preprocess sentence; launch header, the delta field of the argument struct);
+//               here also the per-head power-of-two scales and scaled fp16 copies of q, k, dO
+//               (and v) that let the main kernels run their GEMMs on fp16 operands (the backward
+//               test page's tolerance block measures the result against bf16-rounded
+//               references: fp16 P and dS carry 11 significant bits where bf16 carries 8).
+//               Delta and lse go into a 512-byte record per q block, the initial accumulator
+//               values of the kv-major kernel's S and dP MFMAs;
 //   order       the per-(b, h) length-binned permutation of work items that the launch header
 //               computes on device from 1024 kv blocks on (its order-kernel launch and the
 //               ORDER_MIN_KV_BLOCKS comment); used for the kv-major and the q-major kernel;
@@ -12,49 +15,186 @@
 //               order, contiguous per kv block) and, per q2k entry, where to find it.
 // The preprocess streams with 16-byte accesses, consecutive lanes on consecutive 16-byte chunks
 // of a row. (The pages' dQ postprocess -- scale by sm_scale, round to bf16 -- is fused into the
-// q-major dQ kernel's epilogue here.)
+// q-major dQ kernels' epilogues here.)
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
 namespace vsa {
 
-// grid (nb, BH), 256 threads; each pass covers 16 rows x 16 chunks of 8 elements.
-__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdPreParams p) {
+namespace {
+
+// Max over the 64 lanes of a wave, then over the four waves through LDS; every thread gets it.
+// Values are non-negative fp32 bit patterns, so the integer max is the value max.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();  // red may still be read from the previous call
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Sum of the 16 lanes that share a row (fixed order), every lane of the group gets it.
+__device__ __forceinline__ float row_sum16(float a) {
+  a += __shfl_xor(a, 8, 64);
+  a += __shfl_xor(a, 4, 64);
+  a += __shfl_xor(a, 2, 64);
+  a += __shfl_xor(a, 1, 64);
+  return a;
+}
+
+__device__ __forceinline__ float fbits(uint32_t u) { return __uint_as_float(u); }
+
+// ceil(log2(b)) for a positive normal fp32 value
+__device__ __forceinline__ int ceil_log2(float b) {
+  const uint32_t u = __float_as_uint(b);
+  const int ex = (int)((u >> 23) & 0xFF) - 127;
+  return (u & 0x7FFFFF) ? ex + 1 : ex;
+}
+
+}  // namespace
+
+// Pass 1, grid (nb, BH), 256 threads (each pass of four covers 16 rows x 16 chunks of 8
+// elements): the block's maxima of |q|, |k|, |v|, |dO|, of the row norms |v_j|^2, |dO_i|^2 and of
+// |Delta_i|; Delta_i = rowsum(bf16(o) * dO) in fp32 goes (negated) into the dP half of the record;
+// the exact-zero dK/dV rows of a kv block that no q block selects.
+__global__ void __launch_bounds__(256) bwd_stats_kernel(BwdPreParams p) {
+  __shared__ uint32_t red[4];
   const int blk = blockIdx.x;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
   const int rr = tid >> 4;  // row inside the pass
-  const int c = tid & 15;   // 16-byte chunk of the row (8 bf16 / 8 fp32 halves)
+  const int c = tid & 15;   // 16-byte chunk of the row
   const size_t row0 = (size_t)bh * p.S + (size_t)blk * BLOCK;
   const bool empty = p.k2q_num[(size_t)bh * p.nb + blk] == 0;
+  float* rec = p.lse_delta + ((size_t)bh * p.nb + blk) * LD_RECORD_FLOATS;
+  uint32_t mq = 0, mk = 0, mv = 0, mo = 0;
+  float n2v = 0.0f, n2o = 0.0f, md = 0.0f;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const size_t row = row0 + pass * 16 + rr;
-    const bf16x8 o = *(const bf16x8*)(p.o + row * HEAD_DIM + c * 8);
-    const bf16x8 d = *(const bf16x8*)(p.dout + row * HEAD_DIM + c * 8);
-    float acc = 0.0f;
+    const size_t at = row * HEAD_DIM + c * 8;
+    const bf16x8 q = *(const bf16x8*)(p.q + at);
+    const bf16x8 k = *(const bf16x8*)(p.k + at);
+    const bf16x8 v = *(const bf16x8*)(p.v + at);
+    const bf16x8 o = *(const bf16x8*)(p.o + at);
+    const bf16x8 d = *(const bf16x8*)(p.dout + at);
+    mq = max(mq, absmax_bits8(q));
+    mk = max(mk, absmax_bits8(k));
+    mv = max(mv, absmax_bits8(v));
+    mo = max(mo, absmax_bits8(d));
+    float delta = 0.0f, sv = 0.0f, so = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)d[e], acc);
-    // fixed-order reduction over the 16 lanes of the row
-    acc += __shfl_xor(acc, 8, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 1, 64);
-    if (c == 0) {
-      float* rec = p.lse_delta + ((size_t)bh * p.nb + blk) * LD_RECORD_FLOATS;
-      const int r = pass * 16 + rr;
-      rec[r] = -(p.lse[row] / p.scale_log2);  // IEEE division: a fixed, testable rounding
-      rec[BLOCK + r] = -acc;
+    for (int e = 0; e < 8; ++e) {
+      delta = __builtin_fmaf((float)o[e], (float)d[e], delta);
+      sv = __builtin_fmaf((float)v[e], (float)v[e], sv);
+      so = __builtin_fmaf((float)d[e], (float)d[e], so);
     }
+    delta = row_sum16(delta);
+    n2v = fmaxf(n2v, row_sum16(sv));
+    n2o = fmaxf(n2o, row_sum16(so));
+    md = fmaxf(md, fabsf(delta));
+    if (c == 0) rec[BLOCK + pass * 16 + rr] = -delta;
     if (empty) {
-      *(bf16x8*)(p.dk + row * HEAD_DIM + c * 8) = bf16x8{};
-      *(bf16x8*)(p.dv + row * HEAD_DIM + c * 8) = bf16x8{};
+      *(bf16x8*)(p.dk + at) = bf16x8{};
+      *(bf16x8*)(p.dv + at) = bf16x8{};
+    }
+  }
+  // (max over NaN: fmaxf drops it and integer max keeps the larger pattern; a NaN input
+  // propagates through the kernels' arithmetic either way)
+  uint32_t out[7] = {mq, mk, mv, mo, __float_as_uint(n2v), __float_as_uint(n2o),
+                     __float_as_uint(md)};
+  uint32_t* st = p.stats + ((size_t)bh * p.nb + blk) * STAT_WORDS;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const uint32_t m = block_max_u32(out[i], red);
+    if (tid == 0) st[i] = m;
+  }
+  if (tid == 0) st[7] = 0;
+}
+
+// Pass 2, one 256-thread workgroup per head: reduce the block statistics, derive the exponents.
+__global__ void __launch_bounds__(256) bwd_scales_kernel(BwdPreParams p) {
+  __shared__ uint32_t red[4];
+  const int bh = blockIdx.x;
+  const uint32_t* st = p.stats + (size_t)bh * p.nb * STAT_WORDS;
+  uint32_t m[7] = {0, 0, 0, 0, 0, 0, 0};
+  for (int b = threadIdx.x; b < p.nb; b += 256) {
+#pragma unroll
+    for (int i = 0; i < 7; ++i) m[i] = max(m[i], st[(size_t)b * STAT_WORDS + i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 7; ++i) m[i] = block_max_u32(m[i], red);
+  if (threadIdx.x != 0) return;
+  // q16, k16 exponents, moved (equally) where needed so that c = scale_log2 * 2^(eq + ek) stays
+  // within [2^-101, 2^102]: only a head whose scores are all far below fp32 resolution (or
+  // beyond its range) gets there, and then loses fp16 precision in q16, k16
+  int eq = f16_exponent(m[ST_Q], 14);
+  int ek = f16_exponent(m[ST_K], 14);
+  {
+    const int l = (int)((__float_as_uint(p.scale_log2) >> 23) & 0xFF) - 127;  // normal: >= 2^-120
+    const int t = l + eq + ek;
+    const int d = t < -100 ? -100 - t : (t > 100 ? 100 - t : 0);
+    eq += d / 2;
+    ek += d - d / 2;
+  }
+  const int ev = f16_exponent(m[ST_V], 0);
+  const int eo = f16_exponent(m[ST_DO], 0);
+  // |dP_ij - Delta_i| in the scaled units, with margin for the fp32 sums
+  const float nv = __builtin_ldexpf(sqrtf(fbits(m[ST_V2])), -ev);
+  const float no = __builtin_ldexpf(sqrtf(fbits(m[ST_DO2])), -eo);
+  const float dm = __builtin_ldexpf(__builtin_ldexpf(fbits(m[ST_DELTA]), -eo), -ev);
+  const float b = 1.0625f * (no * nv + dm);
+  int pp = 15;
+  if (!(b <= 3.0e38f)) pp = -30;                 // inf or NaN inputs
+  else if (b >= 0x1p-126f) pp = 15 - ceil_log2(b);
+  pp = pp > 15 ? 15 : (pp < -30 ? -30 : pp);
+  int32_t* out = p.scales + (size_t)bh * HEAD_SCALE_WORDS;
+  out[SC_EQ] = eq;
+  out[SC_EK] = ek;
+  out[SC_EV] = ev;
+  out[SC_EO] = eo;
+  out[SC_PP] = pp;
+  out[SC_ES] = pp - eo - ev;
+  out[SC_C] = (int32_t)__float_as_uint(__builtin_ldexpf(p.scale_log2, eq + ek));
+  out[7] = 0;
+}
+
+// Pass 3, grid (nb, BH), 256 threads: the fp16 copies of block blk's rows of q, k, dO (and v when
+// asked), and the record: (pp - lse) / c (IEEE fp32 subtraction and division), -Delta 2^-(eo+ev).
+__global__ void __launch_bounds__(256) bwd_convert_kernel(BwdPreParams p) {
+  const int blk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int rr = tid >> 4;
+  const int c = tid & 15;
+  const int32_t* sc = p.scales + (size_t)bh * HEAD_SCALE_WORDS;
+  const int eq = ld_const(sc, SC_EQ), ek = ld_const(sc, SC_EK), ev = ld_const(sc, SC_EV);
+  const int eo = ld_const(sc, SC_EO), pp = ld_const(sc, SC_PP);
+  const float cc = __uint_as_float((uint32_t)ld_const(sc, SC_C));
+  const size_t row0 = (size_t)bh * p.S + (size_t)blk * BLOCK;
+  float* rec = p.lse_delta + ((size_t)bh * p.nb + blk) * LD_RECORD_FLOATS;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const size_t row = row0 + pass * 16 + rr;
+    const size_t at = row * HEAD_DIM + c * 8;
+    *(f16x8*)(p.q16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.q + at), eq);
+    *(f16x8*)(p.k16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.k + at), ek);
+    *(f16x8*)(p.do16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.dout + at), eo);
+    if (p.v16) *(f16x8*)(p.v16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.v + at), ev);
+    if (c == 0) {
+      const int r = pass * 16 + rr;
+      rec[r] = ((float)pp - p.lse[row]) / cc;
+      rec[BLOCK + r] = __builtin_ldexpf(__builtin_ldexpf(rec[BLOCK + r], -eo), -ev);
     }
   }
 }
 
 void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3(p.nb, p.BH), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(bwd_stats_kernel, dim3(p.nb, p.BH), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(bwd_scales_kernel, dim3(p.BH), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(bwd_convert_kernel, dim3(p.nb, p.BH), dim3(256), 0, stream, p);
 }
 
 // Work order of one (b, h) (one 1024-thread workgroup): bitonic sort of 32-bit keys (inverted

@@ -15,6 +15,12 @@
 // the preprocess wrote their zero rows. dQ is computed by the q-major kernel (bwd_dq.hip), so
 // this kernel issues no atomics and its results are bitwise reproducible.
 //
+// Every GEMM runs on fp16 operands (v_mfma_f32_32x32x16_f16): the preprocess's per-head scaled
+// copies q16, k16, do16, v converted to v 2^-ev in LDS, P' = P 2^pp and dS' = dS 2^es in
+// fp16 (11 significant bits where bf16 has 8). The accumulators hold S' = S 2^-(eq+ek),
+// dP' = dP 2^-(eo+ev), dV' = dV 2^(pp-eo) and dK' = dK 2^(es-eq); the epilogue scales back by
+// exact powers of two (vsa_kernels.h, HeadScaleWord).
+//
 // gfx950 design:
 //   * one 256-thread workgroup (4 waves, one per SIMD) per item; wave w owns q rows 32*(w&1)..
 //     of every q block and kv rows 32*(w>>1).. of the item, so each 64x64x128 GEMM is eight
@@ -23,12 +29,12 @@
 //     with padded kv rows zeroed there. They arrive by DMA through LDS like everything else, so
 //     every vector memory operation of the kernel is an LDS DMA whose completion is counted by
 //     hand;
-//   * Q_i, dO_i and the q block's 512-byte statistics record (-lse_i / scale_log2 and -Delta_i,
+//   * Q_i, dO_i and the q block's 512-byte statistics record ((pp - lse_i) / c and -Delta'_i,
 //     written by the preprocess) stream through a four-stage ring of XOR-swizzled LDS tiles,
 //     fetched by global_load_lds_dwordx4 two steps before their first use; one barrier per q
 //     block, between the two phases of a step;
 //   * the S and dP accumulators start from the record's values, so the MFMAs deliver
-//     S - lse/scale_log2 and dP - Delta directly: P = exp2(scale_log2 * acc), dS = P * acc';
+//     S' + (pp - lse) / c and dP' - Delta' directly: P' = exp2(c * acc), dS' = P' * acc';
 //   * software pipeline across q blocks: phase B of step t runs the S/dP MFMAs of q block t+1
 //     interleaved with the exp2/convert work of q block t and its transposed reads; phase C runs
 //     the dV/dK MFMAs of q block t interleaved with the row and record reads of q block t+2, so
@@ -117,8 +123,9 @@ bwd_dkdv_kernel(BwdParams p) {
   const int j = item - bh * p.nb;
   const int vb = ld_const(p.vbs, j);
   const size_t head = (size_t)bh * p.S * HEAD_DIM;
-  const bf16* __restrict__ qh = p.q + head;
-  const bf16* __restrict__ doh = p.dout + head;
+  const f16* __restrict__ qh = p.q16 + head;
+  const f16* __restrict__ doh = p.do16 + head;
+  const int32_t* __restrict__ hs = p.scales + (size_t)bh * HEAD_SCALE_WORDS;
   const float* __restrict__ recs = p.lse_delta + (size_t)bh * p.nb * LD_RECORD_FLOATS;
   const int* __restrict__ list = p.k2q_idx + (size_t)item * p.k2q_stride + start;
   // q block ids outside [0, nb) violate the caller contract; clamp them so no access leaves the
@@ -153,7 +160,7 @@ bwd_dkdv_kernel(BwdParams p) {
     // K_j, V_j into stage 3 of the rings; q blocks 0, 1, 2 into stages 0, 1, 2.
     {
       const size_t tile = (size_t)j * BLOCK * HEAD_DIM;
-      dma_tile_pair(p.k + head + tile, p.v + head + tile, toff, q_lds + 3 * STAGE_BYTES,
+      dma_tile_pair(p.k16 + head + tile, p.v + head + tile, toff, q_lds + 3 * STAGE_BYTES,
                     do_lds + 3 * STAGE_BYTES);
     }
     {
@@ -163,7 +170,7 @@ bwd_dkdv_kernel(BwdParams p) {
       issue(clampq(e2), 2);
     }
     // dS tiles (spill mode): q block t of this item goes to slot kbase[item] + t of its head. A
-    // lane stores its 16 dS values (two bf16x8) as one 32-byte record; the records of a wave's
+    // lane stores its 16 dS' values (two f16x8) as one 32-byte record; the records of a wave's
     // 32 kv rows are laid out so that the q-major kernel's transposed reads of two record groups
     // fall on disjoint banks: record (w, g, l32) at ((8w + l32/4) * 256 + 128g + 32(l32%4)) bytes.
     char* ds_item = nullptr;
@@ -181,46 +188,60 @@ bwd_dkdv_kernel(BwdParams p) {
       // address land in order), so that every wait below counts the same two stores between the
       // DMA groups of consecutive q blocks.
       char* d = ds_tile(0) + ds_rec;
-      *(bf16x8*)d = bf16x8{};
-      *(bf16x8*)(d + 16) = bf16x8{};
+      *(f16x8*)d = f16x8{};
+      *(f16x8*)(d + 16) = f16x8{};
     }
     const int e3 = entry(3);
     // K/V and q blocks 0, 1 landed (own DMAs); q block 2's may still be in flight
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_BLOCK + (SPILL ? STORES_PER_BLOCK : 0)));
     barrier_lds_with(e3);  // ... everyone's
     int raw = entry(4);    // the list entry step 0 fetches; in by step 0's barrier
+    // V_j to fp16 (v 2^-ev, exact like the preprocess's copies) in place in LDS, 16 bytes at a
+    // time, then meet again. (Converting the register fragments instead keeps more registers live
+    // through the main loop.)
+    {
+      const int ev = ld_const(hs, SC_EV);
+      VSA_LDS bf16x8* vt = (VSA_LDS bf16x8*)(dr + 3 * STAGE_BYTES);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int idx = c * 256 + (int)threadIdx.x;
+        const bf16x8 x = vt[idx];
+        *(VSA_LDS f16x8*)&vt[idx] = bf16x8_to_f16x8(x, ev);
+      }
+      barrier_lds();
+    }
 
-    // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7.
+    // B operand of S = Q K^T and dP = dO V^T: lane holds kv row 32*wk + l32, d = 16*s + 8*g + 0..7
     const int kv_l = 32 * wk + l32;
     const bool kv_valid = kv_l < vb;
-    bf16x8 kf[8], vf[8];
+    f16x8 kf[8], vf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int b = 3 * STAGE_BYTES + tile_byte(kv_l, 2 * s + g);
-      kf[s] = *(const VSA_LDS bf16x8*)(qr + b);
-      vf[s] = *(const VSA_LDS bf16x8*)(dr + b);
+      kf[s] = *(const VSA_LDS f16x8*)(qr + b);
+      vf[s] = *(const VSA_LDS f16x8*)(dr + b);
     }
     if (!kv_valid) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        kf[s] = bf16x8{};
-        vf[s] = bf16x8{};
+        kf[s] = f16x8{};
+        vf[s] = f16x8{};
       }
     }
 
-    const float scale_log2 = p.scale_log2;
+    const float cexp = __uint_as_float((uint32_t)ld_const(hs, SC_C));
     const int qrow = 32 * wq + l32;
 
     // A operands of S = Q K^T and dP = dO V^T for the q block in stage st: q rows 32*wq + l32,
     // d = 16*s + 8*g + 0..7
-    bf16x8 qa[8], da[8];
+    f16x8 qa[8], da[8];
     auto load_rows = [&](int st, int sb) __attribute__((always_inline)) {  // steps sb .. sb+3
       VSA_LDS char* qt = qr + st * STAGE_BYTES;
       VSA_LDS char* dt = dr + st * STAGE_BYTES;
 #pragma unroll
       for (int s = sb; s < sb + 4; ++s) {
-        qa[s] = *(const VSA_LDS bf16x8*)(qt + tile_byte(qrow, 2 * s + g));
-        da[s] = *(const VSA_LDS bf16x8*)(dt + tile_byte(qrow, 2 * s + g));
+        qa[s] = *(const VSA_LDS f16x8*)(qt + tile_byte(qrow, 2 * s + g));
+        da[s] = *(const VSA_LDS f16x8*)(dt + tile_byte(qrow, 2 * s + g));
       }
     };
     // Initial accumulators of the q block in stage st from its record: element i of S / dP is
@@ -272,15 +293,15 @@ bwd_dkdv_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      s0 = mfma32(qa[s], kf[s], s0);
-      p0 = mfma32(da[s], vf[s], p0);
+      s0 = mfma32_f16(qa[s], kf[s], s0);
+      p0 = mfma32_f16(da[s], vf[s], p0);
     }
     load_rows(1, 0);  // a repeat of q block 0 when n == 1
     load_rows(1, 4);
     load_init(1, s1, p1);
 
-    // Step t (q block t in stage st = t % 4): on entry (sc, pc) hold S - lse/scale_log2 and
-    // dP - Delta of q block t, (sn, pn) the initial values of q block t+1 and (qa, da) its rows.
+    // Step t (q block t in stage st = t % 4): on entry (sc, pc) hold S' + (pp - lse) / c and
+    // dP' - Delta' of q block t, (sn, pn) the initial values of q block t+1 and (qa, da) its rows.
     //   phase B: the dO DMA of q block t+3, then the S/dP MFMAs of t+1, interleaved with the
     //            transposed dO^T, Q^T reads of t and P, dS of t;
     //   mid:     q block t+2 has landed (own DMAs, then the barrier: everyone's) and everyone is
@@ -303,34 +324,34 @@ bwd_dkdv_kernel(BwdParams p) {
       // ---- phase B ----
       // transposed B operands of dV/dK for q block t: k slot jj of step s2 is q row
       // 32*wq + 16*s2 + 8*(jj/4) + 4*g + jj%4, matching the D layout of S
-      bf16x8 db[2][4], qbt[2][4];
+      f16x8 db[2][4], qbt[2][4];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const uint32_t o = st * STAGE_BYTES + s2 * 16 * 256;  // stage, then 16 rows further down
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          db[s2][nt] = join(rd_tr(trd[nt][0] + o), rd_tr(trd[nt][1] + o));
-          qbt[s2][nt] = join(rd_tr(trq[nt][0] + o), rd_tr(trq[nt][1] + o));
+          db[s2][nt] = join_f16(rd_tr(trd[nt][0] + o), rd_tr(trd[nt][1] + o));
+          qbt[s2][nt] = join_f16(rd_tr(trq[nt][0] + o), rd_tr(trq[nt][1] + o));
         }
       }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sn = mfma32(qa[s], kf[s], sn);
-        pn = mfma32(da[s], vf[s], pn);
+        sn = mfma32_f16(qa[s], kf[s], sn);
+        pn = mfma32_f16(da[s], vf[s], pn);
       }
-      // P and dS of q block t, half h (elements 8h .. 8h+7: q rows 32*wq + 16h + ..) in bf16. A
-      // padded kv column (zero K/V fragment) gets some finite or non-finite P; it only feeds that
+      // P' and dS' of q block t, half h (elements 8h .. 8h+7: q rows 32*wq + 16h + ..) in fp16. A
+      // padded kv column (zero K/V fragment) gets some finite or non-finite P'; it only feeds that
       // kv row of dV/dK, which the epilogue overwrites with 0.
-      bf16x8 pa[2], sa[2];
+      f16x8 pa[2], sa[2];
       auto softmax_half = [&](int h) __attribute__((always_inline)) {
         float pv[8], dsv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(sc[8 * h + e] * scale_log2);
+          pv[e] = __builtin_amdgcn_exp2f(sc[8 * h + e] * cexp);
           dsv[e] = pv[e] * pc[8 * h + e];
         }
-        pa[h] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        sa[h] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        pa[h] = pack8_f16(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        sa[h] = pack8_f16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
       };
       // Under the S/dP MFMAs; the empty asm keeps this arithmetic in this phase (it is otherwise
       // free to sink next to its use after the barrier).
@@ -362,8 +383,8 @@ bwd_dkdv_kernel(BwdParams p) {
       // phase C delay its MFMAs and DMAs.
       if (SPILL) {  // streamed past the caches: read once, by the q-major kernel
         char* d = ds_tile(t) + ds_rec;
-        __builtin_nontemporal_store(sa[0], (bf16x8*)d);
-        __builtin_nontemporal_store(sa[1], (bf16x8*)(d + 16));
+        __builtin_nontemporal_store(sa[0], (f16x8*)d);
+        __builtin_nontemporal_store(sa[1], (f16x8*)(d + 16));
       }
       barrier_lds_with(raw);  // ... everyone's; everyone is done with stage st
       const int qb = clampq(raw);
@@ -385,13 +406,13 @@ bwd_dkdv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        dv_acc[nt] = mfma32(pa[0], db[0][nt], dv_acc[nt]);
-        dk_acc[nt] = mfma32(sa[0], qbt[0][nt], dk_acc[nt]);
+        dv_acc[nt] = mfma32_f16(pa[0], db[0][nt], dv_acc[nt]);
+        dk_acc[nt] = mfma32_f16(sa[0], qbt[0][nt], dk_acc[nt]);
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        dv_acc[nt] = mfma32(pa[1], db[1][nt], dv_acc[nt]);
-        dk_acc[nt] = mfma32(sa[1], qbt[1][nt], dk_acc[nt]);
+        dv_acc[nt] = mfma32_f16(pa[1], db[1][nt], dv_acc[nt]);
+        dk_acc[nt] = mfma32_f16(sa[1], qbt[1][nt], dk_acc[nt]);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -430,7 +451,10 @@ bwd_dkdv_kernel(BwdParams p) {
   }
   barrier_lds();
   bf16* outp = (wq == 0 ? p.dv : p.dk) + head + (size_t)j * BLOCK * HEAD_DIM;
+  // dv = dV' 2^(eo - pp), dk = sm_scale dK' 2^(eq - es)
   const float oscale = wq == 0 ? 1.0f : p.sm_scale;
+  const int oexp = wq == 0 ? ld_const(hs, SC_EO) - ld_const(hs, SC_PP)
+                           : ld_const(hs, SC_EQ) - ld_const(hs, SC_ES);
   // this wave's tensor (dV for wq 0, dK for wq 1) in the chunk partial sums: [64][128] fp32
   float* part = p.part ? p.part + ((size_t)item * 2 + wq) * (BLOCK * HEAD_DIM) : nullptr;
 #pragma unroll
@@ -446,7 +470,8 @@ bwd_dkdv_kernel(BwdParams p) {
         float sum = mine + o[e];
         if (!first) sum += part[kv * HEAD_DIM + d];
         if (last)  // padded kv rows are exactly zero by definition
-          outp[(size_t)kv * HEAD_DIM + d] = kv < vb ? (bf16)(sum * oscale) : (bf16)0.0f;
+          outp[(size_t)kv * HEAD_DIM + d] =
+              kv < vb ? (bf16)__builtin_ldexpf(sum * oscale, oexp) : (bf16)0.0f;
         else
           part[kv * HEAD_DIM + d] = sum;
       }

@@ -7,7 +7,10 @@
 //     S^T  = K_j Q_i^T,   P^T = exp2(S^T * scale_log2 - lse_i)   (kv rows >= vbs[j] -> 0)
 //     dP^T = V_j dO_i^T,  dS^T = P^T * (dP^T - Delta_i)
 //     dQ_i += dS K_j
-// and dq_i = bf16(sm_scale * dQ_i). A q block with an empty list gets zero rows.
+// and dq_i = bf16(sm_scale * dQ_i). A q block with an empty list gets zero rows. The GEMMs run on
+// the preprocess's scaled fp16 copies (v_mfma_f32_32x32x16_f16): S' = S 2^-(eq+ek),
+// dP' = dP 2^-(eo+ev), P' = P 2^pp = exp2(c S' + pp - lse), dS' = P' (dP' - Delta') = dS 2^es,
+// and the sum dS' k16 = dQ 2^(es-ek) is scaled back in the epilogue.
 //
 // The pages reduce per-pair dQ partials into an fp32 accumulator with bulk asynchronous
 // reductions. On MI355X the equivalent, global_atomic_add_f32, sustains about 3.4e11 lane adds/s
@@ -18,7 +21,7 @@
 //
 // gfx950 layout: one 256-thread workgroup per q block; wave w owns q rows 32*(w&1).. and kv rows
 // 32*(w>>1).. of every kv block. Q_i and dO_i live in registers as the B operands of S^T = K Q^T
-// and dP^T = V dO^T (v_mfma_f32_32x32x16_bf16), so lse and Delta are one scalar per lane. K_j,
+// and dP^T = V dO^T (v_mfma_f32_32x32x16_f16), so lse and Delta are one scalar per lane. K_j,
 // V_j stream through a four-stage ring of swizzled LDS tiles fetched three kv blocks ahead
 // (global_load_lds_dwordx4). Step t runs the S^T/dP^T MFMAs of kv block t+1 interleaved with the
 // exp2/convert work of kv block t and its K^T transposed reads (ds_read_b64_tr_b16), then the
@@ -80,8 +83,9 @@ bwd_dq_kernel(BwdParams p) {
   const int bh = item / p.nb;
   const int i = item - bh * p.nb;
   const size_t head = (size_t)bh * p.S * HEAD_DIM;
-  const bf16* __restrict__ kh = p.k + head;
-  const bf16* __restrict__ vh = p.v + head;
+  const bf16* __restrict__ kh = (const bf16*)(p.k16 + head);  // fp16 tiles (the DMA moves bytes)
+  const bf16* __restrict__ vh = (const bf16*)(p.v16 + head);
+  const int32_t* __restrict__ hs = p.scales + (size_t)bh * HEAD_SCALE_WORDS;
   const int* __restrict__ list = p.q2k_idx + (size_t)item * p.q2k_stride + start;
   auto kvblock = [&](int t) {
     const int kb = ld_const(list, t);
@@ -102,10 +106,10 @@ bwd_dq_kernel(BwdParams p) {
 
   // B operands: lane holds q row 32*wq + l32, d = 16*s + 8*g + 0..7
   const int qrow = i * BLOCK + 32 * wq + l32;
-  bf16x8 qf[8], df[8];
+  f16x8 qf[8], df[8];
   {
-    const bf16x8* qrp = (const bf16x8*)(p.q + head + (size_t)qrow * HEAD_DIM);
-    const bf16x8* drp = (const bf16x8*)(p.dout + head + (size_t)qrow * HEAD_DIM);
+    const f16x8* qrp = (const f16x8*)(p.q16 + head + (size_t)qrow * HEAD_DIM);
+    const f16x8* drp = (const f16x8*)(p.do16 + head + (size_t)qrow * HEAD_DIM);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       qf[s] = qrp[2 * s + g];
@@ -115,10 +119,12 @@ bwd_dq_kernel(BwdParams p) {
   // a q row with no valid key has lse = -inf; +inf makes its P exactly 0 (no inf * 0)
   float lse_q = p.lse[(size_t)bh * p.S + qrow];
   lse_q = lse_q == -__builtin_inff() ? __builtin_inff() : lse_q;
-  // -Delta of this q row, from the preprocess record of q block i
+  // P' = exp2(c S' + (pp - lse))
+  const float off_q = (float)ld_const(hs, SC_PP) - lse_q;
+  // -Delta' of this q row, from the preprocess record of q block i
   const float ndelta_q =
       p.lse_delta[((size_t)bh * p.nb + i) * LD_RECORD_FLOATS + BLOCK + 32 * wq + l32];
-  const float scale_log2 = p.scale_log2;
+  const float cexp = __uint_as_float((uint32_t)ld_const(hs, SC_C));
 
   // dQ^T tiles: element e of tile mt is d = 32*mt + 8*(e/4) + 4*g + e%4, q = 32*wq + l32
   f32x16 dq_acc[4];
@@ -127,13 +133,13 @@ bwd_dq_kernel(BwdParams p) {
 
   const int kvrow = 32 * wk + l32;
   // A operands of S^T = K Q^T and dP^T = V dO^T: kv row 32*wk + l32, d = 16*s + 8*g + 0..7
-  auto load_rows = [&](int st, bf16x8* ka, bf16x8* va) __attribute__((always_inline)) {
+  auto load_rows = [&](int st, f16x8* ka, f16x8* va) __attribute__((always_inline)) {
     VSA_LDS char* kt = kr + st * STAGE_BYTES;
     VSA_LDS char* vt = vr + st * STAGE_BYTES;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      ka[s] = *(const VSA_LDS bf16x8*)(kt + tile_byte(kvrow, 2 * s + g));
-      va[s] = *(const VSA_LDS bf16x8*)(vt + tile_byte(kvrow, 2 * s + g));
+      ka[s] = *(const VSA_LDS f16x8*)(kt + tile_byte(kvrow, 2 * s + g));
+      va[s] = *(const VSA_LDS f16x8*)(vt + tile_byte(kvrow, 2 * s + g));
     }
   };
 
@@ -155,7 +161,7 @@ bwd_dq_kernel(BwdParams p) {
 
   if (n > 0) {
     f32x16 s0, p0, s1, p1;
-    bf16x8 ka0[8], va0[8], ka1[8], va1[8];
+    f16x8 ka0[8], va0[8], ka1[8], va1[8];
     // vbs of the kv block in each ring stage (set when its padding is zeroed, two steps ahead)
     int vbs0 = BLOCK, vbs1 = BLOCK, vbs2 = BLOCK, vbs3 = BLOCK;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stages 0..2 landed (own DMAs)
@@ -167,8 +173,8 @@ bwd_dq_kernel(BwdParams p) {
     p0 = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      s0 = mfma32(ka0[s], qf[s], s0);
-      p0 = mfma32(va0[s], df[s], p0);
+      s0 = mfma32_f16(ka0[s], qf[s], s0);
+      p0 = mfma32_f16(va0[s], df[s], p0);
     }
     load_rows(1, ka1, va1);  // stale but in bounds when n == 1
 
@@ -176,7 +182,7 @@ bwd_dq_kernel(BwdParams p) {
     // S^T/dP^T of t are in (sc, pc) and the row operands of t+1 in (ka, va). The last steps use
     // stale (in-bounds, quiescent) stages for throwaway work, keeping the body branch-free.
     auto step = [&](int t, int st, int st2, int st3, f32x16& sc, f32x16& pc, f32x16& sn,
-                    f32x16& pn, bf16x8* ka, bf16x8* va, bf16x8* kn, bf16x8* vn, int vb_t,
+                    f32x16& pn, f16x8* ka, f16x8* va, f16x8* kn, f16x8* vn, int vb_t,
                     int& vb_ahead) __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // stage t+2 landed (own DMAs)
       barrier_lds();  // ... everyone's; everyone is done with stage st3 (kv block t-1)
@@ -187,33 +193,33 @@ bwd_dq_kernel(BwdParams p) {
       // ---- phase B: S^T/dP^T of kv block t+1; dS^T of kv block t; K^T reads of t ----
       // K^T A operand of dQ: lane holds d = 32*mt + l32, k slot jj of step s2 is kv
       // 32*wk + 16*s2 + 8*(jj/4) + 4*g + jj%4, matching the D layout of S^T
-      bf16x8 kt_op[2][4];
+      f16x8 kt_op[2][4];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int kv0 = 32 * wk + 16 * s2 + 4 * (grp >> 1) + (t16 >> 2);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int col = 32 * mt + 16 * (grp & 1) + 4 * (t16 & 3);
-          kt_op[s2][mt] = join(lds_read_tr(kt + tile_elem_byte(kv0, col)),
-                               lds_read_tr(kt + tile_elem_byte(kv0 + 8, col)));
+          kt_op[s2][mt] = join_f16(lds_read_tr(kt + tile_elem_byte(kv0, col)),
+                                   lds_read_tr(kt + tile_elem_byte(kv0 + 8, col)));
         }
       }
       sn = f32x16{};
       pn = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sn = mfma32(ka[s], qf[s], sn);
-        pn = mfma32(va[s], df[s], pn);
+        sn = mfma32_f16(ka[s], qf[s], sn);
+        pn = mfma32_f16(va[s], df[s], pn);
       }
-      // dS^T of kv block t. A padded kv row has a zero K row, so its score is 0 and its P is
-      // exp2(-lse_q): infinite once lse_q <= -128 (every valid score below about -88), and inf
+      // dS'^T of kv block t. A padded kv row has a zero K row, so its score is 0 and its P' is
+      // exp2(pp - lse_q): infinite once lse_q <= pp - 128 (every valid score far below), and inf
       // times the zero K^T row would put NaN into dQ. So a ragged block (a uniform branch, rare)
       // sets the dS^T of its padded rows to exactly 0. Element e is kv row
       // 32*wk + 8*(e/4) + 4*g + e%4.
       float dsv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(sc[e] * scale_log2 - lse_q);
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], cexp, off_q));
         dsv[e] = pe * (pc[e] + ndelta_q);
       }
       if (vb_t < BLOCK) {
@@ -221,10 +227,10 @@ bwd_dq_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e)
           dsv[e] = 32 * wk + 8 * (e >> 2) + 4 * g + (e & 3) < vb_t ? dsv[e] : 0.0f;
       }
-      bf16x8 b[2];
+      f16x8 b[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        b[s2] = pack8(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
+        b[s2] = pack8_f16(dsv[8 * s2 + 0], dsv[8 * s2 + 1], dsv[8 * s2 + 2], dsv[8 * s2 + 3],
                       dsv[8 * s2 + 4], dsv[8 * s2 + 5], dsv[8 * s2 + 6], dsv[8 * s2 + 7]);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -239,7 +245,7 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) dq_acc[mt] = mfma32(kt_op[s2][mt], b[s2], dq_acc[mt]);
+        for (int mt = 0; mt < 4; ++mt) dq_acc[mt] = mfma32_f16(kt_op[s2][mt], b[s2], dq_acc[mt]);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -279,6 +285,7 @@ bwd_dq_kernel(BwdParams p) {
                              (size_t)(32 * wq + l32) * HEAD_DIM
                        : nullptr;
   const float sc = p.sm_scale;
+  const int oexp = ld_const(hs, SC_EK) - ld_const(hs, SC_ES);  // dq = sm_scale dQ' 2^(ek - es)
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int mt = (wk == 0 ? 0 : 2) + u;  // my tiles
@@ -297,7 +304,7 @@ bwd_dq_kernel(BwdParams p) {
           s16x4 s;
         } r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r.b[e] = (bf16)(sum[e] * sc);
+        for (int e = 0; e < 4; ++e) r.b[e] = (bf16)__builtin_ldexpf(sum[e] * sc, oexp);
         *(s16x4*)(dqrow + d0) = r.s;
       } else {
         *(f32x4*)(prow + d0) = sum;

@@ -5,15 +5,16 @@
 // What it computes (the gradient of the FastVideo backward test page's masked-dense reference;
 // launch header argument struct: dq carries sm_scale): for one q block i of (b, h),
 //     dQ_i = sum over kv blocks j in its q2k list of dS_ij K_j,    dq_i = bf16(sm_scale * dQ_i)
-// with dS_ij the bf16 tile the kv-major kernel used for dK_j (so dq and dk see the same dS), kv
-// rows at or past vbs[j] excluded. A q block with an empty list gets zero rows. This is the
+// with dS_ij the tile the kv-major kernel used for dK_j (so dq and dk see the same dS), kv rows
+// at or past vbs[j] excluded. Operands are fp16: the spilled dS' = dS 2^es and the preprocess's
+// k16 = K 2^-ek, so the sum is dQ 2^(es-ek) and the epilogue scales back by 2^(ek-es). A q block with an empty list gets zero rows. This is the
 // pages' dQ accumulation and postprocess, reorganised as a per-q-block sum so that no atomics
 // and no fp32 accumulator are needed; it does one GEMM per pair instead of the three of the
 // recomputing kernel (bwd_dq.hip) and streams 8 KiB of dS per pair from HBM, which bounds it.
 //
 // gfx950 design: one 256-thread workgroup per q block, walking its slot-table row (VSA_WS_QENT:
 // dS slot, kv block and vbs per entry). Wave w computes dQ^T rows d = 32w .. 32w+31 for both q
-// halves: dQ^T += K^T dS^T with v_mfma_f32_32x32x16_bf16, four k-steps of 16 kv per pair. K_j
+// halves: dQ^T += K^T dS^T with v_mfma_f32_32x32x16_f16, four k-steps of 16 kv per pair. K_j
 // (16 KiB) and the dS tile (8 KiB) of each pair arrive by global_load_lds_dwordx4 into two LDS
 // rings of 80 KiB together, so two workgroups share a CU: dS, streamed from HBM, is fetched three
 // steps before it is read; K, mostly L2 hits, two steps before. Both operands come out of LDS
@@ -34,7 +35,7 @@ constexpr int SD = 4;
 constexpr int SK = 3;
 constexpr int UNROLL = 12;      // a multiple of SD and SK: stage offsets are constants
 static_assert(SD >= SK && SK >= 3 && UNROLL % SD == 0 && UNROLL % SK == 0 && UNROLL % 2 == 0, "");
-constexpr int K_BYTES = 16384;  // one [64][128] bf16 K tile, swizzled
+constexpr int K_BYTES = 16384;  // one [64][128] fp16 K tile, swizzled
 constexpr int S_BYTES = 8192;   // one dS tile, as the kv-major kernel stored it
 constexpr int DMA_K = 4;        // per wave per pair: four 1-KiB slices of K
 constexpr int DMA_S = 2;        // ... and two of dS
@@ -73,7 +74,7 @@ bwd_dq_spill_kernel(BwdParams p) {
       *(i32x4*)((char*)dq_blk + (c * 256 + threadIdx.x) * 16) = i32x4{};
     return;
   }
-  const bf16* __restrict__ kh_ptr = p.k + head;
+  const f16* __restrict__ kh_ptr = p.k16 + head;
   const char* __restrict__ ds_head = (const char*)p.ds + (size_t)bh * p.cap * S_BYTES;
   const int64_t* __restrict__ ent = p.qent + (size_t)item * p.qent_stride;
   auto entry = [&](int t) { return (uint64_t)ld_const(ent, t < n ? t : n - 1); };
@@ -107,8 +108,8 @@ bwd_dq_spill_kernel(BwdParams p) {
   // for q half qh: lane holds q column n = lane%32 (the record layout's order, see the epilogue)
   // and the same kv. Each is two transposed reads of four kv rows.
   struct Ops {
-    bf16x8 a[4];
-    bf16x8 b[2][4];
+    f16x8 a[4];
+    f16x8 b[2][4];
   };
   auto read_ops = [&](int sk, int sd, Ops& o) __attribute__((always_inline)) {
     VSA_LDS char* kt = (VSA_LDS char*)k_ring + sk * K_BYTES;
@@ -117,8 +118,8 @@ bwd_dq_spill_kernel(BwdParams p) {
     for (int ks = 0; ks < 4; ++ks) {
       const int k0 = 16 * ks + 8 * kh;  // first kv of this lane's k slots
       const int col = 32 * w + 16 * gc + 4 * (t16 & 3);
-      o.a[ks] = join(lds_read_tr(kt + tile_elem_byte(k0 + (t16 >> 2), col)),
-                     lds_read_tr(kt + tile_elem_byte(k0 + 4 + (t16 >> 2), col)));
+      o.a[ks] = join_f16(lds_read_tr(kt + tile_elem_byte(k0 + (t16 >> 2), col)),
+                         lds_read_tr(kt + tile_elem_byte(k0 + 4 + (t16 >> 2), col)));
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         s16x4 h2[2];
@@ -129,7 +130,7 @@ bwd_dq_spill_kernel(BwdParams p) {
                           32 * (t16 >> 2) + 8 * (t16 & 3);
           h2[u] = lds_read_tr(sb + rec);
         }
-        o.b[qh][ks] = join(h2[0], h2[1]);
+        o.b[qh][ks] = join_f16(h2[0], h2[1]);
       }
     }
   };
@@ -140,15 +141,15 @@ bwd_dq_spill_kernel(BwdParams p) {
       const int k0 = 16 * ks + 8 * kh;
       union {
         i32x4 m;
-        bf16x8 v;
+        f16x8 v;
       } mk;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         mk.m[d] = (k0 + 2 * d < vb ? 0xFFFF : 0) | (k0 + 2 * d + 1 < vb ? (int)0xFFFF0000u : 0);
-      auto andv = [&](bf16x8& x) {
+      auto andv = [&](f16x8& x) {
         union {
           i32x4 m;
-          bf16x8 v;
+          f16x8 v;
         } u;
         u.v = x;
         u.m &= mk.m;
@@ -201,8 +202,8 @@ bwd_dq_spill_kernel(BwdParams p) {
     read_ops(sk1, sd1, nxt);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      acc[0] = mfma32(cur.a[ks], cur.b[0][ks], acc[0]);
-      acc[1] = mfma32(cur.a[ks], cur.b[1][ks], acc[1]);
+      acc[0] = mfma32_f16(cur.a[ks], cur.b[0][ks], acc[0]);
+      acc[1] = mfma32_f16(cur.a[ks], cur.b[1][ks], acc[1]);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -231,13 +232,15 @@ bwd_dq_spill_kernel(BwdParams p) {
   // no DMA may still be writing this workgroup's LDS when it ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // ---- epilogue: dq = bf16(sm_scale * dQ). acc[qh] element e of this lane is d = 32w +
+  // ---- epilogue: dq = bf16(sm_scale * dQ' 2^(ek - es)). acc[qh] element e of this lane is d = 32w +
   // 8(e/4) + 4kh + e%4 and q = 32qh + q(n), n = lane%32, where the record layout puts column
   // n = 16g + c at q = 16(c/8) + 8((c%8)/4) + 4g + c%4 ----
   const int nn = lane & 31;
   const int cq = nn & 15, gq = nn >> 4;
   const int qoff = 16 * (cq >> 3) + 8 * ((cq & 7) >> 2) + 4 * gq + (cq & 3);
   const float sc = p.sm_scale;
+  const int32_t* hs = p.scales + (size_t)bh * HEAD_SCALE_WORDS;
+  const int oexp = ld_const(hs, SC_EK) - ld_const(hs, SC_ES);
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     bf16* row = dq_blk + (size_t)(32 * qh + qoff) * HEAD_DIM + 32 * w + 4 * kh;
@@ -248,7 +251,7 @@ bwd_dq_spill_kernel(BwdParams p) {
         s16x4 s;
       } r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r.b[e] = (bf16)(acc[qh][4 * c + e] * sc);
+      for (int e = 0; e < 4; ++e) r.b[e] = (bf16)__builtin_ldexpf(acc[qh][4 * c + e] * sc, oexp);
       *(s16x4*)(row + 8 * c) = r.s;
     }
   }

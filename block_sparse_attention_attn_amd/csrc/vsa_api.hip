@@ -269,6 +269,12 @@ size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride
       dq_nchunks ? align256(bh * nb * (dq_nchunks + 1) * sizeof(int32_t)) : 0,     // dq bounds
       dq_nchunks ? align256(bh * nb * (size_t)(vsa::BLOCK * vsa::HEAD_DIM) * sizeof(float))
                  : 0,                                                              // dQ
+      align256(bh * nb * vsa::STAT_WORDS * sizeof(uint32_t)),                     // block stats
+      align256(bh * vsa::HEAD_SCALE_WORDS * sizeof(int32_t)),                     // head scales
+      align256(bh * (size_t)seqlen * vsa::HEAD_DIM * 2),                          // q16
+      align256(bh * (size_t)seqlen * vsa::HEAD_DIM * 2),                          // k16
+      align256(bh * (size_t)seqlen * vsa::HEAD_DIM * 2),                          // do16
+      spill ? 0 : align256(bh * (size_t)seqlen * vsa::HEAD_DIM * 2),              // v16
   };
   size_t off = 0;
   for (int r = 0; r < region; ++r) off += sizes[r];
@@ -373,11 +379,17 @@ struct WsView {
   uint32_t* bitmap;
   int32_t* kbase;
   int64_t* qent;
-  vsa::bf16* ds;
+  vsa::f16* ds;
   int32_t* chunk_bounds;
   float* part;
   int32_t* dq_bounds;
   float* dq_part;
+  uint32_t* stats;
+  int32_t* scales;
+  vsa::f16* q16;
+  vsa::f16* k16;
+  vsa::f16* do16;
+  vsa::f16* v16;
 };
 
 WsView ws_view(const vsa_bwd_args* a) {
@@ -391,18 +403,23 @@ WsView ws_view(const vsa_bwd_args* a) {
                 (int32_t*)at(VSA_WS_Q_ORDER),  (int32_t*)at(VSA_WS_Q2K_NUM),
                 (int32_t*)at(VSA_WS_Q2K_IDX),  (uint32_t*)at(VSA_WS_BITMAP),
                 (int32_t*)at(VSA_WS_KBASE),    (int64_t*)at(VSA_WS_QENT),
-                (vsa::bf16*)at(VSA_WS_DS),     (int32_t*)at(VSA_WS_CHUNK_BOUNDS),
+                (vsa::f16*)at(VSA_WS_DS),      (int32_t*)at(VSA_WS_CHUNK_BOUNDS),
                 (float*)at(VSA_WS_DKV_PART),   (int32_t*)at(VSA_WS_DQ_BOUNDS),
-                (float*)at(VSA_WS_DQ_PART)};
+                (float*)at(VSA_WS_DQ_PART),    (uint32_t*)at(VSA_WS_STATS),
+                (int32_t*)at(VSA_WS_SCALES),   (vsa::f16*)at(VSA_WS_Q16),
+                (vsa::f16*)at(VSA_WS_K16),     (vsa::f16*)at(VSA_WS_DO16),
+                a->dq_mode == VSA_DQ_SPILL ? nullptr : (vsa::f16*)at(VSA_WS_V16)};
 }
 
 vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
   vsa::BwdParams m;
   const bool derive = a->q2k_idx == nullptr;
-  m.q = (const vsa::bf16*)a->q;
-  m.k = (const vsa::bf16*)a->k;
   m.v = (const vsa::bf16*)a->v;
-  m.dout = (const vsa::bf16*)a->dout;
+  m.q16 = ws.q16;
+  m.k16 = ws.k16;
+  m.v16 = ws.v16;
+  m.do16 = ws.do16;
+  m.scales = ws.scales;
   m.lse = a->lse;
   m.lse_delta = ws.lse_delta;
   m.k2q_idx = a->k2q_idx;
@@ -428,7 +445,6 @@ vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
   m.total_items = a->batch * a->heads * a->num_kv_blocks;
   m.items_per_xcd = (m.total_items + 7) / 8;
   m.sm_scale = a->sm_scale;
-  m.scale_log2 = scale_log2(a->sm_scale);
   const int cq = chunk_blocks_of(a->num_kv_blocks, a->chunk_blocks);
   m.nchunks = cq > 0 ? (a->num_kv_blocks + cq - 1) / cq : 0;
   m.kv_rounds = kv_rounds_of(a->batch * a->heads, cq > 0 ? cq : a->num_kv_blocks);
@@ -445,11 +461,20 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
   switch (stage) {
     case VSA_BWD_PREPROCESS: {
       vsa::BwdPreParams pre;
+      pre.q = (const vsa::bf16*)a->q;
+      pre.k = (const vsa::bf16*)a->k;
+      pre.v = (const vsa::bf16*)a->v;
       pre.o = (const vsa::bf16*)a->o;
       pre.dout = (const vsa::bf16*)a->dout;
       pre.k2q_num = a->k2q_num;
       pre.lse = a->lse;
       pre.lse_delta = ws.lse_delta;
+      pre.stats = ws.stats;
+      pre.scales = ws.scales;
+      pre.q16 = ws.q16;
+      pre.k16 = ws.k16;
+      pre.do16 = ws.do16;
+      pre.v16 = ws.v16;
       pre.dk = (vsa::bf16*)a->dk;
       pre.dv = (vsa::bf16*)a->dv;
       pre.BH = BH;

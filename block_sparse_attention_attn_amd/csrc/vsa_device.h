@@ -118,16 +118,41 @@ __device__ __forceinline__ f16x8 pack8_f16(float a0, float a1, float a2, float a
   return r;
 }
 
-// The power-of-two exponent e that brings a head's largest |value| (fp32 bits `amax_bits`, as
-// kept by an atomicMax on the bit pattern of non-negative floats) into [2^14, 2^15): an fp16 copy
-// x * 2^-e then holds every bf16 value of magnitude >= 2^-28 * max exactly (8 significant bits in
-// fp16's normal range). 0 for an all-zero head and for inf/NaN (those propagate either way).
-__device__ __forceinline__ int f16_head_exponent(uint32_t amax_bits) {
+// floor(log2(x)) - top for a non-negative fp32 value given by its bits (the largest |value| of a
+// tile or head, as an integer max over bit patterns keeps it): the power-of-two exponent e with
+// x * 2^-e in [2^top, 2^(top+1)). 0 for x = 0 and for inf/NaN (those propagate either way).
+__device__ __forceinline__ int f16_exponent(uint32_t amax_bits, int top) {
   const int ex = (int)((amax_bits >> 23) & 0xFF);
   if (ex == 255 || amax_bits == 0) return 0;
   // floor(log2(max)) for normal and subnormal fp32 values
   const int l2 = ex > 0 ? ex - 127 : -118 - __builtin_clz(amax_bits & 0x7FFFFF);
-  return l2 - 14;
+  return l2 - top;
+}
+// The exponent that brings a head's largest |value| into [2^14, 2^15): an fp16 copy x * 2^-e then
+// holds every bf16 value of magnitude >= 2^-28 * max exactly (8 significant bits in fp16's normal
+// range).
+__device__ __forceinline__ int f16_head_exponent(uint32_t amax_bits) {
+  return f16_exponent(amax_bits, 14);
+}
+// bf16 -> fp32 -> times 2^-e -> fp16 (round to nearest even): exact for values that land in fp16's
+// normal range after the scaling.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(bf16x8 x, int e) {
+  f16x8 y;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = (f16)__builtin_ldexpf((float)x[k], -e);
+  return y;
+}
+// The largest |x| of a bf16x8 as fp32 bits (sign cleared, shifted into fp32 position).
+__device__ __forceinline__ uint32_t absmax_bits8(bf16x8 x) {
+  union {
+    bf16x8 b;
+    uint32_t u[4];
+  } r;
+  r.b = x;
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = max(m, max(r.u[e] & 0x7FFFu, (r.u[e] >> 16) & 0x7FFFu));
+  return m << 16;
 }
 
 // ---------------------------------------------------------------------------------------------

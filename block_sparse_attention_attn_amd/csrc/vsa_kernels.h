@@ -50,23 +50,53 @@ void launch_fwd(const FwdParams& p, hipStream_t stream);
 void launch_v16(const bf16* v, int BH, int S, uint32_t* amax, uint32_t* tmax, f16* v16,
                 hipStream_t stream);
 
-// ---- backward preprocess: Delta, zero dK/dV rows of empty kv blocks ----
+// ---- backward preprocess: operand scaling, Delta, records, zero dK/dV rows of empty kv blocks ----
+// The backward's MFMAs run in fp16 (v_mfma_f32_32x32x16_f16, the bf16 rate): P and dS keep 11
+// significant bits instead of 8. Every operand is an fp16 copy scaled by a per-head power of two,
+// so each GEMM's sum has one exact scale per head that the epilogues take back out:
+//   q16 = q 2^-eq, k16 = k 2^-ek      (max |.| in [2^14, 2^15): exact copies of the bf16 values)
+//   v16 = v 2^-ev, do16 = dO 2^-eo    (max |.| in [1, 2))
+//   P'  = P 2^pp,  dS' = dS 2^es with es = pp - eo - ev
+// pp is the largest exponent (at most 15) with 2^pp * bound(|dP - Delta|) <= 2^15 in the scaled
+// units, so |dS'| <= |P'| |dP' - Delta'| stays inside fp16's range; the bound is
+// 1.0625 (max_i |dO_i| max_j |v_j| + max |Delta|) with row 2-norms (Cauchy-Schwarz).
+// Per head, as int32 words (c as fp32 bits):
+enum HeadScaleWord { SC_EQ = 0, SC_EK, SC_EV, SC_EO, SC_PP, SC_ES, SC_C, HEAD_SCALE_WORDS = 8 };
+// SC_C = scale_log2 * 2^(eq + ek): the base-2 softmax exponent per unit of q16 . k16.
+// Per (bh, 64-row block), fp32 bit patterns of non-negative values (integer max = value max):
+enum StatWord {
+  ST_Q = 0, ST_K, ST_V, ST_DO,  // max |x| over the block's rows
+  ST_V2, ST_DO2,                // max row |x|^2
+  ST_DELTA,                     // max |Delta|
+  STAT_WORDS = 8
+};
 // The main kernels read a q block's row statistics as one record of LD_RECORD_FLOATS floats per
-// (bh, q block): -lse / scale_log2 of its 64 rows, then -Delta of its 64 rows. The kv-major kernel
-// loads them straight into its S and dP accumulators as the initial values, so the MFMAs produce
-// S - lse/scale_log2 and dP - Delta with no per-element subtraction.
+// (bh, q block): (pp - lse) / c of its 64 rows, then -Delta 2^-(eo + ev) of its 64 rows. The
+// kv-major kernel loads them straight into its S and dP accumulators as the initial values, so
+// the MFMAs produce S' + (pp - lse) / c and dP' - Delta' with no per-element subtraction, and
+// P' = exp2(c acc).
 constexpr int LD_RECORD_FLOATS = 2 * BLOCK;
 struct BwdPreParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
   const bf16* o;
   const bf16* dout;
   const float* lse;        // [BH, S]
   const int32_t* k2q_num;  // [BH, nb]
   float* lse_delta;        // [BH * nb, LD_RECORD_FLOATS]
+  uint32_t* stats;         // [BH * nb, STAT_WORDS]
+  int32_t* scales;         // [BH, HEAD_SCALE_WORDS]
+  f16* q16;                // fp16 copies [BH, S, 128]
+  f16* k16;
+  f16* do16;
+  f16* v16;                // nullptr: not needed (only the recomputing dQ kernel reads it)
   bf16* dk;
   bf16* dv;
   int BH, S, nb;
   float scale_log2;
 };
+// Three launches: block statistics (and Delta), per-head scales, then the copies and records.
 void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream);
 
 // ---- work order: per (b, h) a length-binned permutation of its items ----
@@ -91,10 +121,12 @@ void launch_index_tasks(const IndexTasks& t, int BH, int nb, int bin_width, int 
 
 // ---- the two main backward kernels (kv-major dK/dV, q-major dQ) ----
 struct BwdParams {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  const bf16* dout;
+  const bf16* v;           // bf16 v (the kv-major kernel converts its tile in registers)
+  const f16* q16;          // the preprocess's scaled fp16 copies
+  const f16* k16;
+  const f16* v16;          // recompute mode only
+  const f16* do16;
+  const int32_t* scales;   // [BH, HEAD_SCALE_WORDS]
   const float* lse;        // [BH, S] base-2 M-form lse (the dQ kernel's)
   const float* lse_delta;  // [BH*nb, LD_RECORD_FLOATS]: the q blocks' records (see above)
   const int32_t* k2q_idx;  // [BH*nb, k2q_stride]
@@ -110,19 +142,20 @@ struct BwdParams {
   // dS spill (nullptr ds: recompute mode): slot tables from the index stage and the tiles
   const int32_t* kbase;  // [BH*nb]: first slot of each kv block's pairs inside its head
   const int64_t* qent;   // [BH*nb, qent_stride]: slot | kv << 32 | vbs[kv] << 48
-  bf16* ds;              // [BH, cap, 64*64]
+  f16* ds;               // [BH, cap, 64*64]: dS' tiles
   int cap, qent_stride;  // slots per head (nb * K'), q2k row width K'
   // q-range chunks of the kv-major kernel (nchunks 0: one launch over whole lists): this launch
   // takes list positions [bounds[item][chunk], bounds[item][chunk+1]) and carries dV, dK
   // (unscaled fp32, [item][2][64][128]) in part from chunk to chunk
-  // (defaults: one launch, so a caller that predates the chunks cannot leave them undefined)
+  // (defaults: one launch, so a caller that predates the chunks cannot leave them undefined);
+  // partial sums are in the scaled units of the fp16 operands
   const int32_t* chunk_bounds = nullptr;  // [total_items, nchunks + 1]
   float* part = nullptr;
   int chunk = 0, nchunks = 0;
   int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
   // rounds of the kv-major kernel's XCD mapping (xcd_work_id); items_per_xcd is a multiple
   int kv_rounds = 1;
-  float scale_log2, sm_scale;
+  float sm_scale;
 };
 void launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 void launch_bwd_dq(const BwdParams& p, hipStream_t stream);

@@ -113,14 +113,23 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  * block selects get exact-zero dk/dv rows, and so do kv rows at or past vbs. lse is the forward's
  * M-form log-sum-exp; o is the forward's bf16 output (Delta = rowsum(o * dout) uses it).
  *
+ * Arithmetic: every GEMM runs on fp16 operands with fp32 accumulation (v_mfma_f32_32x32x16_f16,
+ * the rate of the bf16 form). The preprocess scales each head's q and k by powers of two into
+ * [2^14, 2^15) and v and dout into [1, 2) (exact copies of the bf16 values down to 2^-28 times
+ * the head's largest one) and P, dS by powers of two chosen so that dS stays within fp16's range
+ * (a bound from the row norms of dout and v and the largest |Delta|); P and dS then carry 11
+ * significant bits instead of bf16's 8, and the epilogues take the scales back out exactly. A head
+ * whose scores q.k * sm_scale * log2 e are all far below 2^-100 (or above 2^100) in size gives up
+ * fp16 precision in its q, k copies.
+ *
  * The main step runs as two kernels without atomics: a kv-major one (one work item per
  * (b, h, kv block), walking the k2q list) for dk and dv, and a q-major one (one item per
  * (b, h, q block), walking the q2k list) for dq. All three outputs are bitwise reproducible run
  * to run, whatever the work order. The q-major kernel gets dS in one of two ways (dq_mode):
  *   VSA_DQ_RECOMPUTE  it recomputes S and dP for each pair from Q, K, V, dO, lse and Delta
- *                     (three GEMMs per pair, no extra memory);
- *   VSA_DQ_SPILL      the kv-major kernel writes every pair's dS (bf16, the same values its dK
- *                     GEMM uses) into the workspace and dq is one block-sparse GEMM dS K per
+ *                     (three GEMMs per pair; an fp16 copy of v in the workspace);
+ *   VSA_DQ_SPILL      the kv-major kernel writes every pair's dS (fp16, scaled, the same values
+ *                     its dK GEMM uses) into the workspace and dq is one block-sparse GEMM dS K per
  *                     pair, reading 8 KiB of dS per pair from HBM. This needs 8 KiB of workspace
  *                     per possible pair (B*H*nb*q2k_stride of them, nb*nb when q2k is derived)
  *                     and k2q rows in ascending order (as vsa_invert_indices writes them); it
@@ -144,9 +153,10 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  * Workspace (device, vsa_bwd_workspace_bytes() bytes, contents on entry irrelevant), regions in
  * this order, each at a 256-byte boundary (vsa_bwd_workspace_offset() gives the offsets); a
  * region the call does not use has size 0. K' below is q2k_stride, or nb when q2k is derived.
- *   VSA_WS_LSE_DELTA fp32 [B, H, nb, 2, 64]: per q block, -lse / scale_log2 of its 64 rows
- *                    (scale_log2 = fp32(sm_scale * log2 e)), then -Delta of its 64 rows; left
- *                    holding them after the call
+ *   VSA_WS_LSE_DELTA fp32 [B, H, nb, 2, 64]: per q block, (pp - lse) / c of its 64 rows (fp32
+ *                    subtraction, then division), then -Delta * 2^-(eo + ev) of its 64 rows,
+ *                    with the head's pp, c, eo, ev from VSA_WS_SCALES; left holding them after
+ *                    the call
  *   VSA_WS_KV_ORDER  int32 [B*H*nb] kv-major work order (when the library computes it)
  *   VSA_WS_Q_ORDER   int32 [B*H*nb] q-major work order (when the library computes it)
  * only when the q2k lists are derived (q2k_stride argument 0):
@@ -158,7 +168,7 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *                    (exclusive prefix sum of k2q_num inside the head)
  *   VSA_WS_QENT      int64 [B, H, nb, K']: per q2k entry, its dS slot | kv block << 32 |
  *                    vbs[kv block] << 48
- *   VSA_WS_DS        bf16 [B, H, nb*K', 64, 64]: the dS tiles, slot-major
+ *   VSA_WS_DS        fp16 [B, H, nb*K', 64, 64]: the dS tiles (dS * 2^es), slot-major
  * only when the main kernels run in chunks (below), with C chunks:
  *   VSA_WS_CHUNK_BOUNDS int32 [B*H*nb, C+1]: per kv item, the position in its k2q list of the
  *                    first q block of each chunk (the last entry is the list length)
@@ -168,6 +178,16 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *                    (VSA_DQ_RECOMPUTE mode with chunk_blocks > 0)
  *   VSA_WS_DQ_PART   fp32 [B*H*nb, 64, 128]: per q item, dQ (unscaled) summed over the chunks so
  *                    far (VSA_DQ_RECOMPUTE mode with chunk_blocks > 0)
+ * always (the partial sums above are in the scaled units these define):
+ *   VSA_WS_STATS     uint32 [B, H, nb, 8]: per 64-row block, fp32 bit patterns of max |q|, max |k|,
+ *                    max |v|, max |dout|, max row |v|^2, max row |dout|^2, max |Delta|, 0
+ *   VSA_WS_SCALES    int32 [B, H, 8]: per head eq, ek, ev, eo, pp, es = pp - eo - ev, c (fp32 bits)
+ *                    = fp32(sm_scale * log2 e) * 2^(eq + ek), 0. The fp16 operands are
+ *                    q * 2^-eq, k * 2^-ek, v * 2^-ev, dout * 2^-eo, P * 2^pp and dS * 2^es
+ *   VSA_WS_Q16       fp16 [B, H, S, 128]: q * 2^-eq
+ *   VSA_WS_K16       fp16 [B, H, S, 128]: k * 2^-ek
+ *   VSA_WS_DO16      fp16 [B, H, S, 128]: dout * 2^-eo
+ *   VSA_WS_V16       fp16 [B, H, S, 128]: v * 2^-ev (VSA_DQ_RECOMPUTE mode only)
  *
  * Chunks (chunk_blocks argument; 0 = the library's choice): with R = chunk_blocks (> 0) each
  * main kernel runs as C = ceil(nb / R) launches; with 0, the kv-major kernel alone does, with
@@ -203,7 +223,13 @@ typedef enum {
   VSA_WS_DKV_PART = 10,
   VSA_WS_DQ_BOUNDS = 11,
   VSA_WS_DQ_PART = 12,
-  VSA_WS_END = 13
+  VSA_WS_STATS = 13,
+  VSA_WS_SCALES = 14,
+  VSA_WS_Q16 = 15,
+  VSA_WS_K16 = 16,
+  VSA_WS_DO16 = 17,
+  VSA_WS_V16 = 18,
+  VSA_WS_END = 19
 } vsa_bwd_ws_region;
 
 typedef enum { VSA_DQ_RECOMPUTE = 0, VSA_DQ_SPILL = 1 } vsa_dq_mode;
@@ -255,7 +281,8 @@ int vsa_bwd(const vsa_bwd_args* a, void* stream);
  * what PREPROCESS and INDEX wrote and may run in either order; in VSA_DQ_SPILL mode DQ reads the
  * dS tiles DKDV writes and must follow it. */
 typedef enum {
-  VSA_BWD_PREPROCESS = 0,  /* Delta; zero dk/dv rows of kv blocks with an empty k2q list */
+  VSA_BWD_PREPROCESS = 0,  /* operand scales and fp16 copies, Delta, the records; zero dk/dv
+                              rows of kv blocks with an empty k2q list */
   VSA_BWD_INDEX = 1,       /* q2k derivation (if needed), the length-binned work orders, in
                               VSA_DQ_SPILL mode the dS slot tables, with q-range chunks the
                               chunk bounds */

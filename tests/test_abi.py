@@ -67,6 +67,17 @@ def test_status_strings():
     assert b"unknown" in L.vsa_status_string(42)
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def _tail(B, H, S, spill):
+    """Bytes of the regions every backward uses after the mode- and chunk-dependent ones: block
+    statistics, head scales, the fp16 copies of q, k, dO (and v in recompute mode)."""
+    copy = _a256(B * H * S * 128 * 2)
+    return _a256(B * H * (S // 64) * 8 * 4) + _a256(B * H * 8 * 4) + (3 if spill else 4) * copy
+
+
 def test_workspace_sizes_and_layout():
     B, H, S = 1, 8, 32768
     nb = S // 64
@@ -79,21 +90,30 @@ def test_workspace_sizes_and_layout():
     assert offs[V.WS_Q2K_IDX] == offs[V.WS_Q2K_NUM] + B * H * nb * 4
     assert offs[V.WS_BITMAP] == offs[V.WS_Q2K_IDX] + B * H * nb * nb * 4
     assert offs[V.WS_KBASE] == offs[V.WS_BITMAP] + B * H * nb * ((nb + 31) // 32) * 4
-    assert offs[V.WS_KBASE] == offs[V.WS_QENT] == offs[V.WS_DS] == offs[V.WS_END]
+    assert offs[V.WS_KBASE] == offs[V.WS_QENT] == offs[V.WS_DS] == offs[V.WS_STATS]
+    assert offs[V.WS_SCALES] == offs[V.WS_STATS] + B * H * nb * 8 * 4
+    assert offs[V.WS_Q16] == offs[V.WS_SCALES] + 256
+    assert offs[V.WS_K16] == offs[V.WS_Q16] + B * H * S * 128 * 2
+    assert offs[V.WS_DO16] == offs[V.WS_K16] + B * H * S * 128 * 2
+    assert offs[V.WS_V16] == offs[V.WS_DO16] + B * H * S * 128 * 2
+    assert offs[V.WS_END] == offs[V.WS_V16] + B * H * S * 128 * 2
+    assert offs[V.WS_END] - offs[V.WS_STATS] == _tail(B, H, S, False)
     assert V.bwd_workspace_bytes(B, H, S) == offs[V.WS_END]
     # given q2k lists (row width 128): no derivation regions
     given = [V.bwd_workspace_offset(B, H, S, r, 128) for r in range(V.WS_END + 1)]
-    assert given[V.WS_Q2K_NUM] == given[V.WS_END] == offs[V.WS_Q2K_NUM]
-    assert V.bwd_workspace_bytes(B, H, S, 128) == offs[V.WS_Q2K_NUM]
+    assert given[V.WS_Q2K_NUM] == given[V.WS_STATS] == offs[V.WS_Q2K_NUM]
+    assert V.bwd_workspace_bytes(B, H, S, 128) == offs[V.WS_Q2K_NUM] + _tail(B, H, S, False)
     # spill mode: slot bases, the slot table and one 8 KiB dS tile per possible pair
     sp = [V.bwd_workspace_offset(B, H, S, r, 128, V.DQ_SPILL) for r in range(V.WS_END + 1)]
     assert sp[V.WS_KBASE] == offs[V.WS_Q2K_NUM]
     assert sp[V.WS_QENT] == sp[V.WS_KBASE] + B * H * nb * 4
     assert sp[V.WS_DS] == sp[V.WS_QENT] + B * H * nb * 128 * 8
-    assert sp[V.WS_END] == sp[V.WS_DS] + B * H * nb * 128 * 64 * 64 * 2
+    assert sp[V.WS_STATS] == sp[V.WS_DS] + B * H * nb * 128 * 64 * 64 * 2
+    assert sp[V.WS_END] - sp[V.WS_STATS] == _tail(B, H, S, True)  # no fp16 copy of v
+    assert sp[V.WS_V16] == sp[V.WS_END]
     # derived q2k in spill mode: row width nb for the slot table and tiles
     spd = [V.bwd_workspace_offset(1, 2, 64 * 5, r, 0, V.DQ_SPILL) for r in range(V.WS_END + 1)]
-    assert spd[V.WS_END] - spd[V.WS_DS] == 2 * 5 * 5 * 8192
+    assert spd[V.WS_STATS] - spd[V.WS_DS] == 2 * 5 * 5 * 8192
     # every region starts on a 256-byte boundary, also for odd sizes
     for kq in (0, 3):
         for mode in (V.DQ_RECOMPUTE, V.DQ_SPILL):
@@ -110,28 +130,29 @@ def test_workspace_chunk_regions():
     a256 = lambda x: (x + 255) // 256 * 256
     # below the default threshold: no chunk regions
     o = offs(1, 8, 64 * 512, 128, 0)
-    assert o[V.WS_CHUNK_BOUNDS] == o[V.WS_DKV_PART] == o[V.WS_END] == o[V.WS_DS]
+    assert o[V.WS_CHUNK_BOUNDS] == o[V.WS_DKV_PART] == o[V.WS_STATS] == o[V.WS_DS]
     # from the threshold on, chunks of CHUNK_BLOCKS q blocks for the kv-major kernel: bounds and
     # fp32 dV/dK sums; the q-major kernel's chunks only on request
     nb = V.CHUNK_MIN_KV_BLOCKS
     o = offs(1, 2, 64 * nb, 128, 0)
     c = -(-nb // V.CHUNK_BLOCKS)
     assert o[V.WS_DKV_PART] - o[V.WS_CHUNK_BOUNDS] == a256(2 * nb * (c + 1) * 4)
-    assert o[V.WS_END] == o[V.WS_DQ_BOUNDS] == o[V.WS_DKV_PART] + 2 * nb * 2 * 64 * 128 * 4
-    assert V.bwd_workspace_bytes(1, 2, 64 * nb, 128, V.DQ_RECOMPUTE, -1) == o[V.WS_CHUNK_BOUNDS]
+    assert o[V.WS_STATS] == o[V.WS_DQ_BOUNDS] == o[V.WS_DKV_PART] + 2 * nb * 2 * 64 * 128 * 4
+    assert V.bwd_workspace_bytes(1, 2, 64 * nb, 128, V.DQ_RECOMPUTE, -1) == (
+        o[V.WS_CHUNK_BOUNDS] + _tail(1, 2, 64 * nb, False))
     o = offs(1, 2, 64 * nb, 128, V.CHUNK_BLOCKS)  # requested: both kernels
     assert o[V.WS_DQ_PART] - o[V.WS_DQ_BOUNDS] == a256(2 * nb * (c + 1) * 4)
-    assert o[V.WS_END] - o[V.WS_DQ_PART] == 2 * nb * 64 * 128 * 4
+    assert o[V.WS_STATS] - o[V.WS_DQ_PART] == 2 * nb * 64 * 128 * 4
     # the dS-reading q-major kernel runs as one launch: no dQ chunk regions in spill mode
     sp = [V.bwd_workspace_offset(1, 2, 64 * nb, r, 128, V.DQ_SPILL, 0) for r in range(V.WS_END + 1)]
-    assert sp[V.WS_DQ_BOUNDS] == sp[V.WS_END] == sp[V.WS_DKV_PART] + 2 * nb * 2 * 64 * 128 * 4
+    assert sp[V.WS_DQ_BOUNDS] == sp[V.WS_STATS] == sp[V.WS_DKV_PART] + 2 * nb * 2 * 64 * 128 * 4
     # a forced chunk size at any size; one chunk covering every block is no chunk
     o = offs(1, 1, 64 * 10, 0, 3)
     assert o[V.WS_DKV_PART] - o[V.WS_CHUNK_BOUNDS] == a256(10 * 5 * 4)
     assert o[V.WS_DQ_BOUNDS] - o[V.WS_DKV_PART] == 10 * 2 * 64 * 128 * 4
-    assert o[V.WS_END] - o[V.WS_DQ_PART] == 10 * 64 * 128 * 4
+    assert o[V.WS_STATS] - o[V.WS_DQ_PART] == 10 * 64 * 128 * 4
     o = offs(1, 1, 64 * 10, 0, 10)
-    assert o[V.WS_END] == o[V.WS_CHUNK_BOUNDS]
+    assert o[V.WS_STATS] == o[V.WS_CHUNK_BOUNDS]
     # the forward: per-head max |v| bits and the fp16 copy of v, then with kv-range chunks the
     # bounds and per-wave state of 66 x 64 floats
     def v16(bh, S):

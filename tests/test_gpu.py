@@ -58,7 +58,13 @@ def nan_like(t):
 
 
 def check_close(name, got, ref, report=None):
-    """got: GPU tensor (any float dtype); ref: float64 numpy array of the same shape."""
+    """got: GPU tensor (any float dtype); ref: float64 numpy array of the same shape.
+
+    Three gates on every tensor: max|diff|/max|ref| <= 1e-2; mean|diff| <= 1e-3 mean|ref| plus
+    the mean error of rounding the exact result to bf16 (which no bf16 output can avoid); and the
+    strict form of the mean bound, measured against the bf16-rounded exact result:
+    mean|got - bf16(ref)| <= 1e-3 mean|ref|.
+    """
     g = got.detach().to("cpu", torch.float64).numpy()
     assert g.shape == ref.shape, f"{name}: shape {g.shape} vs {ref.shape}"
     assert np.isfinite(g).all(), f"{name}: non-finite values"
@@ -67,10 +73,12 @@ def check_close(name, got, ref, report=None):
     mean_ref = np.abs(ref).mean()
     rel_max = diff.max() / max_ref
     mean_abs = diff.mean()
-    rounding = np.abs(O.bf16_rne(ref) - ref).mean()
+    rounded = O.bf16_rne(ref)
+    rounding = np.abs(rounded - ref).mean()
+    strict = np.abs(g - rounded).mean()
     line = dict(tensor=name, rel_max=float(rel_max), mean_abs=float(mean_abs),
                 mean_ref=float(mean_ref), mean_rel=float(mean_abs / max(mean_ref, 1e-30)),
-                mean_rel_vs_bf16_ref=float(np.abs(g - O.bf16_rne(ref)).mean() / max(mean_ref, 1e-30)),
+                mean_rel_vs_bf16_ref=float(strict / max(mean_ref, 1e-30)),
                 page_abs_mean_ok=bool(mean_abs <= 1e-3))
     say("  " + json.dumps(line))
     if report is not None:
@@ -79,6 +87,8 @@ def check_close(name, got, ref, report=None):
     assert mean_abs <= MEAN_REL_TOL * mean_ref + rounding, (
         f"{name}: mean|diff| = {mean_abs:.3e} > 1e-3*mean|ref| ({mean_ref:.3e}) + bf16 rounding "
         f"{rounding:.3e}")
+    assert strict <= MEAN_REL_TOL * mean_ref, (
+        f"{name}: mean|got - bf16(ref)| = {strict:.3e} > 1e-3*mean|ref| ({mean_ref:.3e})")
 
 
 # -----------------------------------------------------------------------------------------------
@@ -303,17 +313,47 @@ def _bwd_small(c, label, mode=V.DQ_RECOMPUTE):
     for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
         assert got.dtype == torch.bfloat16
         check_close(name, got, ref)
-    # Delta from the preprocess (the records hold -Delta), on the bf16 o it was given
+    sc = _check_scales(c, plan, o)
+    # Delta from the preprocess (the records hold -Delta 2^-(eo + ev)), on the bf16 o it was given
     rdelta = O.delta(o.cpu(), c.do)
-    gd = -plan.lse_delta()[:, :, :, 1, :].reshape(c.B, c.H, c.S).cpu().double().numpy()
+    shift = 2.0 ** (sc[..., V.SC_EO] + sc[..., V.SC_EV]).double().numpy()[..., None]
+    gd = -plan.lse_delta()[:, :, :, 1, :].reshape(c.B, c.H, c.S).cpu().double().numpy() * shift
     assert np.abs(gd - rdelta).max() <= 1e-5 * max(1.0, np.abs(rdelta).max())
-    # the records also carry -lse / scale_log2 with scale_log2 = fp32(sm_scale * log2 e), divided
-    # in IEEE fp32 (torch's division rounds the same way)
+    # the records also carry (pp - lse) / c, subtracted and divided in IEEE fp32 (torch rounds
+    # the same way)
     glse = plan.lse_delta()[:, :, :, 0, :].reshape(c.B, c.H, c.S)
+    pp = sc[..., V.SC_PP].float()[..., None]
+    cc = sc[..., V.SC_C].contiguous().view(torch.float32)[..., None]
+    assert torch.equal(glse.cpu(), (pp - lse.cpu()) / cc)
+    return dq, dk, dv, rdq, rdk, rdv
+
+
+def _check_scales(c, plan, o):
+    """The preprocess's per-head exponents against the inputs (vsa.h, VSA_WS_SCALES): q, k
+    copies with max |.| in [2^14, 2^15), v, dO in [1, 2), c = fp32(sm_scale log2 e) 2^(eq + ek),
+    es = pp - eo - ev, and pp the largest exponent <= 15 with 2^pp times the bound on
+    |dP - Delta| (row norms, largest |Delta|, margin 1.0625) in the scaled units at most 2^15."""
+    sc = plan.scales().cpu()
+    q, k, v, do = (t.double().numpy() for t in (c.q, c.k, c.v, c.do))
+    delta = O.delta(o.cpu(), c.do)
     c2 = (torch.tensor(c.sm_scale, dtype=torch.float32)
           * torch.tensor(1.4426950408889634, dtype=torch.float32))
-    assert torch.equal(glse.cpu(), -(lse.cpu() / c2))
-    return dq, dk, dv, rdq, rdk, rdv
+    for b in range(c.B):
+        for h in range(c.H):
+            w = [int(x) for x in sc[b, h]]
+            eq, ek, ev, eo, pp, es = w[:6]
+            for x, e, lo in ((q, eq, 2.0 ** 14), (k, ek, 2.0 ** 14), (v, ev, 1.0), (do, eo, 1.0)):
+                m = np.abs(x[b, h]).max() * 2.0 ** -e
+                assert lo <= m < 2 * lo, (b, h, w)
+            assert es == pp - eo - ev
+            assert sc[b, h, V.SC_C:V.SC_C + 1].view(torch.float32).item() == (
+                c2 * 2.0 ** (eq + ek)).item()
+            nv = np.sqrt((v[b, h] ** 2).sum(-1)).max() * 2.0 ** -ev
+            no = np.sqrt((do[b, h] ** 2).sum(-1)).max() * 2.0 ** -eo
+            bound = 1.0625 * (no * nv + np.abs(delta[b, h]).max() * 2.0 ** -(eo + ev))
+            assert 2.0 ** pp * bound <= 2.0 ** 15 * (1 + 1e-5), (b, h, w, bound)
+            assert pp == 15 or 2.0 ** (pp + 1) * bound > 2.0 ** 15 * (1 - 1e-5), (b, h, w, bound)
+    return sc
 
 
 @pytest.mark.parametrize("mode", sorted(MODES))
