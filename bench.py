@@ -25,7 +25,8 @@ The headline workload is B=1 H=8 S=32768 D=128, 25 % density (default); --worklo
 S=65536 at 12.5 % density. The line also carries, under `secondary`, the other headline workload
 and the 524288-token workload (recompute dQ mode, 2 steps after 1 warm-up; --no-524k skips it).
 `api_backward_ms` times the public V.backward() on its defaults (inverting q2k, default dQ mode,
-outputs and workspace from torch's caching allocator), i.e. invert + backward chain.
+outputs and workspace from torch's caching allocator), i.e. invert + backward chain, each call
+right after a forward as in a step.
 --workload 5 times the 524288-token case alone (recompute dQ mode; use few steps, e.g. --steps 3
 --warmup 1: a step is a few seconds).
 Only one GPU is used: --gpus above 1 exits with a message.
@@ -169,17 +170,22 @@ def run_workload(n, steps, warmup, dq_mode, api_steps=0):
     torch.cuda.empty_cache()
     if api_steps:
         # the public entry a caller uses, on its defaults: inverts q2k, picks the dQ mode
-        # (default_dq_mode) and allocates outputs and workspace through torch's caching allocator
+        # (default_dq_mode) and allocates outputs and workspace through torch's caching
+        # allocator. Each call follows a forward, as the backward chain does in a step, and the
+        # events bracket the call alone (its inversion included).
         for _ in range(2):
             V.backward(do, q, k, v, o, lse, idx, num, vbs)
         torch.cuda.synchronize()
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record()
+        api = []
         for _ in range(api_steps):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            V.forward(q, k, v, idx, num, vbs, out=(o, lse))
+            a0.record()
             V.backward(do, q, k, v, o, lse, idx, num, vbs)
-        a1.record()
+            a1.record()
+            api.append((a0, a1))
         torch.cuda.synchronize()
-        res["api_backward_ms"] = a0.elapsed_time(a1) / api_steps
+        res["api_backward_ms"] = statistics.mean(a0.elapsed_time(a1) for a0, a1 in api)
         res["api_dq_mode"] = "spill" if V.default_dq_mode(c.B, c.H, c.S, idx.shape[-1]) == V.DQ_SPILL \
             else "recompute"
         torch.cuda.empty_cache()
