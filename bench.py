@@ -23,12 +23,14 @@ bracketed by HIP events on the stream it runs on (torch's current stream, which 
 
 The headline workload is B=1 H=8 S=32768 D=128, 25 % density (default); --workload 4 selects
 S=65536 at 12.5 % density. The line also carries, under `secondary`, the other headline workload
-and the 524288-token workload (recompute dQ mode, 2 steps after 1 warm-up; --no-524k skips it).
+and the 524288-token workload (the library's default dQ mode, 2 steps after 1 warm-up; --no-524k
+skips it).
 `api_backward_ms` times the public V.backward() on its defaults (inverting q2k, default dQ mode,
 outputs and workspace from torch's caching allocator), i.e. invert + backward chain, each call
 right after a forward as in a step.
---workload 5 times the 524288-token case alone (recompute dQ mode; use few steps, e.g. --steps 3
---warmup 1: a step is a few seconds).
+--workload 5 times the 524288-token case alone (the library's default dQ mode unless --dq-mode
+says otherwise; use few steps, e.g. --steps 3 --warmup 1: a step is a few seconds).
+--chunk-blocks sets the backward's chunk width (with the spill: one chunk's dS tiles at a time).
 Only one GPU is used: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -55,8 +57,10 @@ WORKLOAD_TEXT = {
        "(top-k 128 of 1024 kv blocks per q block), all blocks full, device work order",
     5: "VSA 64-token block-sparse attention backward, B=1 H=8 S=524288 D=128 bf16, 25% density "
        "(top-k 2048 of 8192 kv blocks per q block), last kv block 40 valid tokens, inputs "
-       "0.5*N(0,1), dq recomputed (the dS tiles would need 1 TiB)",
+       "0.5*N(0,1)",
 }
+# (batch, heads, seqlen, q2k row width) of the 524288-token workload, for the default dQ mode
+WORKLOAD_SHAPE = {5: (1, 8, 524288, 2048)}
 
 
 PROFILE = {3: "profiles/backward_S32768_H8_topk128of512.md"}
@@ -91,7 +95,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_workload(n, steps, warmup, dq_mode, api_steps=0):
+def run_workload(n, steps, warmup, dq_mode, api_steps=0, chunk_blocks=0):
     import torch
 
     import block_sparse_attention_attn_amd as V
@@ -110,7 +114,7 @@ def run_workload(n, steps, warmup, dq_mode, api_steps=0):
     inv_ws = torch.empty(V.invert_workspace_bytes(c.B, c.H, c.nb, c.nb), dtype=torch.uint8,
                          device=dev)
     plan = V.BwdPlan(do, q, k, v, o, lse, k2q_idx, k2q_num, vbs, q2k_idx=idx, q2k_num=num,
-                     dq_mode=dq_mode)
+                     dq_mode=dq_mode, chunk_blocks=chunk_blocks)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -161,10 +165,18 @@ def run_workload(n, steps, warmup, dq_mode, api_steps=0):
     # executed MFMA work: 4 GEMMs per pair in the dK/dV kernel; 3 in the recomputing dQ kernel,
     # 1 in the spill one, which reads 8 KiB of dS per pair from HBM
     spill = dq_mode == V.DQ_SPILL
-    res["dkdv_tflops"] = pairs * 4 * GEMM_FLOP / (res["dkdv_ms"] * 1e-3) / 1e12
-    res["dq_tflops"] = pairs * (1 if spill else 3) * GEMM_FLOP / (res["dq_ms"] * 1e-3) / 1e12
-    if spill:
-        res["dq_ds_read_GBps"] = pairs * 8192 / (res["dq_ms"] * 1e-3) / 1e9
+    # a chunked spill (spill mode whose kv-major kernel runs in chunks) runs the dQ launches inside
+    # the DKDV stage, after each chunk's kv-major launch: dkdv_ms then covers both kernels
+    cb = chunk_blocks if chunk_blocks != 0 else (V.CHUNK_BLOCKS if c.nb >= V.CHUNK_MIN_KV_BLOCKS
+                                                 else 0)
+    res["dq_in_dkdv_stage"] = spill and 0 < cb < c.nb
+    if res["dq_in_dkdv_stage"]:
+        res["dkdv_dq_tflops"] = pairs * 5 * GEMM_FLOP / (res["dkdv_ms"] * 1e-3) / 1e12
+    else:
+        res["dkdv_tflops"] = pairs * 4 * GEMM_FLOP / (res["dkdv_ms"] * 1e-3) / 1e12
+        res["dq_tflops"] = pairs * (1 if spill else 3) * GEMM_FLOP / (res["dq_ms"] * 1e-3) / 1e12
+        if spill:
+            res["dq_ds_read_GBps"] = pairs * 8192 / (res["dq_ms"] * 1e-3) / 1e9
     res["fwd_tflops"] = pairs * 2 * GEMM_FLOP / (res["fwd_ms"] * 1e-3) / 1e12
     del plan
     torch.cuda.empty_cache()
@@ -234,9 +246,13 @@ def main():
     ap.add_argument("--no-524k", action="store_true",
                     help="skip the 524288-token secondary leg (about a minute, mostly input "
                          "generation)")
-    ap.add_argument("--dq-mode", choices=("spill", "recompute"), default="spill",
+    ap.add_argument("--dq-mode", choices=("spill", "recompute"), default=None,
                     help="dQ from dS tiles the dK/dV kernel spills to the workspace (8 KiB per "
-                         "pair), or recomputed from Q, K, V, dO")
+                         "pair), or recomputed from Q, K, V, dO; default: spill, and for "
+                         "--workload 5 the library's default_dq_mode")
+    ap.add_argument("--chunk-blocks", type=int, default=0,
+                    help="the backward's chunk_blocks (0: the library's choice, < 0: no chunks); "
+                         "with chunks the spill holds one chunk's dS tiles")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (a known byte count for "
                          "scaling hardware traffic counters)")
@@ -260,12 +276,17 @@ def main():
         del src, dst
     log(f"[bench] workload {args.workload}: steps={args.steps} warmup={args.warmup}")
     import block_sparse_attention_attn_amd as V
-    if args.workload == 5 and args.dq_mode == "spill":
-        log("[bench] workload 5: the dS tiles would need 1 TiB of workspace; dq is recomputed")
-        args.dq_mode = "recompute"
-    mode = V.DQ_SPILL if args.dq_mode == "spill" else V.DQ_RECOMPUTE
+    if args.dq_mode is None:
+        if args.workload == 5:
+            c5 = WORKLOAD_SHAPE[5]
+            mode = V.default_dq_mode(*c5, chunk_blocks=args.chunk_blocks, device="cuda:0")
+        else:
+            mode = V.DQ_SPILL
+    else:
+        mode = V.DQ_SPILL if args.dq_mode == "spill" else V.DQ_RECOMPUTE
     res, case = run_workload(args.workload, args.steps, args.warmup, mode,
-                             api_steps=10 if args.workload != 5 else 0)
+                             api_steps=10 if args.workload != 5 else 0,
+                             chunk_blocks=args.chunk_blocks)
     log(f"[bench] {json.dumps(res)}")
     secondary = None
     if not args.no_secondary and args.workload != 5:
@@ -275,9 +296,11 @@ def main():
             others.append(5)
         for other in others:
             log(f"[bench] secondary workload {other}")
-            if other == 5:  # a step takes about 1.6 s; the dS tiles would need 1 TiB
-                r2, _ = run_workload(5, 2, 1, V.DQ_RECOMPUTE)
+            if other == 5:  # a step takes about 1.6 s; the library's default dQ mode
+                mode2 = V.default_dq_mode(*WORKLOAD_SHAPE[5], device="cuda:0")
+                r2, _ = run_workload(5, 2, 1, mode2)
             else:
+                mode2 = mode
                 r2, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2), mode)
             log(f"[bench] {json.dumps(r2)}")
             secondary.append(dict(
@@ -285,6 +308,7 @@ def main():
                 bwd_tflops=round(r2["bwd_tflops"], 2), bwd_ms=round(r2["bwd_ms"], 4),
                 fwd_ms=round(r2["fwd_ms"], 4), dkdv_ms=round(r2["dkdv_ms"], 4),
                 dq_ms=round(r2["dq_ms"], 4),
+                dq_mode="spill" if mode2 == V.DQ_SPILL else "recompute",
                 frac_of_peak=round(r2["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)))
     cpu = None
     if not args.no_cpu_baseline:
@@ -292,7 +316,8 @@ def main():
         cpu = cpu_baseline(case)
         log(f"[bench] cpu {json.dumps(cpu)}")
 
-    achieved = res["dkdv_tflops"]
+    # the dominant kernel; with a chunked spill its stage also holds the dQ launches
+    achieved = res["dkdv_tflops"] if "dkdv_tflops" in res else res["dkdv_dq_tflops"]
     line = {
         "metric": METRIC,
         "value": round(res["bwd_tflops"], 2),
@@ -313,7 +338,8 @@ def main():
             "heads": case.H,
             "head_dim": 128,
             "selected_pairs": res["pairs"],
-            "dq_mode": args.dq_mode,
+            "dq_mode": "spill" if mode == V.DQ_SPILL else "recompute",
+            "chunk_blocks": args.chunk_blocks,
             "parallelism": "none (1 GPU)",
         },
         "frac_of_peak": round(res["bwd_tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -322,7 +348,8 @@ def main():
         "api_backward_ms": round(res["api_backward_ms"], 4) if "api_backward_ms" in res else None,
         "api_dq_mode": res.get("api_dq_mode"),
         "roofline": {
-            "kernel": "bwd_dkdv_kernel",
+            "kernel": "bwd_dkdv_kernel" if "dkdv_tflops" in res
+                      else "bwd_dkdv_kernel + bwd_dq_spill_kernel (chunked spill, 5 GEMMs)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "ORDER_BIN_WIDTH", "CHUNK_MIN_KV_BLOCKS",
-    "CHUNK_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
+    "CHUNK_BLOCKS", "SPILL_CHUNK_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
     "DQ_RECOMPUTE", "DQ_SPILL", "default_dq_mode", "backward_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -38,6 +38,7 @@ ORDER_MIN_KV_BLOCKS = 64   # VSA_ORDER_MIN_KV_BLOCKS
 ORDER_BIN_WIDTH = 4        # VSA_ORDER_BIN_WIDTH
 CHUNK_MIN_KV_BLOCKS = 4096  # VSA_CHUNK_MIN_KV_BLOCKS
 CHUNK_BLOCKS = 1024       # VSA_CHUNK_BLOCKS
+SPILL_CHUNK_BLOCKS = 512  # VSA_SPILL_CHUNK_BLOCKS
 FWD_CHUNK_KV_BLOCKS = 512   # VSA_FWD_CHUNK_KV_BLOCKS
 ORDER_MAX_KV_BLOCKS = 16384
 _LOG2E = 1.4426950408889634
@@ -322,19 +323,20 @@ def default_dq_mode(batch: int, heads: int, seqlen: int, q2k_stride: int = 0,
     """The dQ mode a backward call uses when the caller names none: DQ_SPILL (dQ from the dS
     tiles the kv-major kernel writes: one GEMM per pair, the faster mode) when its workspace --
     8 KiB per possible pair, B*H*nb*K tiles for q2k rows of width K (nb when the library derives
-    them) plus the slot tables -- takes at most 1/8 of the device's memory and the spill's size
+    them; with chunks of R q blocks, B*H*R*K: the spill then holds one chunk's tiles) plus the
+    slot tables and the rest -- takes at most 1/3 of the device's memory and the spill's size
     limits hold (at most 65535 kv blocks, nb*K below 2^31); DQ_RECOMPUTE otherwise. The choice
     depends only on the shape and the device (not on the memory free at the time), so a given
     call always runs the same kernels and gives the same bits. On MI355X (288 GB): 32768 tokens
-    with top-k 128 spill into 4 GiB, 65536 tokens into 8 GiB; 524288 tokens with top-k 2048 would
-    need 1 TiB and recompute."""
+    with top-k 128 spill into 4 GiB, 65536 tokens into 8 GiB, 524288 tokens with top-k 2048
+    (B*H = 8) into 72 GiB in chunks of SPILL_CHUNK_BLOCKS (the whole spill would need 1 TiB)."""
     nb = seqlen // BLOCK
     kq = q2k_stride if q2k_stride > 0 else nb
     if nb > 65535 or nb * kq >= 1 << 31:
         return DQ_RECOMPUTE
     need = bwd_workspace_bytes(batch, heads, seqlen, q2k_stride, DQ_SPILL, chunk_blocks)
     total = _total_memory(device)
-    return DQ_SPILL if need <= total // 8 else DQ_RECOMPUTE
+    return DQ_SPILL if 0 < need <= total // 3 else DQ_RECOMPUTE
 
 
 _TOTAL_MEMORY = {}

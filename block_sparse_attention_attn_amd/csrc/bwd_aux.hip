@@ -238,21 +238,16 @@ __device__ void order_block(const int32_t* __restrict__ num_in, int nb, int bin_
     order[(size_t)bh * nb + r] = bh * nb + (int)(keys[r] & 0x3FFFu);
 }
 
-// dS slot bases of one head (one 1024-thread workgroup): exclusive prefix sum of the clamped k2q
-// counts. Thread t sums a contiguous chunk of ceil(nb / 1024) counts, the 1024 chunk sums are
-// scanned in LDS, and each thread writes its chunk's prefixes.
-__device__ void kbase_block(const int32_t* __restrict__ num, int nb, int stride,
-                            int32_t* __restrict__ kbase, int bh) {
+// Exclusive prefix sum of cnt(0 .. nb-1) into out[0 .. nb-1] (one 1024-thread workgroup). Thread t
+// sums a contiguous chunk of ceil(nb / 1024) counts, the 1024 chunk sums are scanned in LDS, and
+// each thread writes its chunk's prefixes.
+template <typename Cnt>
+__device__ void prefix_block(Cnt cnt, int nb, int32_t* __restrict__ out) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   const int chunk = (nb + 1023) / 1024;
   const int lo = tid * chunk;
   const int hi = lo + chunk < nb ? lo + chunk : nb;
-  const int32_t* row = num + (size_t)bh * nb;
-  auto cnt = [&](int i) {
-    const int c = row[i];
-    return c < 0 ? 0 : (c > stride ? stride : c);
-  };
   int sum = 0;
   for (int i = lo; i < hi; ++i) sum += cnt(i);
   part[tid] = sum;
@@ -266,9 +261,48 @@ __device__ void kbase_block(const int32_t* __restrict__ num, int nb, int stride,
   }
   int run = part[tid] - sum;  // exclusive prefix of this chunk
   for (int i = lo; i < hi; ++i) {
-    kbase[(size_t)bh * nb + i] = run;
+    out[i] = run;
     run += cnt(i);
   }
+}
+
+// dS slot bases of one head: exclusive prefix sum of the clamped k2q counts.
+__device__ void kbase_block(const int32_t* __restrict__ num, int nb, int stride,
+                            int32_t* __restrict__ kbase, int bh) {
+  const int32_t* row = num + (size_t)bh * nb;
+  prefix_block(
+      [&](int i) {
+        const int c = row[i];
+        return c < 0 ? 0 : (c > stride ? stride : c);
+      },
+      nb, kbase + (size_t)bh * nb);
+}
+
+// Per-chunk slot bases, workgroup (bh, c): the counts are each kv item's positions in chunk c,
+// with the bounds clamped exactly as the kv-major kernel clamps them.
+__global__ void __launch_bounds__(1024) chunk_kbase_kernel(const int32_t* __restrict__ bounds,
+                                                           const int32_t* __restrict__ k2q_num,
+                                                           int k2q_stride, int nb, int BH,
+                                                           int nchunks, int32_t* __restrict__ kbase) {
+  const int bh = blockIdx.x, c = blockIdx.y;
+  prefix_block(
+      [&](int j) {
+        const size_t item = (size_t)bh * nb + j;
+        int n = k2q_num[item];
+        n = n < 0 ? 0 : (n > k2q_stride ? k2q_stride : n);
+        const int32_t* cb = bounds + item * (nchunks + 1) + c;
+        int b0 = cb[0], b1 = cb[1];
+        b0 = b0 < 0 ? 0 : (b0 > n ? n : b0);
+        b1 = b1 < b0 ? b0 : (b1 > n ? n : b1);
+        return b1 - b0;
+      },
+      nb, kbase + ((size_t)c * BH + bh) * nb);
+}
+
+void launch_chunk_kbase(const int32_t* bounds, const int32_t* k2q_num, int k2q_stride, int BH,
+                        int nb, int nchunks, int32_t* kbase, hipStream_t stream) {
+  hipLaunchKernelGGL(chunk_kbase_kernel, dim3(BH, nchunks), dim3(1024), 0, stream, bounds,
+                     k2q_num, k2q_stride, nb, BH, nchunks, kbase);
 }
 
 __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ num_in, int nb,
@@ -302,12 +336,13 @@ void launch_index_tasks(const IndexTasks& t, int BH, int nb, int bin_width, int 
 
 // One thread per q2k entry (bh, q, s): binary search of q in the ascending k2q row of its kv
 // block. A q missing from that row (a caller-contract violation: k2q is not the inverse of q2k,
-// or not ascending) gets the row's first slot, so every slot stays inside the head's range.
+// or not ascending) gets the row's first slot, so every slot stays inside the head's range. With
+// chunks the slot is numbered inside the chunk of q (launch_spill_qent).
 __global__ void __launch_bounds__(256) spill_qent_kernel(
     const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_num, int q2k_stride,
     const int32_t* __restrict__ k2q_idx, const int32_t* __restrict__ k2q_num, int k2q_stride,
     const int32_t* __restrict__ kbase, const int32_t* __restrict__ vbs, int nb, int cap,
-    int64_t* __restrict__ qent) {
+    const int32_t* __restrict__ bounds, int nchunks, int width, int64_t* __restrict__ qent) {
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;  // entry within the head
   const int bh = blockIdx.y;
   if (e >= (size_t)nb * q2k_stride) return;
@@ -329,7 +364,16 @@ __global__ void __launch_bounds__(256) spill_qent_kernel(
     if (list[mid] < q) lo = mid + 1; else hi = mid;
   }
   const int t = (lo < m && list[lo] == q) ? lo : 0;
-  int slot = kbase[krow] + t;
+  int slot;
+  if (bounds) {
+    int c = q / width;
+    c = c < nchunks ? c : nchunks - 1;
+    int b0 = bounds[krow * (nchunks + 1) + c];
+    b0 = b0 < 0 ? 0 : (b0 > m ? m : b0);
+    slot = kbase[(size_t)c * gridDim.y * nb + krow] + t - b0;
+  } else {
+    slot = kbase[krow] + t;
+  }
   slot = slot < 0 ? 0 : (slot >= cap ? cap - 1 : slot);
   int vb = vbs[kv];
   vb = vb < 0 ? 0 : (vb > BLOCK ? BLOCK : vb);
@@ -371,11 +415,12 @@ void launch_chunk_bounds(const int32_t* idx, const int32_t* num, int stride, int
 void launch_spill_qent(const int32_t* q2k_idx, const int32_t* q2k_num, int q2k_stride,
                        const int32_t* k2q_idx, const int32_t* k2q_num, int k2q_stride,
                        const int32_t* kbase, const int32_t* vbs, int BH, int nb, int cap,
-                       int64_t* qent, hipStream_t stream) {
+                       const int32_t* bounds, int nchunks, int width, int64_t* qent,
+                       hipStream_t stream) {
   const size_t per_head = (size_t)nb * q2k_stride;
   hipLaunchKernelGGL(spill_qent_kernel, dim3((unsigned)((per_head + 255) / 256), BH), dim3(256), 0,
                      stream, q2k_idx, q2k_num, q2k_stride, k2q_idx, k2q_num, k2q_stride, kbase,
-                     vbs, nb, cap, qent);
+                     vbs, nb, cap, bounds, nchunks, width, qent);
 }
 
 }  // namespace vsa

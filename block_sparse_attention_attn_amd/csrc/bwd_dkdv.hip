@@ -183,7 +183,8 @@ bwd_dkdv_kernel(BwdParams p) {
     };
     if (SPILL) {
       ds_item = (char*)p.ds + (size_t)bh * p.cap * (BLOCK * BLOCK * 2);
-      slot0 = ld_const(p.kbase, item) + start;
+      // (chunked spill: the launch's own tiles, numbered from the chunk's slot bases)
+      slot0 = ld_const(p.kbase, item) + (p.ds_chunk_local ? 0 : start);
       // Two stores of zeros into q block 0's tile (rewritten at step 0: one wave's stores to one
       // address land in order), so that every wait below counts the same two stores between the
       // DMA groups of consecutive q blocks.

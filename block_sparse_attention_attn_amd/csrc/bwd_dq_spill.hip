@@ -59,8 +59,16 @@ bwd_dq_spill_kernel(BwdParams p) {
   const int gc = grp & 1;       // column half inside a 32-lane half
 
   const int wid = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);
-  if (wid >= p.total_items) return;
-  const int item = p.q_order ? ld_const(p.q_order, wid) : wid;  // (b, h, q block)
+  int item;  // (b, h, q block)
+  if (p.q_count > 0) {  // one chunk of a chunked spill: q blocks [q_first, q_first + q_count)
+    const int heads = p.total_items / p.nb;
+    if (wid >= heads * p.q_count) return;
+    const int bh_c = wid / p.q_count;
+    item = bh_c * p.nb + p.q_first + (wid - bh_c * p.q_count);
+  } else {
+    if (wid >= p.total_items) return;
+    item = p.q_order ? ld_const(p.q_order, wid) : wid;
+  }
   if (item < 0 || item >= p.total_items) return;
   int n = ld_const(p.q2k_num, item);
   n = n < 0 ? 0 : (n > p.qent_stride ? p.qent_stride : n);

@@ -39,16 +39,26 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // blocks per chunk of the main kernels for nb kv blocks and the caller's chunk_blocks (0: the
 // library's choice, < 0: off); 0 when they run as one launch each
-int chunk_blocks_of(int nb, int chunk_blocks) {
+int chunk_blocks_of(int nb, int chunk_blocks, int dq_mode) {
   if (chunk_blocks < 0) return 0;
-  const int cb = chunk_blocks > 0 ? chunk_blocks
-                                  : (nb >= VSA_CHUNK_MIN_KV_BLOCKS ? VSA_CHUNK_BLOCKS : 0);
+  // the library's width: narrower with the spill, whose workspace holds one chunk's tiles (at
+  // 524288 tokens, 512 gave 978 ms against 1023 ms for 1024 and 1057 ms for 256)
+  const int dflt = dq_mode == VSA_DQ_SPILL ? VSA_SPILL_CHUNK_BLOCKS : VSA_CHUNK_BLOCKS;
+  const int cb = chunk_blocks > 0 ? chunk_blocks : (nb >= VSA_CHUNK_MIN_KV_BLOCKS ? dflt : 0);
   return cb > 0 && cb < nb ? cb : 0;  // one chunk covering every block is no chunk
 }
 // the recomputing q-major kernel runs in chunks only when the caller asks for them (chunk_blocks
 // > 0): at 524288 tokens, chunks of 1024 kv blocks left it unchanged and 2048 gained 3 %
 int dq_chunk_blocks_of(int nb, int chunk_blocks, int dq_mode) {
-  return dq_mode == VSA_DQ_RECOMPUTE && chunk_blocks > 0 ? chunk_blocks_of(nb, chunk_blocks) : 0;
+  return dq_mode == VSA_DQ_RECOMPUTE && chunk_blocks > 0 ? chunk_blocks_of(nb, chunk_blocks, dq_mode)
+                                                         : 0;
+}
+
+// q blocks per chunk of a chunked dS spill (spill mode whose kv-major kernel runs in chunks): the
+// spill then holds one chunk's tiles at a time, the q-major kernel running after each kv-major
+// launch; 0 when the spill holds every pair's tile
+int spill_chunk_blocks_of(int nb, int chunk_blocks, int dq_mode) {
+  return dq_mode == VSA_DQ_SPILL ? chunk_blocks_of(nb, chunk_blocks, dq_mode) : 0;
 }
 
 // sm_scale * log2(e) in fp32: the factor that turns q.k into the base-2 exponent of the softmax
@@ -249,10 +259,15 @@ size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride
   const bool derive = q2k_stride == 0;
   const bool spill = dq_mode == VSA_DQ_SPILL;
   const size_t kq = derive ? nb : (size_t)q2k_stride;  // q2k row width
-  const int cq = chunk_blocks_of((int)nb, chunk_blocks);
+  const int cq = chunk_blocks_of((int)nb, chunk_blocks, dq_mode);
   const size_t nchunks = cq > 0 ? (nb + cq - 1) / cq : 0;
   const int cqq = dq_chunk_blocks_of((int)nb, chunk_blocks, dq_mode);
   const size_t dq_nchunks = cqq > 0 ? (nb + cqq - 1) / cqq : 0;
+  // a chunked spill keeps one chunk's slot bases per chunk and one chunk's tiles (at most
+  // chunk width x q2k row width per head)
+  const int cs = spill_chunk_blocks_of((int)nb, chunk_blocks, dq_mode);
+  const size_t kbase_rows = cs > 0 ? nchunks : 1;
+  const size_t ds_qblocks = cs > 0 ? (size_t)cs : nb;
   const size_t sizes[VSA_WS_END] = {
       align256(bh * (size_t)seqlen * 2 * sizeof(float)),                      // lse, Delta
       align256(bh * nb * sizeof(int32_t)),                                    // kv order
@@ -260,9 +275,9 @@ size_t vsa_bwd_workspace_offset(int batch, int heads, int seqlen, int q2k_stride
       derive ? align256(bh * nb * sizeof(int32_t)) : 0,                       // q2k_num
       derive ? align256(bh * nb * nb * sizeof(int32_t)) : 0,                  // q2k_idx
       derive ? align256(vsa::invert_bitmap_bytes((int)bh, (int)nb, (int)nb)) : 0,  // bitmap
-      spill ? align256(bh * nb * sizeof(int32_t)) : 0,                        // kbase
+      spill ? align256(kbase_rows * bh * nb * sizeof(int32_t)) : 0,           // kbase
       spill ? align256(bh * nb * kq * sizeof(int64_t)) : 0,                   // qent
-      spill ? align256(bh * nb * kq * (size_t)(vsa::BLOCK * vsa::BLOCK) * 2) : 0,  // dS tiles
+      spill ? align256(bh * ds_qblocks * kq * (size_t)(vsa::BLOCK * vsa::BLOCK) * 2) : 0,  // dS
       nchunks ? align256(bh * nb * (nchunks + 1) * sizeof(int32_t)) : 0,          // bounds
       nchunks ? align256(bh * nb * 2 * (size_t)(vsa::BLOCK * vsa::HEAD_DIM) * sizeof(float))
               : 0,                                                                 // dK/dV
@@ -441,11 +456,12 @@ vsa::BwdParams main_params(const vsa_bwd_args* a, const WsView& ws) {
   m.qent = spill ? ws.qent : nullptr;
   m.ds = spill ? ws.ds : nullptr;
   m.qent_stride = m.q2k_stride;
-  m.cap = spill ? a->num_kv_blocks * m.q2k_stride : 0;
+  const int cs = spill_chunk_blocks_of(a->num_kv_blocks, a->chunk_blocks, a->dq_mode);
+  m.cap = spill ? (cs > 0 ? cs : a->num_kv_blocks) * m.q2k_stride : 0;
   m.total_items = a->batch * a->heads * a->num_kv_blocks;
   m.items_per_xcd = (m.total_items + 7) / 8;
   m.sm_scale = a->sm_scale;
-  const int cq = chunk_blocks_of(a->num_kv_blocks, a->chunk_blocks);
+  const int cq = chunk_blocks_of(a->num_kv_blocks, a->chunk_blocks, a->dq_mode);
   m.nchunks = cq > 0 ? (a->num_kv_blocks + cq - 1) / cq : 0;
   m.kv_rounds = kv_rounds_of(a->batch * a->heads, cq > 0 ? cq : a->num_kv_blocks);
   m.chunk = 0;
@@ -493,6 +509,17 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
         const int r = launch_status("vsa_bwd q2k derivation");
         if (r != VSA_OK) return r;
       }
+      // chunk bounds of the kv-major kernel's q-range chunks (a chunked spill numbers its tiles by
+      // them)
+      const int cb = chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode);
+      const int nchunks = cb > 0 ? (nb + cb - 1) / cb : 0;
+      if (cb > 0) {
+        vsa::launch_chunk_bounds(a->k2q_idx, a->k2q_num, a->max_q_blocks, BH * nb, nchunks, cb,
+                                 ws.chunk_bounds, s);
+        const int r = launch_status("vsa_bwd chunk bounds");
+        if (r != VSA_OK) return r;
+      }
+      const int cs = spill_chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode);
       // the work orders and the dS slot bases: independent per-head tasks, one launch
       vsa::IndexTasks tasks{};
       if (uses_device_order(a)) {
@@ -501,26 +528,25 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
         tasks.task[tasks.count++] = {vsa::IndexTask::ORDER, derive ? ws.q2k_num : a->q2k_num,
                                      ws.q_order};
       }
-      if (a->dq_mode == VSA_DQ_SPILL)
+      if (a->dq_mode == VSA_DQ_SPILL && cs == 0)
         tasks.task[tasks.count++] = {vsa::IndexTask::KBASE, a->k2q_num, ws.kbase};
       if (tasks.count > 0) {
         vsa::launch_index_tasks(tasks, BH, nb, VSA_ORDER_BIN_WIDTH, a->max_q_blocks, s);
         const int r = launch_status("vsa_bwd work orders / dS slot bases");
         if (r != VSA_OK) return r;
       }
+      if (cs > 0) {
+        vsa::launch_chunk_kbase(ws.chunk_bounds, a->k2q_num, a->max_q_blocks, BH, nb, nchunks,
+                                ws.kbase, s);
+        const int r = launch_status("vsa_bwd per-chunk dS slot bases");
+        if (r != VSA_OK) return r;
+      }
       if (a->dq_mode == VSA_DQ_SPILL) {
         const vsa::BwdParams m = main_params(a, ws);
         vsa::launch_spill_qent(m.q2k_idx, m.q2k_num, m.q2k_stride, a->k2q_idx, a->k2q_num,
-                               a->max_q_blocks, ws.kbase, a->vbs, BH, nb, m.cap, ws.qent, s);
+                               a->max_q_blocks, ws.kbase, a->vbs, BH, nb, m.cap,
+                               cs > 0 ? ws.chunk_bounds : nullptr, nchunks, cs, ws.qent, s);
         const int r = launch_status("vsa_bwd dS slot table");
-        if (r != VSA_OK) return r;
-      }
-      const int cb = chunk_blocks_of(nb, a->chunk_blocks);
-      if (cb > 0) {
-        const int nchunks = (nb + cb - 1) / cb;
-        vsa::launch_chunk_bounds(a->k2q_idx, a->k2q_num, a->max_q_blocks, BH * nb, nchunks, cb,
-                                 ws.chunk_bounds, s);
-        const int r = launch_status("vsa_bwd chunk bounds");
         if (r != VSA_OK) return r;
       }
       const int cbq = dq_chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode);
@@ -539,16 +565,34 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       const int per_slice = (m.total_items + 8 * m.kv_rounds - 1) / (8 * m.kv_rounds);
       m.items_per_xcd = m.kv_rounds * per_slice;
       const int launches = m.nchunks > 0 ? m.nchunks : 1;
+      // a chunked spill: each kv-major launch writes its chunk's tiles from slot 0 and the q-major
+      // kernel turns them into dq for the chunk's q blocks before the next launch reuses them
+      const int cs = spill_chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode);
       for (int c = 0; c < launches; ++c) {
         m.chunk = c;
+        if (cs > 0) {
+          m.kbase = ws.kbase + (size_t)c * BH * nb;
+          m.ds_chunk_local = 1;
+        }
         vsa::launch_bwd_dkdv(m, s);
-        const int r = launch_status("vsa_bwd dk/dv kernel");
+        int r = launch_status("vsa_bwd dk/dv kernel");
         if (r != VSA_OK) return r;
+        if (cs > 0) {
+          vsa::BwdParams q = main_params(a, ws);
+          q.q_first = c * cs;
+          q.q_count = nb - q.q_first < cs ? nb - q.q_first : cs;
+          q.items_per_xcd = (BH * q.q_count + 7) / 8;
+          vsa::launch_bwd_dq_spill(q, s);
+          r = launch_status("vsa_bwd dq kernel");
+          if (r != VSA_OK) return r;
+        }
       }
       return VSA_OK;
     }
     case VSA_BWD_DQ: {
       vsa::BwdParams m = main_params(a, ws);
+      if (spill_chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode) > 0)
+        return VSA_OK;  // a chunked spill computed dq in the DKDV stage
       if (a->dq_mode == VSA_DQ_SPILL) {
         vsa::launch_bwd_dq_spill(m, s);
         return launch_status("vsa_bwd dq kernel");

@@ -152,6 +152,11 @@ struct BwdParams {
   const int32_t* chunk_bounds = nullptr;  // [total_items, nchunks + 1]
   float* part = nullptr;
   int chunk = 0, nchunks = 0;
+  // chunked dS spill (spill mode with chunks): the kv-major kernel numbers each launch's tiles
+  // from 0 (kbase then points at that chunk's slot bases), and the q-major kernel runs once per
+  // chunk over q blocks [q_first, q_first + q_count) of every head (q_count 0: all items)
+  int ds_chunk_local = 0;
+  int q_first = 0, q_count = 0;
   int S, nb, k2q_stride, q2k_stride, total_items, items_per_xcd;
   // rounds of the kv-major kernel's XCD mapping (xcd_work_id); items_per_xcd is a multiple
   int kv_rounds = 1;
@@ -174,9 +179,19 @@ void launch_chunk_bounds(const int32_t* idx, const int32_t* num, int stride, int
 // an IndexTask::KBASE task.
 // qent[bh, q, s] for s < q2k_num[bh, q]: the slot of pair (q, kv = q2k_idx[bh, q, s]), i.e.
 // kbase[bh, kv] + (position of q in the ascending k2q row of kv), packed with kv and vbs[kv].
+// With chunks (bounds non-null, the kv-major chunk bounds; nchunks chunks of `width` q blocks), the
+// tiles are numbered per chunk: kbase holds [nchunks][BH * nb] slot bases and the pair of q block q
+// takes slot kbase[q / width][bh, kv] + (its position) - bounds[bh, kv][q / width].
 void launch_spill_qent(const int32_t* q2k_idx, const int32_t* q2k_num, int q2k_stride,
                        const int32_t* k2q_idx, const int32_t* k2q_num, int k2q_stride,
                        const int32_t* kbase, const int32_t* vbs, int BH, int nb, int cap,
-                       int64_t* qent, hipStream_t stream);
+                       const int32_t* bounds, int nchunks, int width, int64_t* qent,
+                       hipStream_t stream);
+// Per-chunk dS slot bases: kbase[c][bh * nb + kv] = sum over the kv blocks before kv in head bh of
+// their pair counts in chunk c (bounds[item][c + 1] - bounds[item][c], clamped as the kv-major
+// kernel clamps them against min(max(k2q_num, 0), k2q_stride)). One launch, (BH, nchunks)
+// workgroups.
+void launch_chunk_kbase(const int32_t* bounds, const int32_t* k2q_num, int k2q_stride, int BH,
+                        int nb, int nchunks, int32_t* kbase, hipStream_t stream);
 
 }  // namespace vsa

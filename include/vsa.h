@@ -133,7 +133,10 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *                     pair, reading 8 KiB of dS per pair from HBM. This needs 8 KiB of workspace
  *                     per possible pair (B*H*nb*q2k_stride of them, nb*nb when q2k is derived)
  *                     and k2q rows in ascending order (as vsa_invert_indices writes them); it
- *                     supports num_kv_blocks <= 65535.
+ *                     supports num_kv_blocks <= 65535. When the kv-major kernel runs in chunks
+ *                     of R q blocks (below), the spill is chunked too: it holds the tiles of one
+ *                     chunk (B*H*R*q2k_stride possible pairs), and the q-major kernel runs after
+ *                     each kv-major launch, over that chunk's q blocks.
  *
  * q2k lists (optional): the forward's q2k_idx [B, H, num_kv_blocks, q2k_stride] / q2k_num, which
  * must describe the same selection as k2q (each pair once). NULL: the library derives them from
@@ -165,10 +168,12 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *   VSA_WS_BITMAP    the inversion's bitmap
  * only in VSA_DQ_SPILL mode:
  *   VSA_WS_KBASE     int32 [B, H, nb]: per kv block, the first dS slot of its head's pairs
- *                    (exclusive prefix sum of k2q_num inside the head)
+ *                    (exclusive prefix sum of k2q_num inside the head); with a chunked spill
+ *                    [C, B, H, nb], the same over each chunk's pairs
  *   VSA_WS_QENT      int64 [B, H, nb, K']: per q2k entry, its dS slot | kv block << 32 |
  *                    vbs[kv block] << 48
- *   VSA_WS_DS        fp16 [B, H, nb*K', 64, 64]: the dS tiles (dS * 2^es), slot-major
+ *   VSA_WS_DS        fp16 [B, H, nb*K', 64, 64]: the dS tiles (dS * 2^es), slot-major; with a
+ *                    chunked spill [B, H, R*K', 64, 64], one chunk's tiles
  * only when the main kernels run in chunks (below), with C chunks:
  *   VSA_WS_CHUNK_BOUNDS int32 [B*H*nb, C+1]: per kv item, the position in its k2q list of the
  *                    first q block of each chunk (the last entry is the list length)
@@ -191,9 +196,9 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *
  * Chunks (chunk_blocks argument; 0 = the library's choice): with R = chunk_blocks (> 0) each
  * main kernel runs as C = ceil(nb / R) launches; with 0, the kv-major kernel alone does, with
- * R = VSA_CHUNK_BLOCKS, from VSA_CHUNK_MIN_KV_BLOCKS kv blocks per sequence on (at 524288 tokens
- * its chunks saved 7-12 %, while the q-major kernel gained at most 3 %). Launch c of the kv-major
- * kernel takes, of every
+ * R = VSA_CHUNK_BLOCKS (VSA_SPILL_CHUNK_BLOCKS in VSA_DQ_SPILL mode), from VSA_CHUNK_MIN_KV_BLOCKS
+ * kv blocks per sequence on (at 524288 tokens its chunks saved 7-12 %, while the recomputing
+ * q-major kernel gained at most 3 %). Launch c of the kv-major kernel takes, of every
  * k2q list, the q blocks in [c*R, (c+1)*R); launch c of the recomputing q-major kernel takes, of
  * every q2k list, the positions from the first entry >= c*R to the first entry >= (c+1)*R (the kv
  * blocks in [c*R, (c+1)*R) for an ascending list; any order is correct). Each carries its
@@ -202,9 +207,14 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  * chunks, ascending walks of thousands of entries drift apart and almost every Q/dO (K/V) tile
  * comes from HBM (the pages' long-sequence cache-locality mode serves the same purpose).
  * chunk_blocks < 0: never chunk. Chunking changes only the fp32 summation order of the chunked
- * sums. The dS-reading q-major kernel (VSA_DQ_SPILL) always runs as one launch. */
+ * sums. In VSA_DQ_SPILL mode the chunks also bound the spill: the dS-reading q-major kernel runs
+ * once per chunk, over that chunk's q blocks, right after the kv-major launch that wrote their
+ * tiles; its results are bitwise those of the unchunked spill. At 524288 tokens with top-k 2048
+ * (B*H = 8) the chunked spill with R = 512 holds 64 GiB of tiles and took the backward from
+ * 1139 ms (recompute) to 978 ms. */
 #define VSA_CHUNK_MIN_KV_BLOCKS 4096
 #define VSA_CHUNK_BLOCKS 1024
+#define VSA_SPILL_CHUNK_BLOCKS 512
 #define VSA_ORDER_MIN_KV_BLOCKS 64
 #define VSA_ORDER_BIN_WIDTH 4
 #define VSA_ORDER_MAX_KV_BLOCKS 16384
@@ -279,7 +289,8 @@ int vsa_bwd(const vsa_bwd_args* a, void* stream);
  * VSA_DQ_SPILL mode and the chunk bounds when the kv-major kernel runs in q-range chunks;
  * otherwise it enqueues nothing. In VSA_DQ_RECOMPUTE mode DKDV and DQ only read
  * what PREPROCESS and INDEX wrote and may run in either order; in VSA_DQ_SPILL mode DQ reads the
- * dS tiles DKDV writes and must follow it. */
+ * dS tiles DKDV writes and must follow it, and with a chunked spill DKDV runs the q-major launches
+ * too (each after the kv-major launch of its chunk) and DQ enqueues nothing. */
 typedef enum {
   VSA_BWD_PREPROCESS = 0,  /* operand scales and fp16 copies, Delta, the records; zero dk/dv
                               rows of kv blocks with an empty k2q list */

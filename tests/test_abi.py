@@ -53,7 +53,8 @@ def test_binding_constants_match_the_header():
     for name, value in (("VSA_ORDER_MIN_KV_BLOCKS", V.ORDER_MIN_KV_BLOCKS),
                         ("VSA_ORDER_BIN_WIDTH", V.ORDER_BIN_WIDTH),
                         ("VSA_CHUNK_MIN_KV_BLOCKS", V.CHUNK_MIN_KV_BLOCKS),
-                        ("VSA_CHUNK_BLOCKS", V.CHUNK_BLOCKS)):
+                        ("VSA_CHUNK_BLOCKS", V.CHUNK_BLOCKS),
+                        ("VSA_SPILL_CHUNK_BLOCKS", V.SPILL_CHUNK_BLOCKS)):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == value, name
     m = re.search(r"#define\s+VSA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
@@ -143,9 +144,21 @@ def test_workspace_chunk_regions():
     o = offs(1, 2, 64 * nb, 128, V.CHUNK_BLOCKS)  # requested: both kernels
     assert o[V.WS_DQ_PART] - o[V.WS_DQ_BOUNDS] == a256(2 * nb * (c + 1) * 4)
     assert o[V.WS_STATS] - o[V.WS_DQ_PART] == 2 * nb * 64 * 128 * 4
-    # the dS-reading q-major kernel runs as one launch: no dQ chunk regions in spill mode
+    # spill mode: no dQ chunk regions (the dS-reading q-major kernel runs once per chunk), and a
+    # chunked spill: C rows of slot bases, one chunk's tiles (R x K' per head)
     sp = [V.bwd_workspace_offset(1, 2, 64 * nb, r, 128, V.DQ_SPILL, 0) for r in range(V.WS_END + 1)]
+    cs = -(-nb // V.SPILL_CHUNK_BLOCKS)  # the library's chunks are narrower with the spill
+    assert sp[V.WS_DKV_PART] - sp[V.WS_CHUNK_BOUNDS] == a256(2 * nb * (cs + 1) * 4)
     assert sp[V.WS_DQ_BOUNDS] == sp[V.WS_STATS] == sp[V.WS_DKV_PART] + 2 * nb * 2 * 64 * 128 * 4
+    assert sp[V.WS_QENT] - sp[V.WS_KBASE] == a256(cs * 2 * nb * 4)
+    assert sp[V.WS_CHUNK_BOUNDS] - sp[V.WS_DS] == 2 * V.SPILL_CHUNK_BLOCKS * 128 * 8192
+    un = [V.bwd_workspace_offset(1, 2, 64 * nb, r, 128, V.DQ_SPILL, -1) for r in range(V.WS_END + 1)]
+    assert un[V.WS_QENT] - un[V.WS_KBASE] == a256(2 * nb * 4)
+    assert un[V.WS_CHUNK_BOUNDS] - un[V.WS_DS] == 2 * nb * 128 * 8192
+    # a forced width at a small size: ceil(10 / 3) = 4 chunks, tiles for 3 q blocks x 7 per head
+    sp = [V.bwd_workspace_offset(1, 2, 64 * 10, r, 7, V.DQ_SPILL, 3) for r in range(V.WS_END + 1)]
+    assert sp[V.WS_QENT] - sp[V.WS_KBASE] == a256(4 * 2 * 10 * 4)
+    assert sp[V.WS_CHUNK_BOUNDS] - sp[V.WS_DS] == a256(2 * 3 * 7 * 8192)
     # a forced chunk size at any size; one chunk covering every block is no chunk
     o = offs(1, 1, 64 * 10, 0, 3)
     assert o[V.WS_DKV_PART] - o[V.WS_CHUNK_BOUNDS] == a256(10 * 5 * 4)

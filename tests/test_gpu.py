@@ -534,13 +534,16 @@ def test_backward_q_range_chunks(case, chunk, mode):
         assert np.all(got.float().cpu().numpy()[ref == 0] == 0)
 
 
+@pytest.mark.parametrize("chunk", [-1, 3])
 @pytest.mark.parametrize("give_q2k", [False, True])
 @pytest.mark.parametrize("n", [2, "odd_blocks_ragged"])
-def test_spill_slot_tables_bit_exact(n, give_q2k):
+def test_spill_slot_tables_bit_exact(n, give_q2k, chunk):
     """The dS slot tables of the spill mode (index work: bit-exact). Expected values from their
     definition in include/vsa.h, on the oracle's k2q: kbase = exclusive prefix sum of the k2q
     counts inside each head; qent = (kbase[kv] + position of q in kv's ascending k2q row) |
-    kv << 32 | vbs[kv] << 48 for every q2k entry."""
+    kv << 32 | vbs[kv] << 48 for every q2k entry. With chunks of R q blocks (a chunked spill) the
+    same per chunk: kbase[c] counts each kv block's q blocks in [cR, (c+1)R), and the slot of q is
+    kbase[q // R][kv] + its position - the position of the chunk's first entry."""
     if n == 2:
         c = workloads.config(2)
     else:
@@ -553,17 +556,28 @@ def test_spill_slot_tables_bit_exact(n, give_q2k):
     lse = torch.zeros(c.B, c.H, c.S, dtype=torch.float32, device=DEV)
     extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"]) if give_q2k else {}
     plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
-                     dq_mode=V.DQ_SPILL, **extra)
-    say(f"[slot tables] {n}, q2k {'given' if give_q2k else 'derived'}")
+                     dq_mode=V.DQ_SPILL, chunk_blocks=chunk, **extra)
+    say(f"[slot tables] {n}, q2k {'given' if give_q2k else 'derived'}, chunks {chunk}")
     plan.stage(plan.PREPROCESS)
     plan.stage(plan.INDEX)
     torch.cuda.synchronize()
     BH, nb = c.B * c.H, c.nb
     kq = c.q2k_idx.shape[-1] if give_q2k else nb
+    kidx = ridx.reshape(BH, nb, -1)
     num = rnum.reshape(BH, nb).astype(np.int64)
-    kbase = np.zeros((BH, nb), np.int64)
-    kbase[:, 1:] = np.cumsum(num, axis=1)[:, :-1]
-    assert np.array_equal(plan.region(V.WS_KBASE, BH * nb).cpu().numpy().reshape(BH, nb), kbase)
+    R = chunk if chunk > 0 else nb
+    nch = -(-nb // R)
+    # first[c][bh, kv]: position in kv's k2q row of its first q block >= cR
+    first = np.zeros((nch + 1, BH, nb), np.int64)
+    for bh in range(BH):
+        for kv in range(nb):
+            row = kidx[bh, kv, :num[bh, kv]]
+            first[:, bh, kv] = np.searchsorted(row, np.arange(nch + 1) * R)
+    first[nch] = num
+    kbase = np.zeros((nch, BH, nb), np.int64)
+    kbase[:, :, 1:] = np.cumsum(first[1:] - first[:-1], axis=2)[:, :, :-1]
+    got_kb = plan.region(V.WS_KBASE, nch * BH * nb).cpu().numpy().reshape(nch, BH, nb)
+    assert np.array_equal(got_kb, kbase)
     got = plan.region(V.WS_QENT, BH * nb * kq, torch.int64).cpu().numpy().reshape(BH, nb, kq)
     # the q2k lists the library walks: the given ones, or the inverse of k2q (ascending)
     if give_q2k:
@@ -573,13 +587,14 @@ def test_spill_slot_tables_bit_exact(n, give_q2k):
         di, dn = O.invert_indices(ridx, rnum, nb)
         qidx, qnum = di.reshape(BH, nb, -1), dn.reshape(BH, nb)
     vbs = c.vbs.numpy()
-    kidx = ridx.reshape(BH, nb, -1)
     for bh in range(BH):
         for q in range(nb):
+            ch = q // R
             for s_ in range(int(qnum[bh, q])):
                 kv = int(qidx[bh, q, s_])
                 row = list(kidx[bh, kv, :num[bh, kv]])
-                want = (int(kbase[bh, kv]) + row.index(q)) | (kv << 32) | (int(vbs[kv]) << 48)
+                slot = int(kbase[ch, bh, kv]) + row.index(q) - int(first[ch, bh, kv])
+                want = slot | (kv << 32) | (int(vbs[kv]) << 48)
                 assert int(got[bh, q, s_]) == want, (bh, q, s_)
 
 
@@ -754,11 +769,14 @@ def _head(c, h):
 @pytest.fixture(scope="module")
 def c5_run():
     """524288 tokens, 8192 kv blocks, top-k 2048, inputs x0.5, last kv block 40 valid tokens:
-    GPU forward -> invert -> backward (default chunked dK/dV launches), run once for the tests
+    GPU forward -> invert -> backward on the library's defaults for this shape with the q2k rows
+    given (the chunked dS spill: chunks of SPILL_CHUNK_BLOCKS q blocks), run once for the tests
     below."""
     c = workloads.config(5)
-    say("[end-to-end] config 5 (B=1 H=8 S=524288, 25%, ragged last block)")
-    d, o, lse, (k2q_idx, k2q_num), plan, grads = _end_to_end(c)
+    mode = V.default_dq_mode(c.B, c.H, c.S, c.q2k_idx.shape[-1], device=DEV)
+    assert mode == V.DQ_SPILL  # 72 GiB of workspace, within a third of the device's memory
+    say("[end-to-end] config 5 (B=1 H=8 S=524288, 25%, ragged last block), chunked spill")
+    d, o, lse, (k2q_idx, k2q_num), plan, grads = _end_to_end(c, mode, give_q2k=True)
     yield c, d, o, lse, (k2q_idx, k2q_num), plan, grads
     del d, o, lse, k2q_idx, k2q_num, plan, grads
     torch.cuda.empty_cache()
@@ -778,8 +796,9 @@ def test_config5_524k_invert_bit_exact(c5_run):
 @pytest.mark.timeout(900)
 def test_config5_524k_end_to_end_sampled(c5_run):
     """o, lse and dq on sampled q blocks against the oracle (each one q block of one head);
-    the invariants and the exact zeros of the ragged block; dk and dv of the default chunked
-    dK/dV launches against one launch, within the fp32 reordering bound."""
+    the invariants and the exact zeros of the ragged block; the default chunked path against one
+    launch per kernel in recompute mode: dk and dv within the fp32 reordering bound, dq within the
+    same bound (the two dQ kernels round dS alike but sum in another arrangement)."""
     c, d, o, lse, (k2q_idx, k2q_num), plan, grads = c5_run
     dq, dk, dv = grads
     _invariants(c, grads)
@@ -800,14 +819,13 @@ def test_config5_524k_end_to_end_sampled(c5_run):
     ms = ev[0].elapsed_time(ev[1])
     say(f"  backward chain {ms:.1f} ms, {c.pairs * 5 * 2 * 64 * 64 * 128 / ms / 1e9:.1f} TFLOPS "
         f"on selected blocks")
-    # the same backward as one launch per kernel: dk, dv equal up to the fp32 summation order of
-    # the chunk partial sums, dq bitwise (its kernel does not run in chunks by default)
-    say("  one-launch dK/dV for comparison")
+    # the same backward as one launch per kernel, recompute mode: dk, dv equal up to the fp32
+    # summation order of the chunk partial sums; dq from the other dQ kernel
+    say("  one-launch recompute backward for comparison")
     one = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
                     dq_mode=V.DQ_RECOMPUTE, chunk_blocks=-1).run()
     torch.cuda.synchronize()
-    assert torch.equal(one[0], dq)
-    for name, g1, g in (("dk", one[1], dk), ("dv", one[2], dv)):
+    for name, g1, g in (("dq", one[0], dq), ("dk", one[1], dk), ("dv", one[2], dv)):
         diff = (g.float() - g1.float()).abs()
         say(f"  {name}: chunked vs one launch max|diff| {diff.max().item():.3e}, "
             f"mean {diff.mean().item():.3e}, mean|one| {g1.float().abs().mean().item():.3e}")
