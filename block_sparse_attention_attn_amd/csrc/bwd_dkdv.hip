@@ -59,7 +59,7 @@ namespace vsa {
 namespace {
 
 constexpr int STAGES = 4;                        // ring depth: stage t%4 holds q block t
-constexpr int STAGE_BYTES = 16384;               // one [64][128] bf16 tile
+constexpr int STAGE_BYTES = 16384;               // one [64][128] tile of 16-bit values
 constexpr int LD_BYTES = LD_RECORD_FLOATS * 4;   // one q block's statistics record
 constexpr int DMA_PER_BLOCK = 9;                 // vector memory operations per wave per q block
 constexpr int STORES_PER_BLOCK = 2;              // dS stores per wave per q block (spill mode)

@@ -315,7 +315,8 @@ int vsa_bwd_check(const vsa_bwd_args* a) {
   if (items * (size_t)a->max_q_blocks >= kMaxElems || items * (size_t)a->num_kv_blocks >= kMaxElems)
     return fail(VSA_EINVAL, "vsa_bwd: index metadata too large");
   if (!std::isfinite(a->sm_scale)) return fail(VSA_EINVAL, "vsa_bwd: sm_scale must be finite");
-  // the statistics records hold lse / scale_log2, finite only for a scale not too close to 0
+  // the statistics records hold (pp - lse) / (scale_log2 2^(eq + ek)), finite only for a scale
+  // not too close to 0
   if (!(std::fabs(scale_log2(a->sm_scale)) >= 0x1p-120f))
     return fail(VSA_EINVAL, "vsa_bwd: |sm_scale * log2(e)| must be at least 2^-120");
   if (!a->q || !a->k || !a->v || !a->o || !a->dout || !a->lse)

@@ -158,7 +158,7 @@ __device__ __forceinline__ uint32_t absmax_bits8(bf16x8 x) {
 // ---------------------------------------------------------------------------------------------
 // LDS tile formats
 // ---------------------------------------------------------------------------------------------
-// A [64 rows][128] bf16 tile (Q, dO, K, V) occupies 16 KiB = 64 rows x 16 chunks of 16 bytes; a
+// A [64 rows][128] tile of 16-bit values (Q, dO, K, V in bf16 or fp16) occupies 16 KiB = 64 rows x 16 chunks of 16 bytes; a
 // row is exactly the 64 banks x 4 bytes of LDS, so the bank group of a chunk is its slot in the
 // row. Chunk cc of row r is stored at chunk slot r*16 + (cc ^ swz128(r)) with
 // swz128(r) = ((r >> 2) & 3) | ((r & 3) << 2), a swap of the row's two low bit pairs:
@@ -259,7 +259,7 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
-// Tile DMA with one M0 write per tile. A [64][128] bf16 tile is 16 slices of 1 KiB (4 rows
+// Tile DMA with one M0 write per tile. A [64][128] 16-bit tile is 16 slices of 1 KiB (4 rows
 // each); wave w of four copies slices 4w .. 4w+3, whose LDS destinations are consecutive KiB.
 // global_load_lds adds its immediate offset to both the global and the LDS address, so M0 is set
 // once to the wave's first slice and the four DMAs carry offsets 0, 1024, 2048, 3072; the
@@ -399,7 +399,7 @@ __device__ __forceinline__ void dma_tile_pair_rec(const void* ga, const void* gb
       : "memory");
 }
 
-// Per-lane byte offsets inside a [64][128] bf16 tile for the slices part, part + NPARTS, ... that
+// Per-lane byte offsets inside a [64][128] 16-bit tile for the slices part, part + NPARTS, ... that
 // tile_load_async<NPARTS> would issue (the same for every tile).
 template <int NPARTS>
 __device__ __forceinline__ void tile_offsets(uint32_t* off, int lane, int part) {
@@ -425,7 +425,7 @@ __device__ __forceinline__ uint32_t lds_addr(const VSA_LDS void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
-// Copy one [64][128] bf16 tile (row stride 128 elements) from global memory into the swizzled LDS
+// Copy one [64][128] 16-bit tile (row stride 128 elements) from global memory into the swizzled LDS
 // format. A wave moves 64 lanes x 16 bytes per DMA; NPARTS waves share the tile, wave `part`
 // issuing slices part, part + NPARTS, ... of the tile's 16 one-KiB slices.
 template <int NPARTS>
