@@ -1,8 +1,9 @@
 """vsa_bwd_noalloc (the backward with its workspace in the library's static scratch) against
 vsa_bwd with a caller workspace: the same kernels, so every output is bitwise identical. Two
 calls in a row, the second on a smaller problem (the scratch keeps the first call's contents),
-in both dQ modes, with the q2k lists given and derived; and a call whose workspace would not
-fit the scratch is refused before anything runs."""
+in both dQ modes, with the q2k lists given and derived; a call whose workspace would not fit
+the scratch is refused before anything runs; and a call captured into a HIP graph replays to the
+same bits."""
 import pytest
 import torch
 
@@ -71,3 +72,44 @@ def test_noalloc_refuses_a_call_beyond_the_scratch():
     with pytest.raises(RuntimeError, match="static scratch"):
         V.backward_noalloc(big, big, big, big, big, lse_big, idx, num, vbs, (big, big, big),
                            q2k_idx=q2k, q2k_num=num, dq_mode=V.DQ_SPILL)
+
+
+@pytest.mark.parametrize("mode", [V.DQ_RECOMPUTE, V.DQ_SPILL])
+def test_noalloc_replays_under_graph_capture(mode):
+    """The callers the entry is for include code under HIP graph capture: the call is captured
+    (its kernels launch on the capturing stream; nothing is allocated or cleared with a memset),
+    then the graph is replayed three times, each after eager work on another problem through the
+    same scratch and with the outputs refilled with NaN; every replay gives the eager call's bits."""
+    c = workloads.make_case(1, 2, 12, 4, seed=64, vbs=[64] * 11 + [30], name="graph")
+    other = workloads.make_case(1, 1, 9, 3, seed=65, vbs=[64] * 8 + [41], name="other")
+    d, o, lse, k2q_idx, k2q_num = _inputs(c)
+    d2, o2, lse2, k2q_idx2, k2q_num2 = _inputs(other)
+    extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"])
+
+    def call(out):
+        return V.backward_noalloc(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num,
+                                  d["vbs"], out, dq_mode=mode, **extra)
+
+    say(f"[noalloc] graph capture, mode {mode}")
+    want = [t.clone() for t in call(_nan_out(d))]  # eager; also resolves the scratch address
+    torch.cuda.synchronize()
+    out = _nan_out(d)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm-up call on the capturing stream, as torch advises
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        V.backward_noalloc(d2["do"], d2["q"], d2["k"], d2["v"], o2, lse2, k2q_idx2, k2q_num2,
+                           d2["vbs"], _nan_out(d2), dq_mode=mode)
+        for t in out:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, g, w in zip(("dq", "dk", "dv"), out, want):
+            assert torch.equal(g, w), (rep, name)
