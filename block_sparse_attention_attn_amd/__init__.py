@@ -372,9 +372,11 @@ class BwdPlan:
     ``q2k_idx``/``q2k_num`` (the forward's metadata, the same selection as k2q) the library skips
     deriving them. ``chunk_blocks``: blocks per chunk of the main kernels, q blocks of each k2q
     list for the kv-major kernel and kv blocks of each q2k list for the recomputing q-major one
-    (0: the library's choice, chunks of CHUNK_BLOCKS for the kv-major kernel alone from
-    CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch each). The plan keeps references to
-    every tensor it points at.
+    (0: the library's choice, chunks of CHUNK_BLOCKS -- SPILL_CHUNK_BLOCKS in DQ_SPILL mode --
+    for the kv-major kernel alone from CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch
+    each). In DQ_SPILL mode with chunks the spill holds one chunk's dS tiles and the dQ kernel runs
+    after each chunk's kv-major launch, inside stage DKDV (stage DQ then enqueues nothing). The
+    plan keeps references to every tensor it points at.
     """
 
     PREPROCESS, INDEX, DKDV, DQ = 0, 1, 2, 3
