@@ -67,7 +67,9 @@ __global__ void __launch_bounds__(256) bwd_stats_kernel(BwdPreParams p) {
   const int rr = tid >> 4;  // row inside the pass
   const int c = tid & 15;   // 16-byte chunk of the row
   const size_t row0 = (size_t)bh * p.S + (size_t)blk * BLOCK;
-  const bool empty = p.k2q_num[(size_t)bh * p.nb + blk] == 0;
+  // (a negative count, a caller-contract violation, also gets zero rows: the kv-major kernel
+  // skips items whose clamped count is 0)
+  const bool empty = p.k2q_num[(size_t)bh * p.nb + blk] <= 0;
   float* rec = p.lse_delta + ((size_t)bh * p.nb + blk) * LD_RECORD_FLOATS;
   uint32_t mq = 0, mk = 0, mv = 0, mo = 0;
   float n2v = 0.0f, n2o = 0.0f, md = 0.0f;
