@@ -102,7 +102,7 @@ _SIGNATURES = {
                                      _p, _p]),
     "vsa_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(_BwdArgs), _p]),
 }
-NOALLOC_SCRATCH_BYTES = 64 << 20  # VSA_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 512 << 20  # VSA_NOALLOC_SCRATCH_BYTES
 
 
 def library_path() -> str:

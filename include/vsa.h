@@ -309,14 +309,15 @@ int vsa_bwd_stage(const vsa_bwd_args* a, int stage, void* stream);
  * workspace taken from a static device array of VSA_NOALLOC_SCRATCH_BYTES inside the library
  * (one per GPU, held until the process ends) instead of a->workspace, which is ignored along with
  * a->workspace_bytes. The caller still passes every input and output. A call whose
- * vsa_bwd_workspace_bytes exceeds the scratch returns VSA_EUNSUPPORTED (recompute mode with the
- * q2k lists given fits up to about 2 * 10^6 q blocks per call (B*H*nb); the dS spill, 8 KiB per
+ * vsa_bwd_workspace_bytes exceeds the scratch returns VSA_EUNSUPPORTED (the workspace holds about
+ * 65 KiB per q block for the fp16 operand copies and records, so recompute mode fits up to about
+ * 8100 q blocks per call (B*H*nb), e.g. 8 heads of 32768 tokens; the dS spill, 8 KiB per
  * possible pair, fits only small problems). Calls on one GPU share its scratch: calls that
  * overlap there (different streams, no ordering between them) race and give undefined results.
  * The chain writes every scratch region it reads within the call, so no clearing is needed
  * between calls. The first call on a device resolves the scratch address there
  * (hipGetSymbolAddress); no call allocates or frees memory. */
-#define VSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define VSA_NOALLOC_SCRATCH_BYTES (512u << 20)
 int vsa_bwd_noalloc(const vsa_bwd_args* a, void* stream);
 
 /* Work order alone: for each (b, h), its kv items ranked by bin = k2q_num / bin_width (larger bin

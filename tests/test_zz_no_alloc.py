@@ -55,6 +55,24 @@ def test_noalloc_matches_workspace_call(mode, give_q2k):
             assert torch.equal(g, w), name
 
 
+def test_noalloc_large_recompute_call():
+    """A call that fills most of the scratch: 8 heads of 16384 tokens, recompute mode, q2k given
+    (about 130 MiB of workspace), against the workspace call."""
+    c = workloads.make_case(1, 8, 256, 32, seed=66, name="large")
+    need = V.bwd_workspace_bytes(c.B, c.H, c.S, c.q2k_idx.shape[-1], V.DQ_RECOMPUTE)
+    assert V.NOALLOC_SCRATCH_BYTES // 8 < need <= V.NOALLOC_SCRATCH_BYTES
+    d, o, lse, k2q_idx, k2q_num = _inputs(c)
+    extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"])
+    say(f"[noalloc] large recompute call, {need >> 20} MiB of workspace")
+    want = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                     out=_nan_out(d), dq_mode=V.DQ_RECOMPUTE, **extra).run()
+    got = V.backward_noalloc(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                             _nan_out(d), dq_mode=V.DQ_RECOMPUTE, **extra)
+    torch.cuda.synchronize()
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        assert torch.equal(g, w), name
+
+
 def test_noalloc_refuses_a_call_beyond_the_scratch():
     # 32768 tokens, top-k 128, dS spill: 4 GiB of workspace
     B, H, S = 1, 8, 32768
