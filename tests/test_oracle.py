@@ -370,6 +370,42 @@ def test_delta_is_the_p_weighted_mean_of_dp():
     assert ds.sum(-1).abs().max().item() <= 1e-12 * max(1.0, ds.abs().max().item())
 
 
+def test_gradient_with_delta_from_a_rounded_o():
+    """The reference the GPU tests use where Delta comes from the bf16 o the backward is given: the
+    exact gradient shifted by delta_i = rowsum((bf16(o) - o) * dO)_i, dq_i by -sm_scale delta_i
+    (P K)_i and dk_j by -sm_scale (P^T (delta * q))_j (from oracle calls: a forward with v := k, a
+    backward with dO := delta * q), equals the gradient computed directly with that Delta from
+    torch's softmax of the masked scores. Scores 64x larger than N(0,1) make the rows nearly
+    one-hot, where the shift is largest."""
+    c = _case(nb=6, topk=3, H=2, B=1, seed=17, vbs=[64, 37, 64, 50, 64, 1],
+              kv_pool=[0, 1, 2, 3, 5])
+    c.q = (c.q.float() * 8).to(torch.bfloat16)
+    c.k = (c.k.float() * 8).to(torch.bfloat16)
+    ro, _ = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    o16 = O.bf16_rne(ro)
+    rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    do = c.do.double().numpy()
+    delta = ((o16 - ro) * do).sum(-1, keepdims=True)
+    pk, _ = O.forward(c.q, c.k, c.k, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    _, _, ptdq = O.backward(c.q, c.k, c.v, torch.from_numpy(delta * c.q.double().numpy()),
+                            c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    got_dq = rdq - c.sm_scale * delta * pk
+    got_dk = rdk - c.sm_scale * ptdq
+    mask = _mask_torch(c)
+    q, k, v, dO = (t.to(torch.float64) for t in (c.q, c.k, c.v, c.do))
+    s_ = c.sm_scale * q @ k.transpose(-1, -2)
+    p = torch.softmax(s_.masked_fill(~mask, float("-inf")), dim=-1)
+    dp = dO @ v.transpose(-1, -2)
+    d16 = (torch.from_numpy(o16) * dO).sum(-1, keepdim=True)
+    ds = p * (dp - d16)
+    want_dq = (c.sm_scale * ds @ k).numpy()
+    want_dk = (c.sm_scale * ds.transpose(-1, -2) @ q).numpy()
+    _close(got_dq, want_dq, 1e-12)
+    _close(got_dk, want_dk, 1e-12)
+    # the shift is not negligible here (so the test can see a wrong sign or a dropped term)
+    assert np.abs(want_dq - rdq).max() > 1e-4 * np.abs(rdq).max()
+
+
 def test_work_order_matches_hand_worked_fixture_and_invariants():
     with open(os.path.join(GOLDEN, "order_tiny.json")) as f:
         g = json.load(f)
