@@ -456,6 +456,49 @@ def test_backward_edge_cases(name, mode):
         assert np.all(got.float().cpu().numpy()[zero] == 0)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_backward_random_shapes(seed):
+    """Seeded random shapes and options: B, H, nb, per-row top-k, ragged vbs (0 to 64), a kv pool,
+    empty q rows, the dQ mode, q-range chunks and whether the q2k lists are given. GPU forward
+    and backward against the oracle (all gates on o, lse and the three gradients)."""
+    rng = np.random.default_rng(1000 + seed)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    nb = int(rng.integers(1, 14))
+    pool = sorted(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+    choices = sorted({int(x) for x in rng.integers(1, len(pool) + 1, size=3)})
+    vbs = [int(x) if rng.random() < 0.35 else 64 for x in rng.integers(0, 65, size=nb)]
+    mode = V.DQ_SPILL if rng.random() < 0.5 else V.DQ_RECOMPUTE
+    chunk = int(rng.integers(1, nb + 1)) if rng.random() < 0.5 else 0
+    give = bool(rng.random() < 0.5)
+    c = workloads.make_case(B, H, nb, None, seed=2000 + seed, vbs=vbs, kv_pool=pool,
+                            topk_choices=choices, name=f"random{seed}")
+    for _ in range(int(rng.integers(0, 3))):  # a few empty q rows
+        c.q2k_num[int(rng.integers(0, B)), int(rng.integers(0, H)), int(rng.integers(0, nb))] = 0
+    say(f"[backward] random shape {seed}: B={B} H={H} nb={nb} pool={pool} top-k {choices} "
+        f"vbs={vbs} mode={mode} chunk={chunk} q2k {'given' if give else 'derived'}")
+    d = to_dev(c)
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], nb)
+    extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"]) if give else {}
+    dq, dk, dv = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                           out=(nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"])),
+                           dq_mode=mode, chunk_blocks=chunk, **extra).run()
+    torch.cuda.synchronize()
+    ro, rl = O.forward(c.q, c.k, c.v, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    check_close("o", o, ro)
+    finite = np.isfinite(rl)
+    got_lse = lse.cpu().double().numpy()
+    assert np.array_equal(np.isfinite(got_lse), finite)
+    assert np.abs(got_lse[finite] - rl[finite]).max(initial=0.0) <= LSE_ABS_TOL
+    rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        if np.abs(ref).max() == 0:  # nothing selected anywhere: exact zeros
+            assert torch.all(got == 0), name
+            continue
+        check_close(name, got, ref)
+        assert np.all(got.float().cpu().numpy()[ref == 0] == 0), name
+
+
 @pytest.mark.parametrize("mode", sorted(MODES))
 def test_backward_negative_scale(mode):
     """The backward with a negative sm_scale (the records hold lse / scale_log2, negative here)
