@@ -339,7 +339,9 @@ void launch_index_tasks(const IndexTasks& t, int BH, int nb, int bin_width, int 
 // One thread per q2k entry (bh, q, s): binary search of q in the ascending k2q row of its kv
 // block. A q missing from that row (a caller-contract violation: k2q is not the inverse of q2k,
 // or not ascending) gets the row's first slot, so every slot stays inside the head's range. With
-// chunks the slot is numbered inside the chunk of q (launch_spill_qent).
+// chunks the slot is numbered inside the chunk of q (launch_spill_qent). The kernel is bound by
+// the latency of its dependent loads, so the independent ones are issued together: the entry
+// with its row's count, then the kv block's list length, slot base, chunk bound and size.
 __global__ void __launch_bounds__(256) spill_qent_kernel(
     const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_num, int q2k_stride,
     const int32_t* __restrict__ k2q_idx, const int32_t* __restrict__ k2q_num, int k2q_stride,
@@ -352,32 +354,39 @@ __global__ void __launch_bounds__(256) spill_qent_kernel(
   const int s = (int)(e - (size_t)q * q2k_stride);
   const size_t qrow = (size_t)bh * nb + q;
   int n = q2k_num[qrow];
+  int kv = q2k_idx[qrow * q2k_stride + s];  // inside the row; used only when s < n
   n = n < 0 ? 0 : (n > q2k_stride ? q2k_stride : n);
   if (s >= n) return;
-  int kv = q2k_idx[qrow * q2k_stride + s];
   kv = kv < 0 ? 0 : (kv >= nb ? nb - 1 : kv);
   const size_t krow = (size_t)bh * nb + kv;
+  int c = 0;
+  if (bounds) {
+    c = q / width;
+    c = c < nchunks ? c : nchunks - 1;
+  }
   int m = k2q_num[krow];
+  const int base = bounds ? kbase[(size_t)c * gridDim.y * nb + krow] : kbase[krow];
+  const int b0raw = bounds ? bounds[krow * (nchunks + 1) + c] : 0;
+  int vb = vbs[kv];
   m = m < 0 ? 0 : (m > k2q_stride ? k2q_stride : m);
   const int32_t* list = k2q_idx + krow * k2q_stride;
-  int lo = 0, hi = m;  // first position with list[pos] >= q
+  // first position with list[pos] >= q; vhi is the value at hi once hi has moved (q >= 0, so
+  // -1 never matches), which spares a last dependent load
+  int lo = 0, hi = m, vhi = -1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (list[mid] < q) lo = mid + 1; else hi = mid;
+    const int v = list[mid];
+    if (v < q) {
+      lo = mid + 1;
+    } else {
+      hi = mid;
+      vhi = v;
+    }
   }
-  const int t = (lo < m && list[lo] == q) ? lo : 0;
-  int slot;
-  if (bounds) {
-    int c = q / width;
-    c = c < nchunks ? c : nchunks - 1;
-    int b0 = bounds[krow * (nchunks + 1) + c];
-    b0 = b0 < 0 ? 0 : (b0 > m ? m : b0);
-    slot = kbase[(size_t)c * gridDim.y * nb + krow] + t - b0;
-  } else {
-    slot = kbase[krow] + t;
-  }
+  const int t = (lo < m && vhi == q) ? lo : 0;
+  const int b0 = b0raw < 0 ? 0 : (b0raw > m ? m : b0raw);
+  int slot = base + t - b0;
   slot = slot < 0 ? 0 : (slot >= cap ? cap - 1 : slot);
-  int vb = vbs[kv];
   vb = vb < 0 ? 0 : (vb > BLOCK ? BLOCK : vb);
   qent[qrow * q2k_stride + s] =
       (int64_t)(uint32_t)slot | ((int64_t)kv << 32) | ((int64_t)vb << 48);

@@ -125,6 +125,22 @@ def test_invert_duplicates_counts_and_rectangular():
     assert np.array_equal(k2q_idx.cpu().numpy(), ridx)
 
 
+@pytest.mark.parametrize("B,H,nq,nkv,K", [(1, 2, 3000, 50, 20), (1, 2, 40, 20000, 6)])
+def test_invert_wide_shapes(B, H, nq, nkv, K):
+    """Rows of more than 64 bitmap words (nq = 3000: the compaction takes its words in several
+    passes), and more kv blocks than one LDS column holds (nkv = 20000: the bitmap is set with
+    global atomics instead)."""
+    g = torch.Generator().manual_seed(nq + nkv)
+    idx = torch.randint(0, nkv, (B, H, nq, K), generator=g, dtype=torch.int32)
+    num = torch.randint(0, K + 1, (B, H, nq), generator=g, dtype=torch.int32)
+    say(f"[invert] nq={nq} nkv={nkv}")
+    k2q_idx, k2q_num = V.invert_indices(idx.to(DEV), num.to(DEV), nkv)
+    torch.cuda.synchronize()
+    ridx, rnum = O.invert_indices(idx, num, nkv)
+    assert np.array_equal(k2q_num.cpu().numpy(), rnum)
+    assert np.array_equal(k2q_idx.cpu().numpy(), ridx)
+
+
 # -----------------------------------------------------------------------------------------------
 # work order (bit-exact)
 # -----------------------------------------------------------------------------------------------
