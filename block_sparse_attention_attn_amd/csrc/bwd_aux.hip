@@ -201,9 +201,10 @@ void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream) {
 
 // Work order of one (b, h) (one 1024-thread workgroup): bitonic sort of 32-bit keys (inverted
 // bin << 14 | kv) in LDS, so the result is larger bins first and ascending kv inside a bin -- a
-// deterministic permutation. bin = count / bin_width, clamped to 18 bits.
-__device__ void order_block(const int32_t* __restrict__ num_in, int nb, int bin_width,
-                            int32_t* __restrict__ order, int bh) {
+// deterministic permutation. bin = cnt(kv) / bin_width, clamped to 18 bits.
+template <typename Cnt>
+__device__ void order_block_of(Cnt cnt, int nb, int bin_width, int32_t* __restrict__ order,
+                               int bh) {
   __shared__ uint32_t keys[ORDER_MAX_KV_BLOCKS];
   const int tid = threadIdx.x;
   int P = 1;
@@ -211,7 +212,7 @@ __device__ void order_block(const int32_t* __restrict__ num_in, int nb, int bin_
   for (int i = tid; i < P; i += 1024) {
     uint32_t key = 0xFFFFFFFFu;
     if (i < nb) {
-      int num = num_in[(size_t)bh * nb + i];
+      int num = cnt(i);
       num = num < 0 ? 0 : num;
       uint32_t bin = (uint32_t)(num / bin_width);
       bin = bin > 0x3FFFFu ? 0x3FFFFu : bin;
@@ -238,6 +239,11 @@ __device__ void order_block(const int32_t* __restrict__ num_in, int nb, int bin_
   }
   for (int r = tid; r < nb; r += 1024)
     order[(size_t)bh * nb + r] = bh * nb + (int)(keys[r] & 0x3FFFu);
+}
+
+__device__ void order_block(const int32_t* __restrict__ num_in, int nb, int bin_width,
+                            int32_t* __restrict__ order, int bh) {
+  order_block_of([&](int i) { return num_in[(size_t)bh * nb + i]; }, nb, bin_width, order, bh);
 }
 
 // Exclusive prefix sum of cnt(0 .. nb-1) into out[0 .. nb-1] (one 1024-thread workgroup). Thread t
@@ -315,6 +321,37 @@ __global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restri
 void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
                       hipStream_t stream) {
   hipLaunchKernelGGL(bwd_order_kernel, dim3(BH), dim3(1024), 0, stream, num, nb, bin_width, order);
+}
+
+// The work order of q-range chunk c of the kv-major kernel: items binned by the length of their
+// list's part inside the chunk (the positions chunk_bounds gives, clamped as the kv-major kernel
+// clamps them), so the items that run together on an XCD walk parts of equal length. One
+// 1024-thread workgroup per (b, h).
+__global__ void __launch_bounds__(1024) chunk_order_kernel(const int32_t* __restrict__ bounds,
+                                                           const int32_t* __restrict__ k2q_num,
+                                                           int k2q_stride, int nb, int nchunks,
+                                                           int c, int bin_width,
+                                                           int32_t* __restrict__ order) {
+  const int bh = blockIdx.x;
+  auto cnt = [&](int i) {
+    const size_t item = (size_t)bh * nb + i;
+    int n = k2q_num[item];
+    n = n > k2q_stride ? k2q_stride : n;
+    if (n <= 0) return 0;
+    const int32_t* cb = bounds + item * (nchunks + 1) + c;
+    int b0 = cb[0], b1 = cb[1];
+    b0 = b0 < 0 ? 0 : (b0 > n ? n : b0);
+    b1 = b1 < b0 ? b0 : (b1 > n ? n : b1);
+    return b1 - b0;
+  };
+  order_block_of(cnt, nb, bin_width, order, bh);
+}
+
+void launch_chunk_order(const int32_t* bounds, const int32_t* k2q_num, int k2q_stride, int BH,
+                        int nb, int nchunks, int c, int bin_width, int32_t* order,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(chunk_order_kernel, dim3(BH), dim3(1024), 0, stream, bounds, k2q_num,
+                     k2q_stride, nb, nchunks, c, bin_width, order);
 }
 
 // The index stage's per-head tasks in one launch: workgroup (bh, task) runs task blockIdx.y of the

@@ -524,7 +524,8 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       // the work orders and the dS slot bases: independent per-head tasks, one launch
       vsa::IndexTasks tasks{};
       if (uses_device_order(a)) {
-        if (!a->order)
+        // (with q-range chunks the DKDV stage orders the items per chunk instead)
+        if (!a->order && cb == 0)
           tasks.task[tasks.count++] = {vsa::IndexTask::ORDER, a->k2q_num, ws.kv_order};
         tasks.task[tasks.count++] = {vsa::IndexTask::ORDER, derive ? ws.q2k_num : a->q2k_num,
                                      ws.q_order};
@@ -569,8 +570,17 @@ int run_stage(const vsa_bwd_args* a, int stage, hipStream_t s) {
       // a chunked spill: each kv-major launch writes its chunk's tiles from slot 0 and the q-major
       // kernel turns them into dq for the chunk's q blocks before the next launch reuses them
       const int cs = spill_chunk_blocks_of(nb, a->chunk_blocks, a->dq_mode);
+      // with chunks the library's work order bins the items by the part of their list inside
+      // each chunk, so the items that run together walk parts of equal length
+      const bool chunk_orders = m.nchunks > 0 && !a->order && uses_device_order(a);
       for (int c = 0; c < launches; ++c) {
         m.chunk = c;
+        if (chunk_orders) {
+          vsa::launch_chunk_order(ws.chunk_bounds, a->k2q_num, a->max_q_blocks, BH, nb, m.nchunks,
+                                  c, VSA_ORDER_BIN_WIDTH, ws.kv_order, s);
+          const int r = launch_status("vsa_bwd chunk work order");
+          if (r != VSA_OK) return r;
+        }
         if (cs > 0) {
           m.kbase = ws.kbase + (size_t)c * BH * nb;
           m.ds_chunk_local = 1;

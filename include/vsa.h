@@ -160,7 +160,9 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  *                    subtraction, then division), then -Delta * 2^-(eo + ev) of its 64 rows,
  *                    with the head's pp, c, eo, ev from VSA_WS_SCALES; left holding them after
  *                    the call
- *   VSA_WS_KV_ORDER  int32 [B*H*nb] kv-major work order (when the library computes it)
+ *   VSA_WS_KV_ORDER  int32 [B*H*nb] kv-major work order (when the library computes it; with
+ *                    q-range chunks the DKDV stage rewrites it before each chunk's launch, by
+ *                    the lengths of the lists' parts in that chunk)
  *   VSA_WS_Q_ORDER   int32 [B*H*nb] q-major work order (when the library computes it)
  * only when the q2k lists are derived (q2k_stride argument 0):
  *   VSA_WS_Q2K_NUM   int32 [B, H, nb]
@@ -297,8 +299,9 @@ typedef enum {
   VSA_BWD_INDEX = 1,       /* q2k derivation (if needed), the length-binned work orders, in
                               VSA_DQ_SPILL mode the dS slot tables, with q-range chunks the
                               chunk bounds */
-  VSA_BWD_DKDV = 2,        /* kv-major kernel (one launch per chunk): dk, dv (and the dS tiles
-                              in VSA_DQ_SPILL mode) */
+  VSA_BWD_DKDV = 2,        /* kv-major kernel (one launch per chunk, each after its chunk's
+                              work order when the library orders the items): dk, dv (and the
+                              dS tiles in VSA_DQ_SPILL mode) */
   VSA_BWD_DQ = 3           /* q-major kernel (VSA_DQ_RECOMPUTE: one launch per chunk):
                               dq = bf16(sm_scale * dS K) */
 } vsa_bwd_stage_id;

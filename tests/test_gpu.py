@@ -728,6 +728,45 @@ def test_backward_any_order_gives_identical_bits(mode):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("mode", ["recompute", "spill"])
+def test_chunk_work_orders(mode):
+    """With q-range chunks and the library's work order (96 kv blocks, chunks of 16 q blocks) the
+    kv-major items are ordered per chunk, by the length of their list's part in the chunk: the
+    workspace holds the last chunk's order, equal to the oracle's work order over those lengths;
+    every output is bitwise that of the same call under a caller-given identity order, and
+    matches the oracle."""
+    c = workloads.make_case(1, 2, 96, None, topk_choices=[3, 8, 13, 21], seed=71,
+                            vbs=[64] * 95 + [29], name="chunk orders")
+    d = to_dev(c)
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
+    R = 16
+    extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"]) if mode == "spill" else {}
+    say(f"[backward] per-chunk work orders ({mode})")
+    plan = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                     out=(nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"])),
+                     dq_mode=MODES[mode], chunk_blocks=R, **extra)
+    got = plan.run()
+    ident = torch.arange(c.B * c.H * c.nb, dtype=torch.int32, device=DEV)
+    other = V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                      order=ident, dq_mode=MODES[mode], chunk_blocks=R, **extra).run()
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), got, other):
+        assert torch.equal(x, y), name
+    # the last chunk's part of each k2q list: its q blocks >= (C - 1) * R
+    idx, num = k2q_idx.cpu().numpy(), k2q_num.cpu().numpy()
+    last = (c.nb + R - 1) // R - 1
+    pos = np.arange(idx.shape[-1])
+    part = ((idx >= last * R) & (pos < num[..., None])).sum(-1).astype(np.int32)
+    n = c.B * c.H * c.nb
+    assert np.array_equal(plan.region(V.WS_KV_ORDER, n).cpu().numpy(),
+                          O.work_order(torch.from_numpy(part), V.ORDER_BIN_WIDTH))
+    rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    check_close("dq", got[0], rdq)
+    check_close("dk", got[1], rdk)
+    check_close("dv", got[2], rdv)
+
+
 def test_nondefault_stream():
     c = workloads.config(1)
     d = to_dev(c)
