@@ -374,8 +374,9 @@ void launch_index_tasks(const IndexTasks& t, int BH, int nb, int bin_width, int 
 
 
 // One thread per q2k entry (bh, q, s): binary search of q in the ascending k2q row of its kv
-// block. A q missing from that row (a caller-contract violation: k2q is not the inverse of q2k,
-// or not ascending) gets the row's first slot, so every slot stays inside the head's range. With
+// block (with chunks, only between the bounds of q's chunk in that row). A q missing from that
+// row (a caller-contract violation: k2q is not the inverse of q2k, or not ascending) gets the
+// first slot of the row (of its chunk's part), so every slot stays inside the head's range. With
 // chunks the slot is numbered inside the chunk of q (launch_spill_qent). The kernel is bound by
 // the latency of its dependent loads, so the independent ones are issued together: the entry
 // with its row's count, then the kv block's list length, slot base, chunk bound and size.
@@ -404,12 +405,17 @@ __global__ void __launch_bounds__(256) spill_qent_kernel(
   int m = k2q_num[krow];
   const int base = bounds ? kbase[(size_t)c * gridDim.y * nb + krow] : kbase[krow];
   const int b0raw = bounds ? bounds[krow * (nchunks + 1) + c] : 0;
+  const int b1raw = bounds ? bounds[krow * (nchunks + 1) + c + 1] : 0;
   int vb = vbs[kv];
   m = m < 0 ? 0 : (m > k2q_stride ? k2q_stride : m);
+  // with chunks, q (in chunk c) sits between the chunk's bounds in the row, clamped as the
+  // kv-major kernel clamps them
+  const int b0 = bounds ? (b0raw < 0 ? 0 : (b0raw > m ? m : b0raw)) : 0;
+  const int b1 = bounds ? (b1raw < b0 ? b0 : (b1raw > m ? m : b1raw)) : m;
   const int32_t* list = k2q_idx + krow * k2q_stride;
-  // first position with list[pos] >= q; vhi is the value at hi once hi has moved (q >= 0, so
-  // -1 never matches), which spares a last dependent load
-  int lo = 0, hi = m, vhi = -1;
+  // first position in [b0, b1) with list[pos] >= q; vhi is the value at hi once hi has moved
+  // (q >= 0, so -1 never matches), which spares a last dependent load
+  int lo = b0, hi = b1, vhi = -1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     const int v = list[mid];
@@ -420,8 +426,7 @@ __global__ void __launch_bounds__(256) spill_qent_kernel(
       vhi = v;
     }
   }
-  const int t = (lo < m && vhi == q) ? lo : 0;
-  const int b0 = b0raw < 0 ? 0 : (b0raw > m ? m : b0raw);
+  const int t = (lo < b1 && vhi == q) ? lo : b0;
   int slot = base + t - b0;
   slot = slot < 0 ? 0 : (slot >= cap ? cap - 1 : slot);
   vb = vb < 0 ? 0 : (vb > BLOCK ? BLOCK : vb);
