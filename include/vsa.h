@@ -150,8 +150,10 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream);
  * parameter 8 (the launch header's order kernel). Here the order also keeps the items that run
  * together on one XCD at equal list lengths, so their ascending walks over Q/dO stay in step and
  * share that XCD's L2; on MI355X that pays from a few hundred kv blocks on, and a narrower bin
- * keeps the walks closer. The order never changes the results, which are bitwise identical for
- * any order.
+ * keeps the walks closer. When the kv-major kernel runs in chunks (below), the library orders
+ * its items again before each chunk's launch, by the lengths of their lists' parts inside that
+ * chunk (a caller's order is used as given for every chunk). The order never changes the
+ * results, which are bitwise identical for any order.
  *
  * Workspace (device, vsa_bwd_workspace_bytes() bytes, contents on entry irrelevant), regions in
  * this order, each at a 256-byte boundary (vsa_bwd_workspace_offset() gives the offsets); a
@@ -287,7 +289,8 @@ int vsa_bwd(const vsa_bwd_args* a, void* stream);
  * validates like vsa_bwd. Run on one stream in the order PREPROCESS, INDEX, DKDV, DQ, they
  * enqueue exactly the kernels vsa_bwd enqueues and produce the same results. INDEX derives the
  * q2k lists when they are not given, computes the work orders when num_kv_blocks is in
- * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS], builds the dS slot tables in
+ * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS] (with q-range chunks, DKDV orders the
+ * kv-major items per chunk instead), builds the dS slot tables in
  * VSA_DQ_SPILL mode and the chunk bounds when the kv-major kernel runs in q-range chunks;
  * otherwise it enqueues nothing. In VSA_DQ_RECOMPUTE mode DKDV and DQ only read
  * what PREPROCESS and INDEX wrote and may run in either order; in VSA_DQ_SPILL mode DQ reads the
