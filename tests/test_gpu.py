@@ -125,11 +125,12 @@ def test_invert_duplicates_counts_and_rectangular():
     assert np.array_equal(k2q_idx.cpu().numpy(), ridx)
 
 
-@pytest.mark.parametrize("B,H,nq,nkv,K", [(1, 2, 3000, 50, 20), (1, 2, 40, 20000, 6)])
+@pytest.mark.parametrize("B,H,nq,nkv,K", [(1, 2, 3000, 50, 20), (1, 1, 70, 16384, 9),
+                                         (1, 2, 40, 20000, 6)])
 def test_invert_wide_shapes(B, H, nq, nkv, K):
     """Rows of more than 64 bitmap words (nq = 3000: the compaction takes its words in several
-    passes), and more kv blocks than one LDS column holds (nkv = 20000: the bitmap is set with
-    global atomics instead)."""
+    passes), the largest LDS column (nkv = 16384: 64 KiB), and more kv blocks than one LDS column
+    holds (nkv = 20000: the bitmap is set with global atomics instead)."""
     g = torch.Generator().manual_seed(nq + nkv)
     idx = torch.randint(0, nkv, (B, H, nq, K), generator=g, dtype=torch.int32)
     num = torch.randint(0, K + 1, (B, H, nq), generator=g, dtype=torch.int32)
