@@ -768,6 +768,38 @@ def test_chunk_work_orders(mode):
     check_close("dv", got[2], rdv)
 
 
+@pytest.mark.parametrize("mode", ["recompute", "spill"])
+@pytest.mark.parametrize("chunk", [0, 24])
+def test_stages_match_one_call(mode, chunk):
+    """The four stages enqueued one at a time (the path the benchmark times) give the bits of the
+    one-call backward, with and without chunks (80 kv blocks: the library's work orders run)."""
+    c = workloads.make_case(1, 2, 80, None, topk_choices=[5, 9, 16], seed=73,
+                            vbs=[64] * 79 + [45], name="stages")
+    d = to_dev(c)
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"])
+    k2q_idx, k2q_num = V.invert_indices(d["q2k_idx"], d["q2k_num"], c.nb)
+    extra = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"]) if mode == "spill" else {}
+    say(f"[stages] {mode}, chunks {chunk}")
+
+    def plan():
+        return V.BwdPlan(d["do"], d["q"], d["k"], d["v"], o, lse, k2q_idx, k2q_num, d["vbs"],
+                         out=(nan_like(d["q"]), nan_like(d["k"]), nan_like(d["v"])),
+                         dq_mode=MODES[mode], chunk_blocks=chunk, **extra)
+
+    first = plan()
+    one = first.run()
+    staged = plan()
+    for s_ in (staged.PREPROCESS, staged.INDEX, staged.DKDV, staged.DQ):
+        staged.stage(s_)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), one, (staged.dq, staged.dk, staged.dv)):
+        assert torch.equal(x, y), name
+    rdq, rdk, rdv = O.backward(c.q, c.k, c.v, c.do, c.q2k_idx, c.q2k_num, c.vbs, c.sm_scale)
+    check_close("dq", one[0], rdq)
+    check_close("dk", one[1], rdk)
+    check_close("dv", one[2], rdv)
+
+
 def test_nondefault_stream():
     c = workloads.config(1)
     d = to_dev(c)
