@@ -37,7 +37,9 @@
 //     unscaled: the block max is taken on raw scores and each exponent is one fma.
 //   * Long lists run in kv-range chunks, one launch each, each wave carrying its running O^T,
 //     max and sum to the next launch exactly: the workgroups on an XCD then share one window of
-//     K/V tiles at a time, and the results are those of one launch, bit for bit.
+//     K/V tiles at a time, and the results are those of one launch, bit for bit. Before each
+//     chunk the items are ordered by the length of their list's part in it (length bins), so the
+//     items that run together on an XCD walk parts of equal length.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -75,8 +77,12 @@ fwd_kernel(FwdParams p) {
   const int grp = lane >> 4;
   const int t16 = lane & 15;
 
-  const int item = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);  // (bh, q block)
+  int item = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);  // (bh, q block)
   if (item >= p.BH * p.nb) return;
+  if (p.order) {  // the launch's work order (kv-range chunks: items binned per chunk)
+    item = ld_const(p.order, item);
+    if (item < 0 || item >= p.BH * p.nb) return;  // a malformed entry: skip, never fault
+  }
   const int bh = item / p.nb;
   const int qb = item - bh * p.nb;
   int n = ld_const(p.q2k_num, item);

@@ -151,6 +151,14 @@ size_t fwd_amax_bytes(size_t bh, int seqlen) {  // per head, then per 64-row til
 size_t fwd_v16_bytes(size_t bh, int seqlen) {
   return align256(bh * (size_t)seqlen * vsa::HEAD_DIM * 2);
 }
+size_t fwd_state_bytes(size_t items) {
+  return align256(items * 4 * (size_t)vsa::FWD_STATE_FLOATS * sizeof(float));
+}
+// with kv-range chunks the items are ordered per chunk by the length of their list's part in it,
+// where the sort fits one workgroup (the backward's order limits)
+bool fwd_chunk_orders(int nb) {
+  return nb >= VSA_ORDER_MIN_KV_BLOCKS && nb <= VSA_ORDER_MAX_KV_BLOCKS;
+}
 
 }  // namespace
 
@@ -164,8 +172,8 @@ size_t vsa_fwd_workspace_bytes(int batch, int heads, int seqlen, int kv_chunk_bl
   const int ck = fwd_chunk_kv_blocks(nb, kv_chunk_blocks);
   if (ck == 0) return v16;
   const size_t items = bh * nb;
-  return v16 + fwd_bounds_bytes(items, (nb + ck - 1) / ck) +
-         align256(items * 4 * (size_t)vsa::FWD_STATE_FLOATS * sizeof(float));
+  return v16 + fwd_bounds_bytes(items, (nb + ck - 1) / ck) + fwd_state_bytes(items) +
+         (fwd_chunk_orders(nb) ? align256(items * sizeof(int32_t)) : 0);
 }
 
 int vsa_fwd_check(const vsa_fwd_args* a) {
@@ -224,11 +232,14 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
     if (r != VSA_OK) return r;
   }
   ws += fwd_amax_bytes(p.BH, p.S) + fwd_v16_bytes(p.BH, p.S);
+  int32_t* order = nullptr;
   if (p.nchunks > 0) {
     const size_t items = (size_t)p.BH * p.nb;
     int32_t* bounds = (int32_t*)ws;
     p.chunk_bounds = bounds;
     p.state = (float*)(ws + fwd_bounds_bytes(items, p.nchunks));
+    if (fwd_chunk_orders(p.nb))
+      order = (int32_t*)(ws + fwd_bounds_bytes(items, p.nchunks) + fwd_state_bytes(items));
     vsa::launch_chunk_bounds(a->q2k_idx, a->q2k_num, a->q2k_stride, (int)items, p.nchunks, ck,
                              bounds, s);
     const int r = launch_status("vsa_fwd chunk bounds");
@@ -237,6 +248,13 @@ int vsa_fwd(const vsa_fwd_args* a, void* stream) {
   const int launches = p.nchunks > 0 ? p.nchunks : 1;
   for (int c = 0; c < launches; ++c) {
     p.chunk = c;
+    if (order) {  // this chunk's items binned by the length of their list's part in it
+      vsa::launch_chunk_order(p.chunk_bounds, a->q2k_num, a->q2k_stride, p.BH, p.nb, p.nchunks, c,
+                              VSA_ORDER_BIN_WIDTH, order, s);
+      const int r = launch_status("vsa_fwd chunk work order");
+      if (r != VSA_OK) return r;
+      p.order = order;
+    }
     vsa::launch_fwd(p, s);
     const int r = launch_status("vsa_fwd");
     if (r != VSA_OK) return r;

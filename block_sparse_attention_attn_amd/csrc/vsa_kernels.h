@@ -40,6 +40,8 @@ struct FwdParams {
   const int32_t* chunk_bounds = nullptr;  // [BH * nb, nchunks + 1]
   float* state = nullptr;                 // [BH * nb, 4 waves, FWD_STATE_FLOATS]
   int chunk = 0, nchunks = 0;
+  // work order of this launch: a permutation of the BH * nb item ids (nullptr: identity)
+  const int32_t* order = nullptr;
 };
 // per wave: 64 lane-major rows of O^T accumulator elements, then the running max and sum rows
 constexpr int FWD_STATE_FLOATS = 66 * 64;

@@ -73,16 +73,20 @@ int vsa_invert_indices(const int32_t* q2k_idx, const int32_t* q2k_num, int batch
  * list is ascending) and carries each wave's running O, max and sum to the next launch in fp32
  * in the workspace, exactly: the results are bitwise those of one launch. The workgroups running
  * together on one XCD then share a window of R kv blocks, so their K/V tiles stay in its L2.
- * Any list order is correct; ascending lists give the locality. kv_chunk_blocks < 0: never
- * chunk.
+ * Any list order is correct; ascending lists give the locality. With num_kv_blocks in
+ * [VSA_ORDER_MIN_KV_BLOCKS, VSA_ORDER_MAX_KV_BLOCKS] each launch also orders its items by the
+ * length of their list's part in its chunk (length bins of VSA_ORDER_BIN_WIDTH), so the items
+ * running together walk parts of equal length; the order never changes the results.
+ * kv_chunk_blocks < 0: never chunk.
  *
  * The P v product runs on fp16 operands (same MFMA rate as bf16, 8x finer rounding of P): a
  * pre-pass writes an fp16 copy of v into the workspace, each head scaled by the power of two that
  * brings its largest |v| into [2^14, 2^15), so every bf16 value of v with |v| >= 2^-28 * max|v|
  * of its head is copied exactly; o is scaled back exactly. Workspace (vsa_fwd_workspace_bytes,
  * 256-byte aligned regions): uint32 [B*H] per-head and [B*H*nb] per-tile max |v| bits, fp16
- * [B, H, S, 128] scaled copy of v, then with chunks int32 [B*H*nb, C+1] chunk bounds and fp32 [B*H*nb, 4, 66, 64]
- * per-wave state. */
+ * [B, H, S, 128] scaled copy of v, then with chunks int32 [B*H*nb, C+1] chunk bounds, fp32
+ * [B*H*nb, 4, 66, 64] per-wave state and (when the items are ordered per chunk) the int32
+ * [B*H*nb] work order. */
 #define VSA_FWD_CHUNK_KV_BLOCKS 512
 typedef struct {
   const void* q;          /* bf16 [B, H, S, 128] */

@@ -167,17 +167,20 @@ def test_workspace_chunk_regions():
     o = offs(1, 1, 64 * 10, 0, 10)
     assert o[V.WS_STATS] == o[V.WS_CHUNK_BOUNDS]
     # the forward: per-head max |v| bits and the fp16 copy of v, then with kv-range chunks the
-    # bounds and per-wave state of 66 x 64 floats
+    # bounds, per-wave state of 66 x 64 floats and the work order
     def v16(bh, S):
         return a256(bh * 4) + a256(bh * (S // 64) * 4) + a256(bh * S * 128 * 2)
     nbf = V.CHUNK_MIN_KV_BLOCKS
     cf = -(-nbf // V.FWD_CHUNK_KV_BLOCKS)
+    # (from VSA_ORDER_MIN_KV_BLOCKS kv blocks on, the chunks' int32 work order follows)
     assert V.fwd_workspace_bytes(1, 2, 64 * nbf) == (v16(2, 64 * nbf) + a256(2 * nbf * (cf + 1) * 4)
-                                                     + 2 * nbf * 4 * 66 * 64 * 4)
+                                                     + 2 * nbf * 4 * 66 * 64 * 4 + a256(2 * nbf * 4))
     assert V.fwd_workspace_bytes(1, 2, 64 * nbf, -1) == v16(2, 64 * nbf)
     assert V.fwd_workspace_bytes(1, 2, 64 * 512) == v16(2, 64 * 512)
     assert V.fwd_workspace_bytes(1, 1, 64 * 10, 4) == (v16(1, 640) + a256(10 * 4 * 4)
                                                        + 10 * 4 * 66 * 64 * 4)
+    assert V.fwd_workspace_bytes(1, 1, 64 * 80, 16) == (v16(1, 64 * 80) + a256(80 * 6 * 4)
+                                                        + 80 * 4 * 66 * 64 * 4 + a256(80 * 4))
     assert V.fwd_workspace_bytes(1, 1, 63) == 0
     assert V.invert_workspace_bytes(2, 3, 100, 50) == ((2 * 3 * 50 * 4 * 4 + 255) // 256) * 256
     assert V.invert_workspace_bytes(1, 1, 0, 1) == 0

@@ -228,6 +228,35 @@ def test_forward_kv_range_chunks(case, chunk, shuffle):
         _fwd_compare(c, d, o, lse)
 
 
+def test_forward_chunk_work_orders():
+    """kv-range chunks with the library's per-chunk work order (96 kv blocks, chunks of 16): o and
+    lse are bitwise those of one launch and match the oracle; the workspace's order (the last
+    chunk's) equals the oracle's work order over the lengths of the lists' parts in that chunk."""
+    c = workloads.make_case(1, 2, 96, None, topk_choices=[3, 8, 13, 21], seed=75,
+                            vbs=[64] * 95 + [29], name="forward chunk orders")
+    d = to_dev(c)
+    say("[forward] per-chunk work orders")
+    one = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"],
+                    kv_chunk_blocks=-1)
+    R = 16
+    nbytes = V.fwd_workspace_bytes(c.B, c.H, c.S, R)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    o, lse = V.forward(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"], d["vbs"],
+                       kv_chunk_blocks=R, workspace=ws, out=(nan_like(d["q"]), nan_like(one[1])))
+    torch.cuda.synchronize()
+    assert torch.equal(o, one[0]) and torch.equal(lse, one[1])
+    # the order is the workspace's last region: [B*H*nb] int32, 256-byte aligned
+    n = c.B * c.H * c.nb
+    tail = -(-n * 4 // 256) * 256
+    order = ws[nbytes - tail:].view(torch.int32)[:n].cpu().numpy()
+    idx, num = c.q2k_idx.numpy(), c.q2k_num.numpy()
+    last = -(-c.nb // R) - 1
+    pos = np.arange(idx.shape[-1])
+    part = ((idx >= last * R) & (pos < num[..., None])).sum(-1).astype(np.int32)
+    assert np.array_equal(order, O.work_order(torch.from_numpy(part), V.ORDER_BIN_WIDTH))
+    _fwd_compare(c, d, o, lse)
+
+
 def test_forward_v_magnitudes_per_head():
     """The P V product runs on an fp16 copy of v scaled per head by a power of two: heads whose
     v is tiny (3e-30), huge (1e30), all zero, or has one large outlier, all against the oracle on
