@@ -26,7 +26,8 @@ import torch
 
 __all__ = [
     "BLOCK", "HEAD_DIM", "ORDER_MIN_KV_BLOCKS", "ORDER_BIN_WIDTH", "CHUNK_MIN_KV_BLOCKS",
-    "CHUNK_BLOCKS", "SPILL_CHUNK_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
+    "CHUNK_BLOCKS", "SPILL_CHUNK_BLOCKS", "FWD_CHUNK_KV_BLOCKS", "FWD_CHUNK_MIN_KV_BLOCKS",
+    "fwd_workspace_bytes", "library_path", "is_built", "is_supported",
     "invert_indices", "forward", "backward_from_k2q", "backward", "bwd_order",
     "bwd_workspace_bytes", "bwd_workspace_offset", "invert_workspace_bytes", "BwdPlan",
     "DQ_RECOMPUTE", "DQ_SPILL", "default_dq_mode", "backward_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -40,6 +41,7 @@ CHUNK_MIN_KV_BLOCKS = 4096  # VSA_CHUNK_MIN_KV_BLOCKS
 CHUNK_BLOCKS = 1024       # VSA_CHUNK_BLOCKS
 SPILL_CHUNK_BLOCKS = 512  # VSA_SPILL_CHUNK_BLOCKS
 FWD_CHUNK_KV_BLOCKS = 512   # VSA_FWD_CHUNK_KV_BLOCKS
+FWD_CHUNK_MIN_KV_BLOCKS = 1024  # VSA_FWD_CHUNK_MIN_KV_BLOCKS
 ORDER_MAX_KV_BLOCKS = 16384
 _LOG2E = 1.4426950408889634
 
@@ -261,7 +263,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q2k_idx: torch.Te
             kv_chunk_blocks: int = 0, workspace: Optional[torch.Tensor] = None):
     """Block-sparse forward: returns ``(o bf16 [B,H,S,128], lse fp32 [B,H,S] M form)``.
     ``kv_chunk_blocks``: kv blocks per kv-range chunk (0: the library's choice, chunks of
-    FWD_CHUNK_KV_BLOCKS from CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch). The
+    FWD_CHUNK_KV_BLOCKS from FWD_CHUNK_MIN_KV_BLOCKS kv blocks on; negative: one launch). The
     workspace (``fwd_workspace_bytes``: the fp16 copy of v, and the chunk state) is allocated
     here unless given."""
     _need_gpu(q, "q")

@@ -134,7 +134,7 @@ int fwd_chunk_kv_blocks(int nb, int kv_chunk_blocks) {
   if (kv_chunk_blocks < 0) return 0;
   const int ck = kv_chunk_blocks > 0
                      ? kv_chunk_blocks
-                     : (nb >= VSA_CHUNK_MIN_KV_BLOCKS ? VSA_FWD_CHUNK_KV_BLOCKS : 0);
+                     : (nb >= VSA_FWD_CHUNK_MIN_KV_BLOCKS ? VSA_FWD_CHUNK_KV_BLOCKS : 0);
   return ck > 0 && ck < nb ? ck : 0;
 }
 

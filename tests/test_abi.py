@@ -54,7 +54,9 @@ def test_binding_constants_match_the_header():
                         ("VSA_ORDER_BIN_WIDTH", V.ORDER_BIN_WIDTH),
                         ("VSA_CHUNK_MIN_KV_BLOCKS", V.CHUNK_MIN_KV_BLOCKS),
                         ("VSA_CHUNK_BLOCKS", V.CHUNK_BLOCKS),
-                        ("VSA_SPILL_CHUNK_BLOCKS", V.SPILL_CHUNK_BLOCKS)):
+                        ("VSA_SPILL_CHUNK_BLOCKS", V.SPILL_CHUNK_BLOCKS),
+                        ("VSA_FWD_CHUNK_KV_BLOCKS", V.FWD_CHUNK_KV_BLOCKS),
+                        ("VSA_FWD_CHUNK_MIN_KV_BLOCKS", V.FWD_CHUNK_MIN_KV_BLOCKS)):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == value, name
     m = re.search(r"#define\s+VSA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
@@ -170,13 +172,13 @@ def test_workspace_chunk_regions():
     # bounds, per-wave state of 66 x 64 floats and the work order
     def v16(bh, S):
         return a256(bh * 4) + a256(bh * (S // 64) * 4) + a256(bh * S * 128 * 2)
-    nbf = V.CHUNK_MIN_KV_BLOCKS
+    nbf = V.FWD_CHUNK_MIN_KV_BLOCKS
     cf = -(-nbf // V.FWD_CHUNK_KV_BLOCKS)
     # (from VSA_ORDER_MIN_KV_BLOCKS kv blocks on, the chunks' int32 work order follows)
     assert V.fwd_workspace_bytes(1, 2, 64 * nbf) == (v16(2, 64 * nbf) + a256(2 * nbf * (cf + 1) * 4)
                                                      + 2 * nbf * 4 * 66 * 64 * 4 + a256(2 * nbf * 4))
     assert V.fwd_workspace_bytes(1, 2, 64 * nbf, -1) == v16(2, 64 * nbf)
-    assert V.fwd_workspace_bytes(1, 2, 64 * 512) == v16(2, 64 * 512)
+    assert V.fwd_workspace_bytes(1, 2, 64 * (nbf - 1)) == v16(2, 64 * (nbf - 1))
     assert V.fwd_workspace_bytes(1, 1, 64 * 10, 4) == (v16(1, 640) + a256(10 * 4 * 4)
                                                        + 10 * 4 * 66 * 64 * 4)
     assert V.fwd_workspace_bytes(1, 1, 64 * 80, 16) == (v16(1, 64 * 80) + a256(80 * 6 * 4)
