@@ -255,6 +255,18 @@ def test_forward_chunk_work_orders():
     part = ((idx >= last * R) & (pos < num[..., None])).sum(-1).astype(np.int32)
     assert np.array_equal(order, O.work_order(torch.from_numpy(part), V.ORDER_BIN_WIDTH))
     _fwd_compare(c, d, o, lse)
+    # lists in no particular order: the chunks partition them by position, the order bins the
+    # parts, and o, lse stay bitwise those of one launch over the same lists
+    g = torch.Generator().manual_seed(5)
+    rows = c.q2k_idx.reshape(-1, c.q2k_idx.shape[-1]).clone()
+    for i, k_ in enumerate(c.q2k_num.reshape(-1).tolist()):
+        rows[i, :k_] = rows[i, :k_][torch.randperm(k_, generator=g)]
+    shuf = rows.reshape(c.q2k_idx.shape).to(DEV)
+    one = V.forward(d["q"], d["k"], d["v"], shuf, d["q2k_num"], d["vbs"], kv_chunk_blocks=-1)
+    o2, lse2 = V.forward(d["q"], d["k"], d["v"], shuf, d["q2k_num"], d["vbs"], kv_chunk_blocks=R,
+                         out=(nan_like(d["q"]), nan_like(one[1])))
+    torch.cuda.synchronize()
+    assert torch.equal(o2, one[0]) and torch.equal(lse2, one[1])
 
 
 def test_forward_v_magnitudes_per_head():
