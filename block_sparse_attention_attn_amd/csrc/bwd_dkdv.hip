@@ -460,6 +460,19 @@ bwd_dkdv_kernel(BwdParams p) {
                            : ld_const(hs, SC_EQ) - ld_const(hs, SC_ES);
   // this wave's tensor (dV for wq 0, dK for wq 1) in the chunk partial sums: [64][128] fp32
   float* part = p.part ? p.part + ((size_t)item * 2 + wq) * (BLOCK * HEAD_DIM) : nullptr;
+  // the chunks before: all of this lane's partial sums are loaded before any store below (a
+  // store to the partial sums may alias a later load, which would otherwise wait for it: one
+  // memory round trip per group of four)
+  float prev[4][4][4];
+  if (!first) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          prev[nt][c][e] = part[(32 * wk + 8 * c + 4 * g + e) * HEAD_DIM + 32 * nt + l32];
+  }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int d = 32 * nt + l32;
@@ -471,7 +484,7 @@ bwd_dkdv_kernel(BwdParams p) {
         const float mine = wq == 0 ? dv_acc[nt][4 * c + e] : dk_acc[nt][4 * c + e];
         const int kv = 32 * wk + 8 * c + 4 * g + e;
         float sum = mine + o[e];
-        if (!first) sum += part[kv * HEAD_DIM + d];
+        if (!first) sum += prev[nt][c][e];
         if (last)  // padded kv rows are exactly zero by definition
           outp[(size_t)kv * HEAD_DIM + d] =
               kv < vb ? (bf16)__builtin_ldexpf(sum * oscale, oexp) : (bf16)0.0f;

@@ -286,6 +286,16 @@ bwd_dq_kernel(BwdParams p) {
                        : nullptr;
   const float sc = p.sm_scale;
   const int oexp = ld_const(hs, SC_EK) - ld_const(hs, SC_ES);  // dq = sm_scale dQ' 2^(ek - es)
+  // the chunks before: this lane's partial sums, all loaded before any store below (a store may
+  // alias a later load, which would otherwise wait for it)
+  f32x4 prev[2][4];
+  if (!first) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        prev[u][c] = *(const f32x4*)(prow + 32 * ((wk == 0 ? 0 : 2) + u) + 8 * c + 4 * g);
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int mt = (wk == 0 ? 0 : 2) + u;  // my tiles
@@ -297,7 +307,7 @@ bwd_dq_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e)
         sum[e] = (wk == 0 ? dq_acc[u][4 * c + e] : dq_acc[2 + u][4 * c + e]) + o[e];
       const int d0 = 32 * mt + 8 * c + 4 * g;
-      if (!first) sum += *(const f32x4*)(prow + d0);
+      if (!first) sum += prev[u][c];
       if (last) {
         union {
           bf16 b[4];
