@@ -73,6 +73,9 @@ __global__ void __launch_bounds__(256) bwd_stats_kernel(BwdPreParams p) {
   float* rec = p.lse_delta + ((size_t)bh * p.nb + blk) * LD_RECORD_FLOATS;
   uint32_t mq = 0, mk = 0, mv = 0, mo = 0;
   float n2v = 0.0f, n2o = 0.0f, md = 0.0f;
+  // the stores come after every load: as far as the compiler knows they may alias the inputs,
+  // and a load placed after a store would wait for it
+  float dl[4];
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const size_t row = row0 + pass * 16 + rr;
@@ -97,8 +100,13 @@ __global__ void __launch_bounds__(256) bwd_stats_kernel(BwdPreParams p) {
     n2v = fmaxf(n2v, row_sum16(sv));
     n2o = fmaxf(n2o, row_sum16(so));
     md = fmaxf(md, fabsf(delta));
-    if (c == 0) rec[BLOCK + pass * 16 + rr] = -delta;
+    dl[pass] = delta;
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    if (c == 0) rec[BLOCK + pass * 16 + rr] = -dl[pass];
     if (empty) {
+      const size_t at = (row0 + pass * 16 + rr) * HEAD_DIM + c * 8;
       *(bf16x8*)(p.dk + at) = bf16x8{};
       *(bf16x8*)(p.dv + at) = bf16x8{};
     }
@@ -177,14 +185,25 @@ __global__ void __launch_bounds__(256) bwd_convert_kernel(BwdPreParams p) {
   const float cc = __uint_as_float((uint32_t)ld_const(sc, SC_C));
   const size_t row0 = (size_t)bh * p.S + (size_t)blk * BLOCK;
   float* rec = p.lse_delta + ((size_t)bh * p.nb + blk) * LD_RECORD_FLOATS;
+  // every load before any store: the copies may alias the inputs as far as the compiler knows,
+  // so a load placed after a store would wait for it
+  bf16x8 xq[4], xk[4], xd[4], xv[4];
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const size_t at = (row0 + pass * 16 + rr) * HEAD_DIM + c * 8;
+    xq[pass] = *(const bf16x8*)(p.q + at);
+    xk[pass] = *(const bf16x8*)(p.k + at);
+    xd[pass] = *(const bf16x8*)(p.dout + at);
+    if (p.v16) xv[pass] = *(const bf16x8*)(p.v + at);
+  }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const size_t row = row0 + pass * 16 + rr;
     const size_t at = row * HEAD_DIM + c * 8;
-    *(f16x8*)(p.q16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.q + at), eq);
-    *(f16x8*)(p.k16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.k + at), ek);
-    *(f16x8*)(p.do16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.dout + at), eo);
-    if (p.v16) *(f16x8*)(p.v16 + at) = bf16x8_to_f16x8(*(const bf16x8*)(p.v + at), ev);
+    *(f16x8*)(p.q16 + at) = bf16x8_to_f16x8(xq[pass], eq);
+    *(f16x8*)(p.k16 + at) = bf16x8_to_f16x8(xk[pass], ek);
+    *(f16x8*)(p.do16 + at) = bf16x8_to_f16x8(xd[pass], eo);
+    if (p.v16) *(f16x8*)(p.v16 + at) = bf16x8_to_f16x8(xv[pass], ev);
     if (c == 0) {
       const int r = pass * 16 + rr;
       rec[r] = ((float)pp - p.lse[row]) / cc;
