@@ -342,20 +342,20 @@ void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t
   hipLaunchKernelGGL(bwd_order_kernel, dim3(BH), dim3(1024), 0, stream, num, nb, bin_width, order);
 }
 
-// The work order of q-range chunk c of the kv-major kernel: items binned by the length of their
-// list's part inside the chunk (the positions chunk_bounds gives, clamped as the kv-major kernel
-// clamps them), so the items that run together on an XCD walk parts of equal length. One
-// 1024-thread workgroup per (b, h).
+// The work order of chunk c of chunked launches (the kv-major kernel over k2q lists, the forward
+// over q2k lists): items binned by the length of their list's part inside the chunk (the
+// positions chunk_bounds gives, clamped as both kernels clamp them), so the items that run
+// together on an XCD walk parts of equal length. One 1024-thread workgroup per (b, h).
 __global__ void __launch_bounds__(1024) chunk_order_kernel(const int32_t* __restrict__ bounds,
-                                                           const int32_t* __restrict__ k2q_num,
-                                                           int k2q_stride, int nb, int nchunks,
+                                                           const int32_t* __restrict__ num,
+                                                           int stride, int nb, int nchunks,
                                                            int c, int bin_width,
                                                            int32_t* __restrict__ order) {
   const int bh = blockIdx.x;
   auto cnt = [&](int i) {
     const size_t item = (size_t)bh * nb + i;
-    int n = k2q_num[item];
-    n = n > k2q_stride ? k2q_stride : n;
+    int n = num[item];
+    n = n > stride ? stride : n;
     if (n <= 0) return 0;
     const int32_t* cb = bounds + item * (nchunks + 1) + c;
     int b0 = cb[0], b1 = cb[1];
@@ -366,11 +366,10 @@ __global__ void __launch_bounds__(1024) chunk_order_kernel(const int32_t* __rest
   order_block_of(cnt, nb, bin_width, order, bh);
 }
 
-void launch_chunk_order(const int32_t* bounds, const int32_t* k2q_num, int k2q_stride, int BH,
-                        int nb, int nchunks, int c, int bin_width, int32_t* order,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL(chunk_order_kernel, dim3(BH), dim3(1024), 0, stream, bounds, k2q_num,
-                     k2q_stride, nb, nchunks, c, bin_width, order);
+void launch_chunk_order(const int32_t* bounds, const int32_t* num, int stride, int BH, int nb,
+                        int nchunks, int c, int bin_width, int32_t* order, hipStream_t stream) {
+  hipLaunchKernelGGL(chunk_order_kernel, dim3(BH), dim3(1024), 0, stream, bounds, num, stride, nb,
+                     nchunks, c, bin_width, order);
 }
 
 // The index stage's per-head tasks in one launch: workgroup (bh, task) runs task blockIdx.y of the

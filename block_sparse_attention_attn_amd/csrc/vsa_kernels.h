@@ -105,14 +105,14 @@ void launch_bwd_pre(const BwdPreParams& p, hipStream_t stream);
 constexpr int ORDER_MAX_KV_BLOCKS = 16384; // LDS holds one 32-bit key per block
 void launch_bwd_order(const int32_t* num, int BH, int nb, int bin_width, int32_t* order,
                       hipStream_t stream);
+// The work order of chunk c of chunked launches: items binned by the length of their list's
+// part inside the chunk (bounds from launch_chunk_bounds over the lists num / stride: k2q for the
+// kv-major kernel, q2k for the forward), one permutation per (b, h).
+void launch_chunk_order(const int32_t* bounds, const int32_t* num, int stride, int BH, int nb,
+                        int nchunks, int c, int bin_width, int32_t* order, hipStream_t stream);
 // Up to three per-head tasks of the index stage in one launch (one 1024-thread workgroup per
 // head and task): ORDER writes the work order of `num` (counts per item) to `out`; KBASE writes
 // the dS slot bases (exclusive prefix sum of the clamped k2q counts `num`) to `out`.
-// The kv-major work order of q-range chunk c: items binned by the length of their list's part
-// inside the chunk (bounds from launch_chunk_bounds), one permutation per (b, h).
-void launch_chunk_order(const int32_t* bounds, const int32_t* k2q_num, int k2q_stride, int BH,
-                        int nb, int nchunks, int c, int bin_width, int32_t* order,
-                        hipStream_t stream);
 struct IndexTask {
   enum Kind { ORDER = 0, KBASE = 1 };
   int kind;
